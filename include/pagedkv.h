@@ -1,0 +1,229 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged KV-cache attention for AMD MI355X
+ * (gfx950).
+ *
+ * The method (web pages, by title and section):
+ *   [P1] "03 | PagedAttention and the KV-cache memory system" (llm-infra-atlas)
+ *        §3 block table, slot formula; §3.1 page bytes; §4 paged kernel loop,
+ *        online-softmax triple, split-KV decode, tiled prefill given the table;
+ *        §4.1 write path through slot_mapping; §4.2 stable buffers, free only
+ *        after consumers finish; §8.1 FP8 KV with FP32 scales.
+ *   [P2] "KV Cache: capacity, layout, lifecycle" (wineandchord)
+ *        "Page-table addressing" (physical_slot and its errors), "Physical
+ *        layout", "Correctness contract" (reject a mismatched descriptor).
+ *
+ * General conventions
+ *   - Every pointer named *device* is device memory the CALLER owns.  The
+ *     library never allocates, frees or synchronises; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and is complete only
+ *     when that stream is.  Nothing is copied host<->device on any call.
+ *   - Blocks must not be freed or reused until the stream work that reads or
+ *     writes them has completed ([P1 §4.2]); that is the caller's job.
+ *   - Device pointers must be 16-byte aligned; tensors are dense, row-major.
+ *   - Outputs never alias inputs.
+ *   - Return value: PKV_OK (0) or a negative status (pkv_strerror explains it).
+ *     Argument errors are detected on the host before anything is enqueued.
+ *     Contents of device arrays (block tables, context lengths, slots) cannot
+ *     be checked without a copy; kernels treat them defensively instead (see
+ *     each call) so that a bad entry can corrupt results but never memory
+ *     outside the caller's buffers.
+ *   - All entry points are thread-safe (no global state).
+ *
+ * Physical pool layout (owned by this library; one pool for K, one for V, per
+ * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
+ *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   V pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *   fp8 scales (K and V separately): float [num_blocks][num_kv_heads]
+ * One (block, kv head) page is contiguous in each pool.  The logical element
+ * K[block][head][t][d] lives at K pool index
+ *   (((block*num_kv_heads + head)*(head_dim/X) + d/X)*block_size + t)*X + d%X
+ * and V[block][head][t][d] at ((block*num_kv_heads + head)*block_size + t)*head_dim + d.
+ * The K layout lets one lane own one token and read 16 bytes per load while
+ * the 16-byte chunks of a wavefront's tokens are consecutive in memory.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_VERSION 100
+
+/* element types; fp8 is OCP E4M3 (bias 7, max 448, no infinity) */
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3
+} pkv_dtype;
+
+/* status codes */
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,       /* invalid argument (null/misaligned pointer, size, mismatch) */
+  PKV_ERANGE = -2,       /* position / block id outside the table or the pool */
+  PKV_EUNSUPPORTED = -3, /* valid request with no kernel instantiation here */
+  PKV_EWORKSPACE = -4,   /* workspace too small */
+  PKV_EHIP = -5          /* HIP runtime reported an error while launching */
+};
+
+/* Descriptor of one layer's paged pool ([P1 §3.1]; [P2 "Correctness contract"]:
+ * every call validates it and rejects a mismatch instead of reinterpreting).
+ * Supported: block_size a power of two in [1, 64]; head_dim 64 or 128;
+ * num_kv_heads >= 1; num_blocks >= 1. */
+typedef struct pkv_pool_desc {
+  int32_t num_blocks;
+  int32_t block_size;   /* tokens per block (B) */
+  int32_t num_kv_heads; /* H_kv */
+  int32_t head_dim;     /* D */
+  int32_t kv_dtype;     /* pkv_dtype */
+} pkv_pool_desc;
+
+/* Human-readable text of a status code (static storage). */
+const char* pkv_strerror(int status);
+
+/* PKV_VERSION of the built library. */
+int pkv_version(void);
+
+/* [P1 §3.1] Bytes of the K pool and the V pool:
+ *   num_blocks * num_kv_heads * block_size * head_dim * E  each,
+ * i.e. the per-layer page size 2*block_size*num_kv_heads*head_dim*E split
+ * into K and V; for fp8 also the bytes of ONE scale array
+ * (num_blocks*num_kv_heads*4), else 0.  Any output pointer may be NULL.
+ * Errors: PKV_EINVAL for a NULL/invalid descriptor, PKV_EUNSUPPORTED for a
+ * valid one this library has no kernels for. */
+int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
+                   size_t* scale_bytes_each);
+
+/* [P2 "Page-table addressing"] Host-side slot of one position, with the page's
+ * error rules: block_size <= 0 or token_pos < 0 -> PKV_EINVAL;
+ * token_pos / block_size >= table_len -> PKV_ERANGE ("logical block is not
+ * allocated"); a negative physical id -> PKV_EINVAL.  Otherwise
+ * *slot = table[token_pos / B] * B + token_pos % B.  `table` is HOST memory. */
+int pkv_physical_slot(const int32_t* table, int32_t table_len, int32_t block_size,
+                      int64_t token_pos, int64_t* slot);
+
+/* Host-side check of block tables before they are uploaded: for each sequence
+ * s, entries [0, ceil(context_lens[s] / block_size)) of its row must lie in
+ * [0, num_blocks), and ceil(ctx/B) <= max_blocks_per_seq.  HOST arrays.
+ * Returns PKV_OK, PKV_ERANGE (bad entry or length) or PKV_EINVAL. */
+int pkv_validate_block_table(const int32_t* block_table, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t block_size, int32_t num_blocks);
+
+/* [P1 §3, §4.1] Slot of every new token, on the device:
+ *   slot_mapping[i] = block_table[seq_idx[i]][positions[i] / B] * B + positions[i] % B.
+ * Device arrays: block_table int32 [num_seqs][max_blocks_per_seq],
+ * seq_idx and positions int32 [num_tokens], slot_mapping int64 [num_tokens] (out).
+ * Token i gets -1 (padding, skipped by pkv_kv_cache_write) wherever the host
+ * reference would raise: seq_idx outside [0, num_seqs), positions[i] < 0,
+ * logical block >= max_blocks_per_seq, or a negative table entry.
+ * num_tokens == 0 enqueues nothing.  Errors: PKV_EINVAL, PKV_EHIP. */
+int pkv_slot_mapping(const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+                     const int32_t* seq_idx, const int32_t* positions, int32_t num_tokens,
+                     int32_t block_size, int64_t* slot_mapping, void* stream);
+
+/* [P1 §4.1, §8.1] Scatter the new tokens' K and V into the pools
+ * ("reshape_and_cache"): for i < num_tokens (the length of slot_mapping, not of
+ * any padded K/V), if 0 <= slot_mapping[i] < num_blocks*block_size, token i's
+ * K/V rows k[i][h][:], v[i][h][:] are stored at block slot/B, offset slot%B.
+ *   k, v: device [num_tokens][num_kv_heads][head_dim] of src_dtype.
+ *   Non-fp8 pools: src_dtype must equal pool->kv_dtype; the copy is bitwise.
+ *   fp8 pools: src_dtype in {F32, F16, BF16}; each element is stored as
+ *     e4m3(x / scale[block][head]) with x / scale an IEEE fp32 division,
+ *     rounded to nearest (ties to even), saturating finite overflow and
+ *     infinities to +-448; NaN stays NaN.  k_scale, v_scale: device float
+ *     [num_blocks][num_kv_heads], read only (the caller owns the scales).
+ * Negative or out-of-pool slots are skipped.  Two tokens with the same slot
+ * race (the caller's slot mapping should be injective).
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
+int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
+                       const void* v, int32_t src_dtype, const pkv_pool_desc* pool,
+                       void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                       void* stream);
+
+/* Workspace bytes pkv_paged_attention_decode needs for a given partition size:
+ * 0 when partition_size == 0 (unsplit), else
+ *   num_seqs * num_q_heads * P_max * (head_dim + 2) * 4,  P_max = ceil(max_context_len / P),
+ * laid out as part_out float [S][H_q][P_max][D], then part_max float [S][H_q][P_max],
+ * then part_sum float [S][H_q][P_max] (the arrays pkv_split_kv_reduce takes).
+ * Errors: PKV_EINVAL (negative sizes, partition_size not a positive multiple of 64). */
+int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_context_len, int32_t partition_size, size_t* bytes);
+
+/* [P1 §4] Paged decode attention, one query token per sequence.
+ * For sequence s and query head h (kv head h / (num_q_heads / num_kv_heads)):
+ *   z_t = scale * <q[s][h], K_t>,  t < ctx_s, K_t/V_t found through
+ *   block_table[s][t / B] at offset t % B (fp8: times the page's scale),
+ *   out[s][h] = sum_t exp(z_t - max z) V_t / sum_t exp(z_t - max z)
+ * with fp32 accumulation; ctx_s = 0 gives zeros.  The newest token's K/V
+ * must already have been written (context_lens counts it).
+ *   q: device [num_seqs][num_q_heads][head_dim] of q_dtype;
+ *      (pool f32, q f32), (f16, f16), (bf16, bf16), (fp8, bf16|f16) supported.
+ *   k_pool, v_pool: device, layout above; k_scale, v_scale: fp8 only, else NULL.
+ *   block_table: device int32 [num_seqs][max_blocks_per_seq].
+ *   context_lens: device int32 [num_seqs]; each is clamped to
+ *      [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ *   max_context_len: host-known upper bound on context_lens (sizes the grid).
+ *   partition_size: 0 = one pass per (sequence, kv head); else a positive
+ *      multiple of 64: the context is split into partitions of that many tokens,
+ *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]).
+ *   workspace: device scratch of pkv_decode_workspace_bytes (NULL if 0 bytes).
+ *   out: device [num_seqs][num_q_heads][head_dim] of q_dtype (rounded to nearest).
+ * Table entries outside [0, num_blocks) are clamped into range (wrong results,
+ * never a fault); pkv_validate_block_table checks tables on the host.
+ * Errors: PKV_EINVAL (incl. num_q_heads % num_kv_heads != 0), PKV_EUNSUPPORTED
+ * (e.g. group size > 16 or a dtype pair above not listed), PKV_EWORKSPACE, PKV_EHIP. */
+int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
+                               int32_t num_q_heads, const pkv_pool_desc* pool,
+                               const void* k_pool, const void* v_pool, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, void* out, void* stream);
+
+/* [P1 §4] Log-sum-exp merge of split-KV partitions.  For sequence s, head h,
+ * partitions i < min(ceil(ctx_s / partition_size), max_partitions) with state
+ * (m_i = part_max, l_i = part_sum, o_i = part_out normalised by l_i):
+ *   M = max_i m_i,  w_i = exp(m_i - M) * l_i,  out = sum_i w_i o_i / sum_i w_i.
+ * m is in natural-log units of the scaled logits z.  Partitions with l_i = 0
+ * contribute nothing; ctx_s = 0 gives zeros.
+ *   part_out: device float [num_seqs][num_q_heads][max_partitions][head_dim];
+ *   part_max, part_sum: device float [num_seqs][num_q_heads][max_partitions];
+ *   context_lens: device int32 [num_seqs] (clamped to [0, max_partitions*P]);
+ *   out: device [num_seqs][num_q_heads][head_dim] of out_dtype (F32/F16/BF16).
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
+int pkv_split_kv_reduce(const float* part_out, const float* part_max, const float* part_sum,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t head_dim, int32_t partition_size, int32_t max_partitions,
+                        void* out, int32_t out_dtype, void* stream);
+
+/* [P1 §4] Chunked prefill over the paged cache (tiled, matrix cores).
+ * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]); with n_s
+ * rows, row i sits at absolute position a = ctx_s - n_s + i and attends to
+ * keys t <= a (causal != 0) or to every t < ctx_s (causal == 0), read through
+ * the block table; those tokens' K/V must already be in the pool.  Rows that
+ * see no key (n_s > ctx_s) get zeros.
+ *   q: device [total_q][num_q_heads][head_dim] of q_dtype; out likewise.
+ *   cu_seqlens_q: device int32 [num_seqs + 1], non-decreasing, last = total_q.
+ *   max_q_len: host-known upper bound on n_s (sizes the grid).
+ *   Supported: pool bf16 with q bf16; pool fp8 with q bf16 (fp8 -> bf16 is
+ *   exact; K's scale multiplies the scores, V's scale the probabilities,
+ *   which are rounded to bf16 for the P.V product); head_dim 128.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
+int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
+                      int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                      const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t causal, void* out,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -1,0 +1,357 @@
+// api.cpp — C-ABI front end of libpagedkv.so: argument validation on the host,
+// then dispatch to the kernel launchers.  Stateless and allocation-free.
+#include "../../include/pagedkv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kMaxHeadsGroup = 16;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Descriptor validation ("KV Cache: capacity, layout, lifecycle", correctness
+// contract: a mismatched descriptor is rejected, never reinterpreted).
+int check_desc(const pkv_pool_desc* d) {
+  if (!d) return PKV_EINVAL;
+  if (d->num_blocks < 1 || d->block_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1)
+    return PKV_EINVAL;
+  if (elem_bytes(d->kv_dtype) == 0) return PKV_EINVAL;
+  if ((d->head_dim * elem_bytes(d->kv_dtype)) % 16 != 0) return PKV_EINVAL;
+  if (!pow2(d->block_size) || d->block_size > 64) return PKV_EUNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
+  // page-aligned pools: total element count must fit the kernels' index math
+  const double rows = (double)d->num_blocks * d->num_kv_heads * d->block_size;
+  if (rows >= 4294967296.0) return PKV_EUNSUPPORTED;
+  return PKV_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_ERANGE: return "position or block id outside the table or the pool";
+    case PKV_EUNSUPPORTED: return "no kernel for this configuration";
+    case PKV_EWORKSPACE: return "workspace too small";
+    case PKV_EHIP: return "HIP runtime error while launching";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return PKV_VERSION; }
+
+int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
+                   size_t* scale_bytes_each) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  const size_t e = (size_t)pool->num_blocks * pool->num_kv_heads * pool->block_size *
+                   pool->head_dim * elem_bytes(pool->kv_dtype);
+  if (k_bytes) *k_bytes = e;
+  if (v_bytes) *v_bytes = e;
+  if (scale_bytes_each)
+    *scale_bytes_each = pool->kv_dtype == PKV_FP8_E4M3
+                            ? (size_t)pool->num_blocks * pool->num_kv_heads * sizeof(float)
+                            : 0;
+  return PKV_OK;
+}
+
+// "KV Cache: capacity, layout, lifecycle", Page-table addressing: the page's
+// reference, with its ValueError cases as PKV_EINVAL and IndexError as PKV_ERANGE.
+int pkv_physical_slot(const int32_t* table, int32_t table_len, int32_t block_size,
+                      int64_t token_pos, int64_t* slot) {
+  if (!slot || table_len < 0 || (table_len > 0 && !table)) return PKV_EINVAL;
+  if (block_size <= 0 || token_pos < 0) return PKV_EINVAL;
+  const int64_t logical = token_pos / block_size;
+  const int64_t offset = token_pos % block_size;
+  if (logical >= table_len) return PKV_ERANGE;
+  const int64_t phys = table[logical];
+  if (phys < 0) return PKV_EINVAL;
+  *slot = phys * block_size + offset;
+  return PKV_OK;
+}
+
+int pkv_validate_block_table(const int32_t* block_table, int32_t num_seqs,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t block_size, int32_t num_blocks) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_EINVAL;
+  if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_table)))
+    return PKV_EINVAL;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t ctx = context_lens[s];
+    if (ctx < 0) return PKV_ERANGE;
+    const int64_t nb = (ctx + block_size - 1) / block_size;
+    if (nb > max_blocks_per_seq) return PKV_ERANGE;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = block_table[(int64_t)s * max_blocks_per_seq + j];
+      if (id < 0 || id >= num_blocks) return PKV_ERANGE;
+    }
+  }
+  return PKV_OK;
+}
+
+int pkv_slot_mapping(const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+                     const int32_t* seq_idx, const int32_t* positions, int32_t num_tokens,
+                     int32_t block_size, int64_t* slot_mapping, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0)
+    return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!seq_idx || !positions || !slot_mapping) return PKV_EINVAL;
+  if (num_seqs > 0 && max_blocks_per_seq > 0 && !block_table) return PKV_EINVAL;
+  if (num_seqs == 0 || max_blocks_per_seq == 0) block_table = nullptr;
+  int rc = pkv::launch_slot_mapping(block_table, block_table ? num_seqs : 0, max_blocks_per_seq,
+                                    seq_idx, positions, num_tokens, block_size, slot_mapping,
+                                    as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
+                       const void* v, int32_t src_dtype, const pkv_pool_desc* pool,
+                       void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                       void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_tokens < 0) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!slot_mapping || !k || !v || !k_pool || !v_pool) return PKV_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_EINVAL;
+  if (elem_bytes(src_dtype) == 0 || src_dtype == PKV_FP8_E4M3) return PKV_EINVAL;
+  if (pool->kv_dtype == PKV_FP8_E4M3) {
+    if (!k_scale || !v_scale) return PKV_EINVAL;
+  } else if (src_dtype != pool->kv_dtype) {
+    return PKV_EINVAL;  // descriptor/dtype mismatch: no silent conversion
+  }
+  pkv::WriteLaunch p;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.k = k;
+  p.v = v;
+  p.src_dtype = src_dtype;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_blocks = pool->num_blocks;
+  p.block_size = pool->block_size;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.kv_dtype = pool->kv_dtype;
+  rc = pkv::launch_kv_cache_write(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_context_len, int32_t partition_size, size_t* bytes) {
+  if (!bytes || num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return PKV_EINVAL;
+  if (partition_size == 0) {
+    *bytes = 0;
+    return PKV_OK;
+  }
+  if (partition_size % 64 != 0) return PKV_EINVAL;
+  const size_t pmax = ((size_t)max_context_len + partition_size - 1) / partition_size;
+  *bytes = (size_t)num_seqs * num_q_heads * pmax * ((size_t)head_dim + 2) * sizeof(float);
+  return PKV_OK;
+}
+
+int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
+                               int32_t num_q_heads, const pkv_pool_desc* pool,
+                               const void* k_pool, const void* v_pool, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, void* out,
+                               void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
+      partition_size < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
+  if (num_q_heads / pool->num_kv_heads > kMaxHeadsGroup) return PKV_EUNSUPPORTED;
+  if (partition_size != 0 && partition_size % 64 != 0) return PKV_EINVAL;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EINVAL;
+  if (max_context_len > (1 << 30)) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PKV_EINVAL;
+  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (num_seqs > 65535 || pool->num_kv_heads > 65535) return PKV_EUNSUPPORTED;
+
+  int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+  if (cap > max_context_len) cap = max_context_len;
+
+  pkv::DecodeLaunch p = {};
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.kv_dtype = pool->kv_dtype;
+  p.block_size = pool->block_size;
+  p.num_blocks = pool->num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.ctx_cap = (int)cap;
+  p.scale = scale;
+
+  if (partition_size == 0) {
+    p.split = 0;
+    p.max_parts = 1;
+    p.part_size = (int)((cap + 63) / 64 * 64);
+    if (p.part_size == 0) p.part_size = 64;
+    rc = pkv::launch_decode(p, as_stream(stream));
+    return rc == 0 ? PKV_OK : rc;
+  }
+
+  // workspace layout follows max_context_len (the documented P_max)
+  size_t need = 0;
+  rc = pkv_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_context_len,
+                                  partition_size, &need);
+  if (rc != PKV_OK) return rc;
+  const int max_parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  p.max_parts = max_parts;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return PKV_EINVAL;
+  const size_t n_part = (size_t)num_seqs * num_q_heads * max_parts;
+  float* ws = static_cast<float*>(workspace);
+  p.split = 1;
+  p.part_size = partition_size;
+  p.part_out = ws;
+  p.part_max = ws ? ws + n_part * pool->head_dim : nullptr;
+  p.part_sum = ws ? p.part_max + n_part : nullptr;
+  if (max_parts > 0) {
+    rc = pkv::launch_decode(p, as_stream(stream));
+    if (rc != 0) return rc;
+  }
+  pkv::ReduceLaunch r;
+  r.part_out = p.part_out;
+  r.part_max = p.part_max;
+  r.part_sum = p.part_sum;
+  r.context_lens = context_lens;
+  r.out = out;
+  r.out_dtype = q_dtype;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = pool->head_dim;
+  r.part_size = partition_size;
+  r.max_parts = max_parts;
+  rc = pkv::launch_split_reduce(r, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_split_kv_reduce(const float* part_out, const float* part_max, const float* part_sum,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t head_dim, int32_t partition_size, int32_t max_partitions,
+                        void* out, int32_t out_dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads < 1 || partition_size < 1 || max_partitions < 0)
+    return PKV_EINVAL;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_F16 && out_dtype != PKV_BF16) return PKV_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens || !out || (max_partitions > 0 && (!part_out || !part_max || !part_sum)))
+    return PKV_EINVAL;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;
+  pkv::ReduceLaunch r;
+  r.part_out = part_out;
+  r.part_max = part_max;
+  r.part_sum = part_sum;
+  r.context_lens = context_lens;
+  r.out = out;
+  r.out_dtype = out_dtype;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = head_dim;
+  r.part_size = partition_size;
+  r.max_parts = max_partitions;
+  int rc = pkv::launch_split_reduce(r, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
+                      int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                      const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, float scale, int32_t causal, void* out,
+                      void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads < 1 ||
+      max_blocks_per_seq < 1 || max_context_len < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
+  if (q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+  if (pool->kv_dtype != PKV_BF16 && pool->kv_dtype != PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
+  if (pool->head_dim != 128) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0) return PKV_OK;
+  if (!q || !cu_seqlens_q || !k_pool || !v_pool || !block_table || !context_lens || !out)
+    return PKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PKV_EINVAL;
+  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;
+  int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+  if (cap > max_context_len) cap = max_context_len;
+  if (cap > (int64_t)1 << 30) return PKV_EUNSUPPORTED;
+  pkv::PrefillLaunch p;
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.num_seqs = num_seqs;
+  p.total_q = total_q;
+  p.max_q_len = max_q_len;
+  p.num_q_heads = num_q_heads;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_blocks = pool->num_blocks;
+  p.block_size = pool->block_size;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.kv_dtype = pool->kv_dtype;
+  p.block_table = block_table;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.context_lens = context_lens;
+  p.ctx_cap = (int)cap;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.out = out;
+  rc = pkv::launch_prefill(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+}  // extern "C"

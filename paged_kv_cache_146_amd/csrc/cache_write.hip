@@ -1,0 +1,154 @@
+// cache_write.hip — the write path: slot mapping and the scatter of new K/V.
+//
+// Method: "03 | PagedAttention and the KV-cache memory system", §3 (slot =
+// physical_id * B + position mod B, physical_id = block_table[position / B])
+// and §4.1 (the model runner scatters each new token's K/V to its slot; the
+// number of tokens written is the length of slot_mapping); §8.1 (fp8 pages
+// carry fp32 scales).  "KV Cache: capacity, layout, lifecycle", "Page-table
+// addressing": the cases where the reference raises become padding (-1) here.
+//
+// The scatter works in 16-byte destination pieces: one thread moves one piece
+// of one (token, kv head) row into the K pool ([block][head][D/X][B][X]) or
+// the V pool ([block][head][B][D]).  Bit copies for f32/f16/bf16 pools; for
+// fp8 pools the thread divides 16 source elements by the page's scale (IEEE
+// fp32 division) and encodes them as OCP E4M3 (nearest, ties to even,
+// saturating).
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+
+constexpr int kWriteThreads = 256;
+
+__global__ __launch_bounds__(kWriteThreads) void slot_mapping_kernel(
+    const int32_t* __restrict__ block_table, int num_seqs, int W,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ positions, int num_tokens,
+    int B, int64_t* __restrict__ slot_mapping) {
+  const int i = blockIdx.x * kWriteThreads + threadIdx.x;
+  if (i >= num_tokens) return;
+  const int s = seq_idx[i];
+  const int pos = positions[i];
+  long long slot = -1;
+  if (s >= 0 && s < num_seqs && pos >= 0) {
+    const int j = pos / B;
+    if (j < W) {
+      const int phys = block_table[(size_t)s * W + j];
+      if (phys >= 0) slot = (long long)phys * B + (pos - j * B);
+    }
+  }
+  slot_mapping[i] = slot;
+}
+
+// Bit copy of one 16-byte piece (non-fp8 pools); ES = bytes per element.
+template <int ES>
+__global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
+    const int64_t* __restrict__ slot_mapping, int num_tokens, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    int num_blocks, int B, int Hkv, int D) {
+  const int NC = D * ES / 16;  // pieces per row
+  const long long total = (long long)num_tokens * Hkv * NC;
+  const long long idx = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % NC);
+  const int h = (int)((idx / NC) % Hkv);
+  const long long i = idx / ((long long)NC * Hkv);
+  const long long slot = slot_mapping[i];
+  if (slot < 0 || slot >= (long long)num_blocks * B) return;
+  const long long blk = slot / B, off = slot % B;
+  const size_t src = ((size_t)i * Hkv + h) * NC + c;  // in 16-byte pieces
+  const size_t page = (size_t)blk * Hkv + h;
+  const size_t kdst = (page * NC + c) * B + off;
+  const size_t vdst = (page * B + off) * NC + c;
+  if (blockIdx.y == 0)
+    reinterpret_cast<u32x4*>(k_pool)[kdst] = reinterpret_cast<const u32x4*>(k)[src];
+  else
+    reinterpret_cast<u32x4*>(v_pool)[vdst] = reinterpret_cast<const u32x4*>(v)[src];
+}
+
+// fp8 pools: 16 source elements of SRC type -> one 16-byte piece of E4M3 codes.
+template <int SRC>
+__global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
+    const int64_t* __restrict__ slot_mapping, int num_tokens, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int num_blocks, int B,
+    int Hkv, int D) {
+  constexpr int SES = Elem<SRC>::bytes;
+  const int NC = D / 16;
+  const long long total = (long long)num_tokens * Hkv * NC;
+  const long long idx = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % NC);
+  const int h = (int)((idx / NC) % Hkv);
+  const long long i = idx / ((long long)NC * Hkv);
+  const long long slot = slot_mapping[i];
+  if (slot < 0 || slot >= (long long)num_blocks * B) return;
+  const long long blk = slot / B, off = slot % B;
+  const bool isv = blockIdx.y != 0;
+  const uint8_t* src = (isv ? v : k) + (((size_t)i * Hkv + h) * D + (size_t)c * 16) * SES;
+  const size_t page = (size_t)blk * Hkv + h;
+  const float scale = (isv ? v_scale : k_scale)[page];
+
+  float x[16];
+  const u32x4* sp = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int part = 0; part < SES; ++part) unpack16<SRC>(sp[part], x + part * (16 / SES));
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float y = __fdiv_rn(x[e], scale);
+    w[e >> 2] |= f32_to_e4m3(y) << (8 * (e & 3));
+  }
+  const u32x4 packed = {w[0], w[1], w[2], w[3]};
+  if (!isv)
+    reinterpret_cast<u32x4*>(k_pool)[(page * NC + c) * B + off] = packed;
+  else
+    reinterpret_cast<u32x4*>(v_pool)[(page * B + off) * NC + c] = packed;
+}
+
+int launch_slot_mapping(const int32_t* block_table, int num_seqs, int W, const int32_t* seq_idx,
+                        const int32_t* positions, int num_tokens, int B, int64_t* slot_mapping,
+                        hipStream_t st) {
+  if (num_tokens == 0) return 0;
+  dim3 grid((num_tokens + kWriteThreads - 1) / kWriteThreads);
+  hipLaunchKernelGGL(slot_mapping_kernel, grid, dim3(kWriteThreads), 0, st, block_table,
+                     num_seqs, W, seq_idx, positions, num_tokens, B, slot_mapping);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
+  if (p.num_tokens == 0) return 0;
+  const int ES = p.kv_dtype == DT_F32 ? 4 : (p.kv_dtype == DT_FP8 ? 1 : 2);
+  const long long pieces = (long long)p.num_tokens * p.num_kv_heads * (p.head_dim * ES / 16);
+  const long long blocks = (pieces + kWriteThreads - 1) / kWriteThreads;
+  if (blocks > 0x7fffffffLL) return -3;
+  dim3 grid((unsigned)blocks, 2);
+  const uint8_t* k = (const uint8_t*)p.k;
+  const uint8_t* v = (const uint8_t*)p.v;
+  uint8_t* kp = (uint8_t*)p.k_pool;
+  uint8_t* vp = (uint8_t*)p.v_pool;
+  if (p.kv_dtype == DT_F32)
+    hipLaunchKernelGGL(kv_write_copy_kernel<4>, grid, dim3(kWriteThreads), 0, st, p.slot_mapping,
+                       p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
+                       p.head_dim);
+  else if (p.kv_dtype == DT_F16 || p.kv_dtype == DT_BF16)
+    hipLaunchKernelGGL(kv_write_copy_kernel<2>, grid, dim3(kWriteThreads), 0, st, p.slot_mapping,
+                       p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
+                       p.head_dim);
+  else if (p.src_dtype == DT_BF16)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_BF16>, grid, dim3(kWriteThreads), 0, st,
+                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
+                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+  else if (p.src_dtype == DT_F16)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F16>, grid, dim3(kWriteThreads), 0, st,
+                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
+                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+  else if (p.src_dtype == DT_F32)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F32>, grid, dim3(kWriteThreads), 0, st,
+                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
+                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+  else
+    return -3;
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace pkv

@@ -1,0 +1,85 @@
+// internal.hpp — host-side declarations shared by the C-ABI front end (api.cpp)
+// and the kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeLaunch {
+  const void* q;
+  int q_dtype;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* out;
+  float* part_out;
+  float* part_max;
+  float* part_sum;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, kv_dtype;
+  int block_size, num_blocks, max_blocks_per_seq;
+  int ctx_cap;        // min(max_context_len, max_blocks_per_seq * block_size)
+  int part_size;      // > 0: tokens per partition (multiple of 64)
+  int max_parts;      // partitions per sequence covered by the grid
+  int split;          // write partials (1) or the final output (0)
+  float scale;
+};
+
+// returns a PKV_* status
+int launch_decode(const DecodeLaunch& p, hipStream_t stream);
+
+struct ReduceLaunch {
+  const float* part_out;
+  const float* part_max;
+  const float* part_sum;
+  const int32_t* context_lens;
+  void* out;
+  int out_dtype;
+  int num_seqs, num_q_heads, head_dim, part_size, max_parts;
+};
+int launch_split_reduce(const ReduceLaunch& p, hipStream_t stream);
+
+int launch_slot_mapping(const int32_t* block_table, int num_seqs, int max_blocks_per_seq,
+                        const int32_t* seq_idx, const int32_t* positions, int num_tokens,
+                        int block_size, int64_t* slot_mapping, hipStream_t stream);
+
+struct WriteLaunch {
+  const int64_t* slot_mapping;
+  int num_tokens;
+  const void* k;
+  const void* v;
+  int src_dtype;
+  void* k_pool;
+  void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  int num_blocks, block_size, num_kv_heads, head_dim, kv_dtype;
+};
+int launch_kv_cache_write(const WriteLaunch& p, hipStream_t stream);
+
+struct PrefillLaunch {
+  const void* q;
+  int q_dtype;
+  const int32_t* cu_seqlens_q;
+  int num_seqs, total_q, max_q_len, num_q_heads;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  int num_blocks, block_size, num_kv_heads, head_dim, kv_dtype;
+  const int32_t* block_table;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int ctx_cap;
+  float scale;
+  int causal;
+  void* out;
+};
+int launch_prefill(const PrefillLaunch& p, hipStream_t stream);
+
+}  // namespace pkv
