@@ -1,0 +1,246 @@
+"""Benchmark: one paged-decode step of a Llama-3-8B-shaped layer on one MI355X.
+
+Workload: 64 sequences, context lengths U[128, 4096] (seed 2), H_q 32, H_kv 8,
+D 128, bf16 KV, block size 16, pool = needed blocks + 20% spare with shuffled
+block tables.  A step is the whole hot path for one new token per sequence:
+slot mapping -> scatter of the new K/V -> paged decode attention (split-KV +
+log-sum-exp reduce when a partition size is set).  Inputs are resident in HBM;
+the L2 and Infinity Cache are flushed before every step (outside the timed
+events), so K/V stream from HBM as they would behind the other layers.
+
+Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth of the
+step (GB/s); `roofline` is the decode kernel's achieved bandwidth against the
+8 TB/s peak; `cpu_baseline` is the plain CPU oracle on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention µs/step + achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_146_amd", "csrc", "decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_llama3_8b_counters.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-KV partition size (0 = unsplit, -1 = balanced; default balanced)")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the CPU oracle leg")
+    return ap.parse_args()
+
+
+DEFAULT_PARTITION = -1  # balanced split-KV
+
+
+def decode_bytes(wl) -> int:
+    """Algorithmic bytes of one decode launch: every K/V element of every sequence's
+    context once, q and out once, the used block-table entries and the lengths."""
+    e = 2  # bf16
+    nblk = sum(math.ceil(int(c) / wl.block_size) for c in wl.context_lens)
+    return (wl.kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * e
+            + 4 * nblk + 4 * wl.num_seqs)
+
+
+def write_bytes(wl) -> int:
+    """Slot mapping (seq, pos, table entry in; slot out) + scatter (K/V rows in and out)."""
+    S = wl.num_seqs
+    row = wl.num_kv_heads * wl.head_dim * 2
+    return S * (4 + 4 + 4 + 8) + S * (8 + 2 * row + 2 * row)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_146_amd as pkv
+    from paged_kv_cache_146_amd import workloads as W
+
+    P = DEFAULT_PARTITION if a.partition is None else a.partition
+    wl = W.llama3_8b_decode(seed=2)
+    dev = "cuda"
+    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # fill the pool through the library's write path (not timed)
+    slab = 1 << 17
+    T = len(wl.fill_seq)
+    for o in range(0, T, slab):
+        e = min(T, o + slab)
+        sl = pkv.pkv_slot_mapping(bt, torch.from_numpy(wl.fill_seq[o:e]).to(dev),
+                                  torch.from_numpy(wl.fill_pos[o:e]).to(dev), wl.block_size)
+        pkv.pkv_kv_cache_write(sl, bits(wl.k_src[o:e]), bits(wl.v_src[o:e]), desc, k_pool, v_pool)
+    q = bits(wl.q)
+    rows = wl.decode_new_token_rows()
+    k_new, v_new = bits(wl.k_src[rows]), bits(wl.v_src[rows])
+    seq_idx = torch.arange(wl.num_seqs, dtype=torch.int32, device=dev)
+    pos_new = (cl - 1).to(torch.int32)
+    slots = torch.empty(wl.num_seqs, dtype=torch.int64, device=dev)
+    out = torch.empty_like(q)
+    ws_bytes = pkv.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                              wl.head_dim, wl.max_context_len, P)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    # cache flush: READ 512 MiB (2x the Infinity Cache) so no dirty lines are left to be
+    # written back while the timed step runs
+    flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        pkv.pkv_slot_mapping(bt, seq_idx, pos_new, wl.block_size, out=slots)
+        pkv.pkv_kv_cache_write(slots, k_new, v_new, desc, k_pool, v_pool)
+        ev_mid.record()
+        pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
+                                       wl.scale, partition_size=P, workspace=ws, out=out)
+
+    ev_mid = torch.cuda.Event(enable_timing=True)
+    for _ in range(a.warmup):
+        if not a.no_flush:
+            flush.sum()
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        if not a.no_flush:
+            flush.sum()
+        ev_mid = mids[i]
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    dec_ms = np.array([m.elapsed_time(e) for m, e in zip(mids, ends)])
+
+    # parity spot check of this very output against the oracle on two sequences
+    parity = None
+    try:
+        import oracle
+        opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "bf16")
+        osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
+        oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+        sel = np.array([0, int(np.argmax(wl.context_lens))], np.int32)
+        ref = oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
+                                  seqs=sel)
+        got = out.float().cpu().numpy().astype(np.float64)[sel]
+        err = np.abs(got - ref)
+        parity = {"seqs": sel.tolist(), "max_abs": float(err.max()),
+                  "within_tol": bool((err <= 2e-3 + 1e-2 * np.abs(ref)).all())}
+    except Exception as ex:  # the bench still reports; the tests are the parity gate
+        parity = {"error": repr(ex)}
+
+    step_us = float(np.mean(step_ms) * 1e3)
+    dec_us = float(np.mean(dec_ms) * 1e3)
+    dbytes = decode_bytes(wl)
+    sbytes = dbytes + write_bytes(wl)
+    achieved = dbytes / (dec_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P:
+            traffic = c.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": round(sbytes / (step_us * 1e-6) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_us / 1e3, 5),
+        "us_per_step": round(step_us, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2)
+                                    for p in (10, 50, 90)],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-shaped paged decode layer (one new token per sequence)",
+            "num_seqs": wl.num_seqs, "context_lens": "U[128,4096], seed 2",
+            "sum_context": int(wl.context_lens.sum()), "H_q": wl.num_q_heads,
+            "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+            "kv_dtype": "bf16", "num_blocks": wl.num_blocks, "partition_size": P,
+            "caches": "warm" if a.no_flush else "flushed before every step",
+            "step": "slot_mapping + kv_cache_write + paged_attention_decode",
+        },
+        "algorithmic_bytes_per_step": sbytes,
+        "decode_tokens_per_s": round(wl.num_seqs / (step_us * 1e-6), 1),
+        "kv_tokens_per_s": round(float(wl.context_lens.sum()) / (step_us * 1e-6), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": {0: "paged_decode_kernel", -1: "paged_decode_balanced_kernel + "
+                       "balanced_merge_kernel"}.get(P, "paged_decode_kernel + split_reduce_kernel"),
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(dec_us, 2),
+        },
+        "wall_s_timed_region": round(wall, 4),
+        "parity_spot_check": parity,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, on the same workload, on this host's cores: the write of
+    the 64 new tokens plus decode attention for a bounded prefix of the sequences."""
+    import oracle
+    opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "bf16")
+    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
+    oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+    rows = wl.decode_new_token_rows()
+    order = np.arange(wl.num_seqs, dtype=np.int32)
+    steps, t_used = 0, 0.0
+    while t_used < budget_s and steps < 1000:  # whole steps, at least one
+        t0 = time.perf_counter()
+        s_new = oracle.slot_mapping(wl.block_table, order, wl.context_lens - 1, wl.block_size)
+        oracle.kv_cache_write(opool, s_new, wl.k_src[rows], wl.v_src[rows], "bf16")
+        oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale)
+        t_used += time.perf_counter() - t0
+        steps += 1
+    step_s = t_used / steps
+    step_bytes = decode_bytes(wl) + write_bytes(wl)
+    return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d whole steps of the same workload (write of the 64 new tokens + decode "
+                      "of all 64 sequences), %.1f s" % (steps, t_used),
+            "us_per_step": round(step_s * 1e6, 1)}
+
+
+if __name__ == "__main__":
+    main()

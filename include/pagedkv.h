@@ -146,14 +146,25 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
                        void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
                        void* stream);
 
+/* partition_size value selecting balanced split-KV (see pkv_paged_attention_decode) */
+#define PKV_PARTITION_BALANCED (-1)
+/* upper bound on the wavefront workers of the balanced mode */
+#define PKV_MAX_WORKERS 4096
+
 /* Workspace bytes pkv_paged_attention_decode needs for a given partition size:
- * 0 when partition_size == 0 (unsplit), else
- *   num_seqs * num_q_heads * P_max * (head_dim + 2) * 4,  P_max = ceil(max_context_len / P),
- * laid out as part_out float [S][H_q][P_max][D], then part_max float [S][H_q][P_max],
- * then part_sum float [S][H_q][P_max] (the arrays pkv_split_kv_reduce takes).
- * Errors: PKV_EINVAL (negative sizes, partition_size not a positive multiple of 64). */
-int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                               int32_t max_context_len, int32_t partition_size, size_t* bytes);
+ *   partition_size == 0 (unsplit): 0.
+ *   partition_size > 0 (fixed partitions of P tokens):
+ *     num_seqs * num_q_heads * P_max * (head_dim + 2) * 4,  P_max = ceil(max_context_len / P),
+ *     laid out as part_out float [S][H_q][P_max][D], then part_max float [S][H_q][P_max],
+ *     then part_sum float [S][H_q][P_max] (the arrays pkv_split_kv_reduce takes).
+ *   partition_size == PKV_PARTITION_BALANCED: enough for PKV_MAX_WORKERS workers,
+ *     2 * PKV_MAX_WORKERS * (num_q_heads / num_kv_heads) * (head_dim + 2) * 4; the
+ *     layout is internal (partial states of the pairs that workers share).
+ * Errors: PKV_EINVAL (negative sizes, num_q_heads % num_kv_heads != 0, any other
+ * partition_size that is not a positive multiple of 64). */
+int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                               size_t* bytes);
 
 /* [P1 §4] Paged decode attention, one query token per sequence.
  * For sequence s and query head h (kv head h / (num_q_heads / num_kv_heads)):
@@ -169,10 +180,16 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t he
  *   context_lens: device int32 [num_seqs]; each is clamped to
  *      [0, min(max_context_len, max_blocks_per_seq * block_size)].
  *   max_context_len: host-known upper bound on context_lens (sizes the grid).
- *   partition_size: 0 = one pass per (sequence, kv head); else a positive
- *      multiple of 64: the context is split into partitions of that many tokens,
- *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]).
- *   workspace: device scratch of pkv_decode_workspace_bytes (NULL if 0 bytes).
+ *   partition_size: 0 = one pass per (sequence, kv head); a positive multiple
+ *      of 64 = the context is split into partitions of that many tokens,
+ *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]);
+ *      PKV_PARTITION_BALANCED = the 64-token chunks of all (sequence, kv head)
+ *      pairs are cut into equal contiguous shares, one per resident wavefront,
+ *      and the pairs that shares split are merged by log-sum-exp (same
+ *      algebra; evenly loaded whatever the length mix; num_seqs <= 16384).
+ *   workspace: device scratch of pkv_decode_workspace_bytes (NULL if 0 bytes);
+ *      in balanced mode a smaller workspace just means fewer workers (it must
+ *      hold at least one worker: 2 * G * (head_dim + 2) * 4 bytes).
  *   out: device [num_seqs][num_q_heads][head_dim] of q_dtype (rounded to nearest).
  * Table entries outside [0, num_blocks) are clamped into range (wrong results,
  * never a fault); pkv_validate_block_table checks tables on the host.

@@ -74,7 +74,7 @@ def lib():
                     "pkv_validate_block_table": (ctypes.c_int, [P, I32, I32, P, I32, I32]),
                     "pkv_slot_mapping": (ctypes.c_int, [P, I32, I32, P, P, I32, I32, P, P]),
                     "pkv_kv_cache_write": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, P, P, P]),
-                    "pkv_decode_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32, P]),
+                    "pkv_decode_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, P]),
                     "pkv_paged_attention_decode": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P,
                                                                   P, I32, P, I32, F, I32, P, SZ,
                                                                   P, P]),
@@ -222,12 +222,17 @@ def pkv_kv_cache_write(slot_mapping, k, v, desc: PoolDesc, k_pool, v_pool, k_sca
            "pkv_kv_cache_write")
 
 
-def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+PARTITION_BALANCED = -1
+MAX_WORKERS = 4096
+
+
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                partition_size) -> int:
     out = ctypes.c_size_t()
-    _check(lib().pkv_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim),
-                                            int(max_context_len), int(partition_size),
-                                            ctypes.byref(out)), "pkv_decode_workspace_bytes")
+    _check(lib().pkv_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(num_kv_heads),
+                                            int(head_dim), int(max_context_len),
+                                            int(partition_size), ctypes.byref(out)),
+           "pkv_decode_workspace_bytes")
     return out.value
 
 
@@ -240,7 +245,8 @@ def pkv_paged_attention_decode(q, desc: PoolDesc, k_pool, v_pool, block_table, c
     qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    need = pkv_decode_workspace_bytes(S, Hq, desc.head_dim, max_context_len, partition_size)
+    need = pkv_decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim, max_context_len,
+                                      partition_size)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0

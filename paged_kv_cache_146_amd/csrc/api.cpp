@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int kMaxHeadsGroup = 16;
+constexpr int kMaxBalancedSeqs = 16384;  // unit prefix lives in LDS
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -163,16 +164,23 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
   return rc == 0 ? PKV_OK : rc;
 }
 
-int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                               int32_t max_context_len, int32_t partition_size, size_t* bytes) {
-  if (!bytes || num_seqs < 0 || num_q_heads < 0 || head_dim < 0 || max_context_len < 0 ||
-      partition_size < 0)
+int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                               size_t* bytes) {
+  if (!bytes || num_seqs < 0 || num_q_heads < 0 || num_kv_heads < 1 || head_dim < 0 ||
+      max_context_len < 0)
     return PKV_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return PKV_EINVAL;
   if (partition_size == 0) {
     *bytes = 0;
     return PKV_OK;
   }
-  if (partition_size % 64 != 0) return PKV_EINVAL;
+  if (partition_size == PKV_PARTITION_BALANCED) {
+    const size_t group = (size_t)(num_q_heads / num_kv_heads);
+    *bytes = 2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
+    return PKV_OK;
+  }
+  if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
   const size_t pmax = ((size_t)max_context_len + partition_size - 1) / partition_size;
   *bytes = (size_t)num_seqs * num_q_heads * pmax * ((size_t)head_dim + 2) * sizeof(float);
   return PKV_OK;
@@ -188,12 +196,12 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
                                void* stream) {
   int rc = check_desc(pool);
   if (rc != PKV_OK) return rc;
-  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
-      partition_size < 0)
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
     return PKV_EINVAL;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
   if (num_q_heads / pool->num_kv_heads > kMaxHeadsGroup) return PKV_EUNSUPPORTED;
-  if (partition_size != 0 && partition_size % 64 != 0) return PKV_EINVAL;
+  const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+  if (!balanced && (partition_size < 0 || partition_size % 64 != 0)) return PKV_EINVAL;
   if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EINVAL;
   if (max_context_len > (1 << 30)) return PKV_EUNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
@@ -227,6 +235,28 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   p.ctx_cap = (int)cap;
   p.scale = scale;
 
+  if (balanced) {
+    // one stream of 64-token chunks over every (sequence, kv head) pair, cut evenly
+    const int64_t units = (int64_t)num_seqs * ((cap + 63) / 64) * pool->num_kv_heads;
+    if (num_seqs > kMaxBalancedSeqs || units >= ((int64_t)1 << 31)) return PKV_EUNSUPPORTED;
+    const int group = num_q_heads / pool->num_kv_heads;
+    const size_t slot_bytes = (size_t)group * ((size_t)pool->head_dim + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < 2 * slot_bytes) return PKV_EWORKSPACE;
+    if (!aligned16(workspace)) return PKV_EINVAL;
+    int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim, group);
+    if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
+    const size_t fit = workspace_bytes / (2 * slot_bytes);
+    if ((size_t)nw > fit) nw = (int)fit;
+    float* ws = static_cast<float*>(workspace);
+    p.balanced = 1;
+    p.split = 1;
+    p.num_workers = nw;
+    p.part_out = ws;                                                  // [2*nw][G][D]
+    p.part_max = ws + (size_t)2 * nw * group * pool->head_dim;        // [2*nw][G][2]
+    rc = pkv::launch_decode(p, as_stream(stream));
+    return rc == 0 ? PKV_OK : rc;
+  }
+
   if (partition_size == 0) {
     p.split = 0;
     p.max_parts = 1;
@@ -238,8 +268,8 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
 
   // workspace layout follows max_context_len (the documented P_max)
   size_t need = 0;
-  rc = pkv_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim, max_context_len,
-                                  partition_size, &need);
+  rc = pkv_decode_workspace_bytes(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                                  max_context_len, partition_size, &need);
   if (rc != PKV_OK) return rc;
   const int max_parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
   p.max_parts = max_parts;

@@ -141,6 +141,9 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// a value the caller knows to be equal in all lanes, made provably wave-uniform
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float lane_read(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -163,6 +166,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 // memory latency; with it every load issued before the call stays one
 // dwordx4 request in flight.
 __device__ __forceinline__ void materialize(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Compiler-only fence: memory operations are not moved across it.  Used to pin
+// where a software-pipelined loop issues its next loads, so that two buffers
+// of the same operand are never live at once.
+__device__ __forceinline__ void issue_point() { asm volatile("" ::: "memory"); }
 
 // order this wave's LDS writes before its later LDS reads (wave-local exchange)
 __device__ __forceinline__ void wave_lds_sync() {

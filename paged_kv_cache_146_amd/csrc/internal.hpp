@@ -27,8 +27,14 @@ struct DecodeLaunch {
   int part_size;      // > 0: tokens per partition (multiple of 64)
   int max_parts;      // partitions per sequence covered by the grid
   int split;          // write partials (1) or the final output (0)
+  int balanced;       // balanced wavefront workers (part_out/part_max hold the slots)
+  int num_workers;    // balanced: wavefront workers
   float scale;
 };
+
+// Wavefront workers the balanced decode can keep resident on the current device
+// for this instantiation (CUs x resident waves per CU), computed once per device.
+int balanced_worker_capacity(int kv_dtype, int q_dtype, int head_dim, int group);
 
 // returns a PKV_* status
 int launch_decode(const DecodeLaunch& p, hipStream_t stream);

@@ -43,19 +43,19 @@ def _run(wl, partitions, seqs=None, check_pools=True):
 
 
 def test_tiny_decode_fp32():
-    print(_run(W.tiny_decode(), [0, 64]))
+    print(_run(W.tiny_decode(), [0, 64, -1]))
 
 
 def test_llama3_8b_small():
-    print(_run(W.llama3_8b_decode(small=True), [0, 64, 512]))
+    print(_run(W.llama3_8b_decode(small=True), [0, 64, 512, -1]))
 
 
 def test_long_context_small():
-    print(_run(W.long_context_decode(small=True), [512, 0]))
+    print(_run(W.long_context_decode(small=True), [512, 0, -1]))
 
 
 def test_shared_prefix_small():
-    print(_run(W.shared_prefix_decode(small=True), [0, 256]))
+    print(_run(W.shared_prefix_decode(small=True), [0, 256, -1]))
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64])
@@ -64,7 +64,7 @@ def test_edge_context_lengths(B):
     ctx = sorted({0, 1, max(B - 1, 0), B, B + 1, 2 * B, 63, 64, 65, 129, 300})
     wl = W.make_decode("edge B=%d" % B, 40 + B, ctx_lens=ctx, Hq=8, Hkv=2, D=128, B=B,
                        kv_dtype="bf16", spare_frac=0.1)
-    print(_run(wl, [0, 64, 128]))
+    print(_run(wl, [0, 64, 128, -1]))
 
 
 @pytest.mark.parametrize("kv,Hq,Hkv,D", [
@@ -75,13 +75,13 @@ def test_dtype_head_grid(kv, Hq, Hkv, D):
     """Group sizes 1..16 including non-powers of two, MHA/GQA/MQA, D 64/128, all dtypes."""
     wl = W.make_decode("grid %s %d/%d D%d" % (kv, Hq, Hkv, D), 7 * Hq + D, ctx_range=(1, 700),
                        num_seqs=5, Hq=Hq, Hkv=Hkv, D=D, B=16, kv_dtype=kv, spare_frac=0.1)
-    print(_run(wl, [0, 192]))
+    print(_run(wl, [0, 192, -1]))
 
 
 def test_fp8_q_f16():
     wl = W.make_decode("fp8 kv, f16 q", 77, ctx_range=(50, 600), num_seqs=4, Hq=8, Hkv=2, D=128,
                        B=16, kv_dtype="fp8", q_dtype="f16", fp8_src_dtype="f16")
-    print(_run(wl, [0, 128]))
+    print(_run(wl, [0, 128, -1]))
 
 
 def test_permutation_invariance_bitwise():
@@ -96,7 +96,7 @@ def test_permutation_invariance_bitwise():
     wl2 = W.Workload(**{**wl.__dict__})
     wl2.block_table = pi[wl.block_table]
     b = GpuCase(wl2)
-    for P in (0, 64):
+    for P in (0, 64, -1):
         oa = a.decode(partition_size=P)
         ob = b.decode(partition_size=P)
         assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
@@ -125,16 +125,16 @@ def test_split_reduce_standalone():
 def test_llama3_8b_full_sampled():
     wl = W.llama3_8b_decode()
     seqs = np.array([0, 5, 17, 31, 42, 63], np.int32)
-    print(_run(wl, [512, 256, 0], seqs=seqs))
+    print(_run(wl, [512, 256, 0, -1], seqs=seqs))
 
 
 def test_long_context_full_sampled():
     wl = W.long_context_decode()
-    print(_run(wl, [512], seqs=np.array([int(np.argmax(wl.context_lens)), 3], np.int32),
+    print(_run(wl, [512, -1], seqs=np.array([int(np.argmax(wl.context_lens)), 3], np.int32),
                check_pools=False))
 
 
 def test_shared_prefix_full_sampled():
     wl = W.shared_prefix_decode()
     seqs = np.array([0, 1, 100, 255] + [int(np.argmin(wl.context_lens))], np.int32)
-    print(_run(wl, [0, 512], seqs=seqs))
+    print(_run(wl, [0, 512, -1], seqs=seqs))

@@ -99,12 +99,18 @@ def test_pool_descriptor_validation(desc, status):
 
 
 def test_decode_workspace_bytes():
-    assert pkv.pkv_decode_workspace_bytes(64, 32, 128, 4096, 0) == 0
-    assert pkv.pkv_decode_workspace_bytes(64, 32, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
-    assert pkv.pkv_decode_workspace_bytes(8, 64, 128, 131072, 512) == 8 * 64 * 256 * 130 * 4
-    assert pkv.pkv_decode_workspace_bytes(2, 4, 64, 0, 64) == 0
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) == 0
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
+    assert pkv.pkv_decode_workspace_bytes(8, 64, 8, 128, 131072, 512) == 8 * 64 * 256 * 130 * 4
+    assert pkv.pkv_decode_workspace_bytes(2, 4, 2, 64, 0, 64) == 0
+    # balanced: two partial states per worker, each G x (D + 2) floats
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == 2 * 4096 * 4 * 130 * 4
     with pytest.raises(pkv.PagedKVError):
-        pkv.pkv_decode_workspace_bytes(2, 4, 64, 100, 100)  # not a multiple of 64
+        pkv.pkv_decode_workspace_bytes(2, 4, 2, 64, 100, 100)  # not a multiple of 64
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pkv_decode_workspace_bytes(2, 4, 2, 64, 100, -2)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pkv_decode_workspace_bytes(2, 6, 4, 64, 100, 64)  # heads not divisible
 
 
 def test_validate_block_table():
@@ -137,6 +143,8 @@ def test_decode_argument_errors_caught_on_host():
     assert _decode_raw(num_q_heads=30) == -1          # H_q % H_kv != 0
     assert _decode_raw(num_q_heads=8 * 17) == -3      # group of 17 > 16
     assert _decode_raw(P=100) == -1                   # partition not a multiple of 64
+    assert _decode_raw(P=-2) == -1
+    assert _decode_raw(P=-1) == -1                    # balanced, NULL pointers
     assert _decode_raw(q_dtype=7) == -1
     assert _decode_raw() == -1                        # NULL device pointers
     assert _decode_raw(num_seqs=0) == 0               # nothing to do
