@@ -27,7 +27,9 @@
  *     be checked without a copy; kernels treat them defensively instead (see
  *     each call) so that a bad entry can corrupt results but never memory
  *     outside the caller's buffers.
- *   - All entry points are thread-safe (no global state).
+ *   - All entry points are thread-safe.  The only process-wide state is a
+ *     per-device cache of device properties and an atomic call counter that
+ *     tags balanced-mode calls.
  *
  * Physical pool layout (owned by this library; one pool for K, one for V, per
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
@@ -158,8 +160,13 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
  *     laid out as part_out float [S][H_q][P_max][D], then part_max float [S][H_q][P_max],
  *     then part_sum float [S][H_q][P_max] (the arrays pkv_split_kv_reduce takes).
  *   partition_size == PKV_PARTITION_BALANCED: enough for PKV_MAX_WORKERS workers,
- *     2 * PKV_MAX_WORKERS * (num_q_heads / num_kv_heads) * (head_dim + 2) * 4; the
- *     layout is internal (partial states of the pairs that workers share).
+ *     C + 2 * PKV_MAX_WORKERS * (num_q_heads / num_kv_heads) * (head_dim + 2) * 4 with
+ *     C = num_seqs * num_kv_heads * 8 rounded up to a multiple of 256; the layout is
+ *     internal (a counter per (sequence, kv head), then the partial states of the
+ *     pairs that workers share).  It needs no initialisation: counters written by
+ *     another call are recognised as stale, and every call leaves its counters at
+ *     rest, so the same workspace serves any number of calls (and graph replays);
+ *     calls that share one workspace must not overlap in time.
  * Errors: PKV_EINVAL (negative sizes, num_q_heads % num_kv_heads != 0, any other
  * partition_size that is not a positive multiple of 64). */
 int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -189,7 +196,9 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
  *      algebra; evenly loaded whatever the length mix; num_seqs <= 16384).
  *   workspace: device scratch of pkv_decode_workspace_bytes (NULL if 0 bytes);
  *      in balanced mode a smaller workspace just means fewer workers (it must
- *      hold at least one worker: 2 * G * (head_dim + 2) * 4 bytes).
+ *      hold the counters and one worker: C + 2 * G * (head_dim + 2) * 4 bytes).
+ *      In balanced mode the pairs that several workers share are merged by the
+ *      last of them to finish, inside the same kernel launch.
  *   out: device [num_seqs][num_q_heads][head_dim] of q_dtype (rounded to nearest).
  * Table entries outside [0, num_blocks) are clamped into range (wrong results,
  * never a fault); pkv_validate_block_table checks tables on the host.

@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace {
@@ -44,6 +46,22 @@ int check_desc(const pkv_pool_desc* d) {
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// balanced mode: one 8-byte counter per (sequence, kv head), rounded to 256 bytes
+size_t balanced_counter_bytes(int num_seqs, int num_kv_heads) {
+  const size_t b = (size_t)num_seqs * num_kv_heads * 8;
+  return (b + 255) / 256 * 256;
+}
+
+// a fresh nonzero tag per balanced call (see the counter scheme in decode.hip)
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0x9e3779b9u};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  } while (e == 0);
+  return e;
+}
 
 }  // namespace
 
@@ -177,7 +195,8 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
   }
   if (partition_size == PKV_PARTITION_BALANCED) {
     const size_t group = (size_t)(num_q_heads / num_kv_heads);
-    *bytes = 2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
+    *bytes = balanced_counter_bytes(num_seqs, num_kv_heads) +
+             2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
     return PKV_OK;
   }
   if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
@@ -241,16 +260,20 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
     if (num_seqs > kMaxBalancedSeqs || units >= ((int64_t)1 << 31)) return PKV_EUNSUPPORTED;
     const int group = num_q_heads / pool->num_kv_heads;
     const size_t slot_bytes = (size_t)group * ((size_t)pool->head_dim + 2) * sizeof(float);
-    if (!workspace || workspace_bytes < 2 * slot_bytes) return PKV_EWORKSPACE;
+    const size_t cnt_bytes = balanced_counter_bytes(num_seqs, pool->num_kv_heads);
+    if (!workspace || workspace_bytes < cnt_bytes + 2 * slot_bytes) return PKV_EWORKSPACE;
     if (!aligned16(workspace)) return PKV_EINVAL;
     int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim, group);
     if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
-    const size_t fit = workspace_bytes / (2 * slot_bytes);
+    const size_t fit = (workspace_bytes - cnt_bytes) / (2 * slot_bytes);
     if ((size_t)nw > fit) nw = (int)fit;
-    float* ws = static_cast<float*>(workspace);
+    char* base = static_cast<char*>(workspace);
+    float* ws = reinterpret_cast<float*>(base + cnt_bytes);
     p.balanced = 1;
     p.split = 1;
     p.num_workers = nw;
+    p.counters = reinterpret_cast<unsigned long long*>(base);         // [S][H_kv]
+    p.epoch = next_epoch();
     p.part_out = ws;                                                  // [2*nw][G][D]
     p.part_max = ws + (size_t)2 * nw * group * pool->head_dim;        // [2*nw][G][2]
     rc = pkv::launch_decode(p, as_stream(stream));

@@ -27,7 +27,7 @@
 //         is cut into equal contiguous shares, one per wavefront ("worker").  A
 //         worker finishes every pair it covers entirely and leaves a partial
 //         state for at most two pairs it shares with neighbours; those are
-//         merged by balanced_merge_kernel.  Inside a worker the chunk loop is
+//         merged by the last worker to finish one (a per-pair counter tells it).  Inside a worker the chunk loop is
 //         software-pipelined: the next chunk's table entry and K rows are in
 //         flight while the current chunk's P.V runs.
 #include "device.hpp"
@@ -51,6 +51,7 @@ struct DecodeScalars {
   int split;
   int out_dtype;
   int num_workers;  // balanced kernel: wavefront workers in the grid
+  uint32_t epoch;   // balanced kernel: call tag of the shared-pair counters
   float scale_log2; // softmax scale * log2(e)
 };
 
@@ -447,6 +448,83 @@ __device__ __forceinline__ int worker_of(int u, int U, int NWe) {
   return (int)((((long long)u + 1) * NWe - 1) / U);
 }
 
+// Count one finished piece of a shared (sequence, kv head) pair; returns 1 for the
+// worker that brings the count to npieces.  The counter word holds (epoch << 32 |
+// count): a word from another call (other epoch) counts as zero, and the last
+// finisher leaves (epoch, 0) behind, so no zero-fill is ever needed and replays
+// of the same call stay correct.  Lock-free: a failed exchange means another
+// worker made progress; nothing waits on anyone.
+__device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch, uint32_t npieces) {
+  unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (true) {
+    const uint32_t ep = (uint32_t)(old >> 32), n = (uint32_t)old;
+    const uint32_t n2 = (ep == epoch ? n : 0u) + 1u;
+    const bool last = n2 >= npieces;
+    const unsigned long long nw = ((unsigned long long)epoch << 32) | (last ? 0u : n2);
+    unsigned long long expected = old;
+    if (__hip_atomic_compare_exchange_strong(c, &expected, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return last ? 1 : 0;
+    old = expected;
+  }
+}
+
+// One wavefront merges the partial states of a shared pair (pieces of workers wa..wb,
+// log2-domain maxima) in a single online pass: every piece's (m, l, o) for all heads
+// is loaded together (device-scope loads) and pieces are unrolled, so the merge
+// costs a few memory round trips, not two per head.
+template <int QDT, int D, int GM>
+__device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict__ out,
+                           const DecodeScalars& sc, int s, int kvh, int u0, int wa, int wb,
+                           int U, int NWe, int lane) {
+  constexpr int PER = D / 64;
+  const int first_slot = worker_start(wa, U, NWe) != u0 ? 2 * wa + 1 : 2 * wa;
+  const int stride = sc.G * D;
+  float M[GM], L[GM], O[GM][PER];
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    M[h] = -INFINITY;
+    L[h] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) O[h][k] = 0.0f;
+  }
+#pragma unroll 4
+  for (int w = wa; w <= wb; ++w) {
+    const int slot = w == wa ? first_slot : 2 * w;
+    float m[GM], l[GM], o[GM][PER];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const int hh = h < sc.G ? h : sc.G - 1;
+      float* ml = slot_ml + ((size_t)slot * sc.G + hh) * 2;
+      m[h] = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      l[h] = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float* so = slot_out + (size_t)slot * stride + hh * D + lane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        o[h][k] = __hip_atomic_load(so + 64 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float mn = fmaxf(M[h], m[h]);
+      const float a_old = __builtin_amdgcn_exp2f(M[h] - mn);
+      const float a_new = __builtin_amdgcn_exp2f(m[h] - mn) * l[h];
+      L[h] = L[h] * a_old + a_new;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) O[h][k] = O[h][k] * a_old + a_new * o[h][k];
+      M[h] = mn;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < sc.G) {
+      const float inv = 1.0f / L[h];
+      const size_t orow = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + h) * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) store_any(out, QDT, orow + lane + 64 * k, O[h][k] * inv);
+    }
+  }
+}
+
 template <int KVT, int QDT, int D, int GM>
 // two resident waves per SIMD: the pipeline needs the second wave to cover its gaps
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
@@ -454,8 +532,8 @@ paged_decode_balanced_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out,
-    float* __restrict__ slot_out, float* __restrict__ slot_ml, const DecodeScalars sc) {
+    const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out, float* slot_out,
+    float* slot_ml, unsigned long long* counters, const DecodeScalars sc) {
   using SH = Shape<KVT, QDT, D>;
   constexpr int X = SH::X, ES = SH::ES, NC = SH::NC, R = SH::R, NPASS = SH::NPASS;
   constexpr bool kFp8 = (KVT == DT_FP8);
@@ -466,6 +544,13 @@ paged_decode_balanced_kernel(
 
   unit_prefix(context_lens, sc.S, sc.ctx_cap, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
+  if (blockIdx.x == 0) {  // sequences with an empty context own no unit: their output is zero
+    for (int s0 = 0; s0 < sc.S; ++s0) {
+      if (prefix[s0 + 1] != prefix[s0]) continue;
+      for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads)
+        store_any(out, QDT, (size_t)s0 * sc.Hq * D + i, 0.0f);
+    }
+  }
   const int NWe = min(sc.num_workers, U);
   // wave-uniform values are passed through readfirstlane so that the compiler
   // keeps them (and every address derived from them, q's in particular) scalar
@@ -615,71 +700,44 @@ paged_decode_balanced_kernel(
         }
       }
     } else {
+      // Publish the partial state with device-scope stores (coherent across the
+      // XCDs' L2 caches without whole-cache write-back), wait until they have
+      // completed, and only then count the piece.  The merging worker reads with
+      // device-scope loads.  No cache-wide fence is needed on either side.
       const int slot = 2 * w + (first_piece ? 0 : 1);
       if (lane < NC) {
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
           if (h < sc.G) {
             const float inv = 1.0f / lw[h];
-            float v[X];
+            float* so = slot_out + (size_t)slot * slot_stride + h * D + col * X;
 #pragma unroll
-            for (int e = 0; e < X; ++e) v[e] = pacc[h][e] * inv;
-            store_row<DT_F32, X>(reinterpret_cast<uint8_t*>(slot_out),
-                                 (size_t)slot * slot_stride + h * D + col * X, v);
+            for (int e = 0; e < X; ++e)
+              __hip_atomic_store(so + e, pacc[h][e] * inv, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
       if (lane == 0) {
         for (int h = 0; h < sc.G && h < GM; ++h) {
-          slot_ml[((size_t)slot * sc.G + h) * 2 + 0] = m_run[h];  // log2 units
-          slot_ml[((size_t)slot * sc.G + h) * 2 + 1] = lw[h];
+          float* ml = slot_ml + ((size_t)slot * sc.G + h) * 2;
+          __hip_atomic_store(ml, m_run[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // log2
+          __hip_atomic_store(ml + 1, lw[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+      __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
+      // ---- the last worker to finish a piece of this pair merges all of them
+      const int wa = worker_of(seg_first, U, NWe);
+      const int wb = worker_of(seg_first + seg_units - 1, U, NWe);
+      int last = 0;
+      if (lane == 0)
+        last = claim_last(counters + (size_t)s * sc.Hkv + kvh, sc.epoch, (uint32_t)(wb - wa + 1));
+      last = uniform(last);  // lane 0's answer
+      if (last)
+        merge_pair<QDT, D, GM>(slot_out, slot_ml, out, sc, s, kvh, seg_first, wa, wb, U, NWe, lane);
     }
     first_piece = false;
     u = seg_first + j1;
-  }
-}
-
-// Merge of the pairs that several workers share: one workgroup per (kv head, sequence).
-template <int D>
-__global__ __launch_bounds__(kThreads) void balanced_merge_kernel(
-    const int32_t* __restrict__ context_lens, const float* __restrict__ slot_out,
-    const float* __restrict__ slot_ml, uint8_t* __restrict__ out, const DecodeScalars sc) {
-  extern __shared__ int prefix[];  // [S + 1]
-  __shared__ int tmp[kThreads];
-  unit_prefix(context_lens, sc.S, sc.ctx_cap, sc.Hkv, prefix, tmp);
-  const int U = prefix[sc.S];
-  const int kvh = blockIdx.x, s = blockIdx.y;
-  const int seg_units = (prefix[s + 1] - prefix[s]) / sc.Hkv;
-  if (seg_units == 0) {  // empty context: zeros
-    for (int i = threadIdx.x; i < sc.G * D; i += kThreads)
-      store_any(out, sc.out_dtype, ((size_t)s * sc.Hq + (size_t)kvh * sc.G) * D + i, 0.0f);
-    return;
-  }
-  const int NWe = min(sc.num_workers, U);
-  const int u0 = prefix[s] + kvh * seg_units;
-  const int u1 = u0 + seg_units;
-  const int wa = worker_of(u0, U, NWe), wb = worker_of(u1 - 1, U, NWe);
-  if (wa == wb) return;  // finished by its only worker
-  const int slot_stride = sc.G * D;
-  for (int idx = threadIdx.x; idx < sc.G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int w = wa; w <= wb; ++w) {
-      const int slot = (w == wa && worker_start(wa, U, NWe) != u0) ? 2 * w + 1 : 2 * w;
-      M = fmaxf(M, slot_ml[((size_t)slot * sc.G + h) * 2]);
-    }
-    float L = 0.0f, O = 0.0f;
-    for (int w = wa; w <= wb; ++w) {
-      const int slot = (w == wa && worker_start(wa, U, NWe) != u0) ? 2 * w + 1 : 2 * w;
-      const float m = slot_ml[((size_t)slot * sc.G + h) * 2];
-      const float l = slot_ml[((size_t)slot * sc.G + h) * 2 + 1];
-      const float a = __builtin_amdgcn_exp2f(m - M) * l;
-      L += a;
-      O += a * slot_out[(size_t)slot * slot_stride + h * D + d];
-    }
-    store_any(out, sc.out_dtype, ((size_t)s * sc.Hq + (size_t)kvh * sc.G + h) * D + d, O / L);
   }
 }
 
@@ -759,11 +817,7 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
     hipLaunchKernelGGL((paged_decode_balanced_kernel<KVT, QDT, D, GM>), grid, dim3(kThreads), lds,
                        st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
                        (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
-                       p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, sc);
-    if (hipGetLastError() != hipSuccess) return -5;
-    dim3 mgrid(p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL(balanced_merge_kernel<D>, mgrid, dim3(kThreads), lds, st, p.context_lens,
-                       p.part_out, p.part_max, (uint8_t*)p.out, sc);
+                       p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.counters, sc);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
@@ -815,6 +869,7 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
   sc.split = p.split;
   sc.out_dtype = p.q_dtype;
   sc.num_workers = p.num_workers;
+  sc.epoch = p.epoch;
   sc.scale_log2 = p.scale * kLog2e;
   if (sc.blog2 < 0 || p.block_size > 64) return -3;
   const int kv = p.kv_dtype, qd = p.q_dtype;

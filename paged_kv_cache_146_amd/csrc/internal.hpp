@@ -29,6 +29,8 @@ struct DecodeLaunch {
   int split;          // write partials (1) or the final output (0)
   int balanced;       // balanced wavefront workers (part_out/part_max hold the slots)
   int num_workers;    // balanced: wavefront workers
+  unsigned long long* counters;  // balanced: one per (sequence, kv head)
+  uint32_t epoch;     // balanced: tag of this call for the counters
   float scale;
 };
 
