@@ -34,14 +34,15 @@
  * Physical pool layout (owned by this library; one pool for K, one for V, per
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
  *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *   V pool: [num_blocks][num_kv_heads][block_size][head_dim]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
  *   fp8 scales (K and V separately): float [num_blocks][num_kv_heads]
  * One (block, kv head) page is contiguous in each pool.  The logical element
  * K[block][head][t][d] lives at K pool index
  *   (((block*num_kv_heads + head)*(head_dim/X) + d/X)*block_size + t)*X + d%X
- * and V[block][head][t][d] at ((block*num_kv_heads + head)*block_size + t)*head_dim + d.
- * The K layout lets one lane own one token and read 16 bytes per load while
- * the 16-byte chunks of a wavefront's tokens are consecutive in memory.
+ * and V[block][head][t][d] at ((block*num_kv_heads + head)*head_dim + d)*block_size + t.
+ * Both are the operand layouts of the matrix-core products: 16 bytes of one K
+ * row (X consecutive dims of a token) and 16 bytes of one V column (16/E
+ * consecutive tokens of a dim) are each one lane's load.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

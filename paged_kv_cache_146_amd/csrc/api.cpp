@@ -263,7 +263,8 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
     const size_t cnt_bytes = balanced_counter_bytes(num_seqs, pool->num_kv_heads);
     if (!workspace || workspace_bytes < cnt_bytes + 2 * slot_bytes) return PKV_EWORKSPACE;
     if (!aligned16(workspace)) return PKV_EINVAL;
-    int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim, group);
+    int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim,
+                                           pool->block_size);
     if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
     const size_t fit = (workspace_bytes - cnt_bytes) / (2 * slot_bytes);
     if ((size_t)nw > fit) nw = (int)fit;

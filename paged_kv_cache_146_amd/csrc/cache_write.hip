@@ -7,12 +7,13 @@
 // carry fp32 scales).  "KV Cache: capacity, layout, lifecycle", "Page-table
 // addressing": the cases where the reference raises become padding (-1) here.
 //
-// The scatter works in 16-byte destination pieces: one thread moves one piece
-// of one (token, kv head) row into the K pool ([block][head][D/X][B][X]) or
-// the V pool ([block][head][B][D]).  Bit copies for f32/f16/bf16 pools; for
-// fp8 pools the thread divides 16 source elements by the page's scale (IEEE
-// fp32 division) and encodes them as OCP E4M3 (nearest, ties to even,
-// saturating).
+// The scatter works in 16-byte source pieces: one thread moves one piece of
+// one (token, kv head) row.  In the K pool ([block][head][D/X][B][X]) the piece
+// lands as one 16-byte store; in the V pool ([block][head][D][B], tokens
+// contiguous per dim) its elements go to D-strided slots, one store each.  Bit
+// copies for f32/f16/bf16 pools; for fp8 pools the thread divides 16 source
+// elements by the page's scale (IEEE fp32 division) and encodes them as OCP
+// E4M3 (nearest, ties to even, saturating).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -57,12 +58,23 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
   const long long blk = slot / B, off = slot % B;
   const size_t src = ((size_t)i * Hkv + h) * NC + c;  // in 16-byte pieces
   const size_t page = (size_t)blk * Hkv + h;
-  const size_t kdst = (page * NC + c) * B + off;
-  const size_t vdst = (page * B + off) * NC + c;
-  if (blockIdx.y == 0)
-    reinterpret_cast<u32x4*>(k_pool)[kdst] = reinterpret_cast<const u32x4*>(k)[src];
-  else
-    reinterpret_cast<u32x4*>(v_pool)[vdst] = reinterpret_cast<const u32x4*>(v)[src];
+  if (blockIdx.y == 0) {
+    reinterpret_cast<u32x4*>(k_pool)[(page * NC + c) * B + off] =
+        reinterpret_cast<const u32x4*>(k)[src];
+  } else {
+    constexpr int E = 16 / ES;
+    const u32x4 x = reinterpret_cast<const u32x4*>(v)[src];
+    const size_t d0 = (page * D + (size_t)c * E) * B + off;  // element (dim c E, token off)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t w = x[e * ES / 4];
+      if constexpr (ES == 4)
+        reinterpret_cast<uint32_t*>(v_pool)[d0 + (size_t)e * B] = w;
+      else
+        reinterpret_cast<uint16_t*>(v_pool)[d0 + (size_t)e * B] =
+            (uint16_t)(w >> (16 * (e & 1)));
+    }
+  }
 }
 
 // fp8 pools: 16 source elements of SRC type -> one 16-byte piece of E4M3 codes.
@@ -98,11 +110,14 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
     const float y = __fdiv_rn(x[e], scale);
     w[e >> 2] |= f32_to_e4m3(y) << (8 * (e & 3));
   }
-  const u32x4 packed = {w[0], w[1], w[2], w[3]};
-  if (!isv)
+  if (!isv) {
+    const u32x4 packed = {w[0], w[1], w[2], w[3]};
     reinterpret_cast<u32x4*>(k_pool)[(page * NC + c) * B + off] = packed;
-  else
-    reinterpret_cast<u32x4*>(v_pool)[(page * B + off) * NC + c] = packed;
+  } else {
+    const size_t d0 = (page * D + (size_t)c * 16) * B + off;  // element (dim 16 c, token off)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v_pool[d0 + (size_t)e * B] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+  }
 }
 
 int launch_slot_mapping(const int32_t* block_table, int num_seqs, int W, const int32_t* seq_idx,

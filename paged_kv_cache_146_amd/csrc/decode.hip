@@ -1,5 +1,5 @@
-// decode.hip — paged decode attention for gfx950, plus the split-KV
-// log-sum-exp merges.
+// decode.hip — paged decode attention for gfx950 on the matrix cores, plus the
+// split-KV log-sum-exp merges.
 //
 // Method: "03 | PagedAttention and the KV-cache memory system", §4 — per
 // sequence and query head, walk the logical blocks of the visible context,
@@ -7,17 +7,33 @@
 // attention into an online-softmax state (max, exp_sum, weighted_value); long
 // contexts are scanned in parallel pieces whose states are merged.
 //
-// Shared by all kernels: a wavefront works on 64 consecutive tokens of one
-// (sequence, kv head) at a time ("chunk"), for all G = H_q/H_kv query heads of
-// that kv head, so every K/V byte is read from HBM once per step (GQA grouping).
-//   QK^T  lane = token.  The K pool is [block][head][D/X][B][X]: a lane's 16-byte
-//         loads walk its token's row and the 64 lanes of one load cover
-//         contiguous 16-byte pieces of the pages; the dot product over D stays in
-//         the lane.  q is wave-uniform and read through the scalar cache.
-//   soft  chunk max per head by DPP row ops + lane reads; p = 2^(z - m) with
-//         log2(e) folded into the scale.
-//   P.V   lane = 16-byte slice of one V row (V pool [block][head][B][D]); each
-//         pass covers 64/(D/X) tokens; p comes from LDS.
+// A wavefront works on 64 consecutive tokens of one (sequence, kv head) at a
+// time ("chunk"), for all G = H_q/H_kv query heads of that kv head, so every
+// K/V byte is read from HBM once per step (GQA grouping).  Both products run
+// on 16x16 MFMA tiles with the query heads as the N = 16 columns (heads past G
+// are zero columns):
+//   S^T = K . Q^T   A = 16 K rows (tokens) x 32 dims, from the K pool
+//                   [block][head][D/X][B][X]: one 16-byte piece per lane;
+//                   B = q, loaded once per (sequence, kv head).
+//   O^T = V^T . P^T A = 16 dims x 32 tokens, from the V pool [block][head][D][B]
+//                   (tokens contiguous per dim): one 16-byte piece per lane;
+//                   B = P, which S^T's output layout already leaves in place.
+// Lane L = 16 g + n.  Tile T's row n is token 16 T + n, so each K load of a
+// wavefront reads 16 consecutive tokens of four consecutive K pieces: 1 KB of
+// one page, contiguous.  In S^T's output the lane holds head n at the tokens
+// 16 T + 4 g + r (rows 4 g + r of tile T).  P.V takes its k-slots in the same
+// order, so the online softmax (max over the four lane groups by permlane
+// swaps, p = 2^(z - m) with log2(e) folded into the scale) feeds the second
+// product without any data exchange, and a lane's V operand is two runs of four
+// consecutive tokens of one dim (each V load of a wavefront: 16 dims x 16
+// tokens, contiguous in the V pool).  O^T leaves head n, dims 16 dt + 4 g + r in
+// the lane.  With block_size >= 16 the 16 tokens of a tile share one block, so
+// the table entries of a chunk are wave-uniform (scalar loads).
+//
+// fp8 (OCP E4M3) pages are widened exactly to the query's 16-bit type before
+// the product; K's per-page scale multiplies the scores and V's is folded into
+// P.  P enters the second product as a hi + lo pair of the 16-bit type.  f32
+// pools use the 16x16x4 f32 product with one k-slot per lane.
 //
 // Three ways to cut the work:
 //   unsplit / fixed partitions — one workgroup (4 waves) per (partition, kv
@@ -27,9 +43,12 @@
 //         is cut into equal contiguous shares, one per wavefront ("worker").  A
 //         worker finishes every pair it covers entirely and leaves a partial
 //         state for at most two pairs it shares with neighbours; those are
-//         merged by the last worker to finish one (a per-pair counter tells it).  Inside a worker the chunk loop is
-//         software-pipelined: the next chunk's table entry and K rows are in
-//         flight while the current chunk's P.V runs.
+//         merged by the last worker to finish one (a per-pair counter tells it).
+// Inside a wavefront the chunk loop is software-pipelined on single buffers:
+// the next chunk's K pieces are requested as soon as the current scores are
+// done and its V pieces as soon as the current P.V is done, the table entries
+// one chunk further ahead; two waves share each SIMD, so one computes while the
+// other waits.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -58,6 +77,92 @@ struct DecodeScalars {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float as_f32(uint32_t w) {
+  float f;
+  __builtin_memcpy(&f, &w, 4);
+  return f;
+}
+
+// ---- matrix-core products ---------------------------------------------------------
+template <int CT>
+__device__ __forceinline__ f32x4 mma16(const u32x4 a, const u32x4 b, const f32x4 c) {
+  if constexpr (CT == DT_BF16) {
+    bf16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  } else {
+    f16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// two floats -> one packed pair of CT, round to nearest even
+template <int CT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  uint32_t w;
+  if constexpr (CT == DT_BF16) {
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    __builtin_memcpy(&w, &b, 4);
+  } else {
+    const f16x2 h = __builtin_convertvector(v, f16x2);
+    __builtin_memcpy(&w, &h, 4);
+  }
+  return w;
+}
+
+// one packed pair of CT -> two floats (exact)
+template <int CT>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+  if constexpr (CT == DT_BF16) {
+    return f32x2{bf16_lo(w), bf16_hi(w)};
+  } else {
+    return f32x2{f16_lo(w), f16_hi(w)};
+  }
+}
+
+// eight E4M3 codes (two words) -> eight CT values; exact, as every E4M3 value is
+// representable in bf16 and in f16
+template <int CT>
+__device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  const u32x4 r = {pack2<CT>(a[0], a[1]), pack2<CT>(b[0], b[1]), pack2<CT>(c[0], c[1]),
+                   pack2<CT>(d[0], d[1])};
+  return r;
+}
+
+// max / sum over the four lane groups {L, L^16, L^32, L^48}; every lane of the
+// set gets the same bits (each swap hands both partners the same operand order)
+__device__ __forceinline__ float max_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+}
+__device__ __forceinline__ float sum_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = as_f32(a[0]) + as_f32(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return as_f32(b[0]) + as_f32(b[1]);
+}
+
 __device__ __forceinline__ void store_any(uint8_t* out, int dt, size_t idx, float x) {
   if (dt == DT_F32)
     reinterpret_cast<float*>(out)[idx] = x;
@@ -67,171 +172,14 @@ __device__ __forceinline__ void store_any(uint8_t* out, int dt, size_t idx, floa
     reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(x);
 }
 
-// q elements [c*X, c*X + X) of one (wave-uniform) query row, as floats
-template <int QDT, int X>
-__device__ __forceinline__ void q_chunk_f32(const uint8_t* __restrict__ qrow, int c, float* qf) {
-  if constexpr (QDT == DT_F32) {
-    const float* p = reinterpret_cast<const float*>(qrow) + c * X;
-#pragma unroll
-    for (int i = 0; i < X; ++i) qf[i] = p[i];
+// four consecutive output elements starting at idx (a multiple of 4)
+__device__ __forceinline__ void store4(uint8_t* out, int dt, size_t idx, const f32x4 v) {
+  if (dt == DT_F32) {
+    *reinterpret_cast<f32x4*>(out + idx * 4) = v;
   } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(qrow) + c * (X / 2);
-#pragma unroll
-    for (int i = 0; i < X / 2; ++i) {
-      uint32_t w = p[i];
-      if constexpr (QDT == DT_BF16) {
-        qf[2 * i] = bf16_lo(w);
-        qf[2 * i + 1] = bf16_hi(w);
-      } else {
-        qf[2 * i] = f16_lo(w);
-        qf[2 * i + 1] = f16_hi(w);
-      }
-    }
-  }
-}
-
-template <int KVT, int QDT, int D>
-struct Shape {
-  static constexpr int X = Elem<KVT>::per16;  // elements per 16 bytes
-  static constexpr int ES = Elem<KVT>::bytes;
-  static constexpr int NC = D / X;            // 16-byte pieces per row (= lanes per V row)
-  static constexpr int R = 64 / NC;           // V rows per pass
-  static constexpr int NPASS = 64 / R;        // passes per 64-token chunk
-  static constexpr int QES = (QDT == DT_F32) ? 4 : 2;
-  static_assert(NC <= 64 && 64 % NC == 0, "row must split into 16-byte lane slices");
-};
-
-// acc[h] = <q_h, K row held in kr> for every head of the group
-template <int KVT, int QDT, int D, int GM>
-__device__ __forceinline__ void chunk_scores(const u32x4 (&kr)[Shape<KVT, QDT, D>::NC],
-                                             const uint8_t* const (&qrow)[GM], float (&acc)[GM]) {
-  using S = Shape<KVT, QDT, D>;
-#pragma unroll
-  for (int h = 0; h < GM; ++h) acc[h] = 0.0f;
-  if constexpr (KVT == DT_BF16 || KVT == DT_F16) {
-    // q slices are scalar loads; only the next 16-byte slice of each head is
-    // prefetched (sched_barrier per slice) so q never floods the scalar registers
-    u32x4 qn[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) qn[h] = *reinterpret_cast<const u32x4*>(qrow[h]);
-#pragma unroll
-    for (int c = 0; c < S::NC; ++c) {
-      u32x4 qc[GM];
-#pragma unroll
-      for (int h = 0; h < GM; ++h) qc[h] = qn[h];
-      if (c + 1 < S::NC) {
-#pragma unroll
-        for (int h = 0; h < GM; ++h) qn[h] = *(reinterpret_cast<const u32x4*>(qrow[h]) + c + 1);
-      }
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t kw = kr[c][w], qw = qc[h][w];
-          if constexpr (KVT == DT_BF16)
-            acc[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw), as_bf16x2(qw), acc[h], false);
-          else
-            acc[h] = __builtin_amdgcn_fdot2(as_f16x2(kw), as_f16x2(qw), acc[h], false);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return;
-  }
-#pragma unroll
-  for (int c = 0; c < S::NC; ++c) {
-    {
-      float kf[S::X];
-      unpack16<KVT>(kr[c], kf);
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        float qf[S::X];
-        q_chunk_f32<QDT, S::X>(qrow[h], c, qf);
-#pragma unroll
-        for (int e = 0; e < S::X; ++e) acc[h] = fmaf(kf[e], qf[e], acc[h]);
-      }
-    }
-  }
-}
-
-// online-softmax update for one chunk: new running max, rescale, p to LDS
-template <int X, int GM, bool FP8>
-__device__ __forceinline__ void chunk_softmax(const float (&acc)[GM], bool valid, float zscale,
-                                              float vs, float (&m_run)[GM], float (&l_lane)[GM],
-                                              float (&pacc)[GM][X], float* pl) {
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    const float z = valid ? acc[h] * zscale : -INFINITY;
-    const float mn = fmaxf(m_run[h], wave_max(z));
-    const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mn);
-    const float p = __builtin_amdgcn_exp2f(z - mn);
-    l_lane[h] = l_lane[h] * alpha + p;
-#pragma unroll
-    for (int e = 0; e < X; ++e) pacc[h][e] *= alpha;
-    m_run[h] = mn;
-    pl[h] = FP8 ? p * vs : p;
-  }
-}
-
-// pacc[h][:] += sum over this lane's rows of p[tok][h] * V row slice.  Each pass
-// is fenced off from the next (sched_barrier) with only the next pass's p
-// prefetched, so that no more than one V row is ever held unpacked.  Rows past
-// the context hold garbage: their packed words are zeroed (every storage type
-// decodes all-zero bits to +0) before the unpack, so 0 * NaN never happens.
-template <int KVT, int GM, int X, int R, int NPASS>
-__device__ __forceinline__ void chunk_pv(const u32x4 (&vr)[NPASS], const float* p_wave, int r,
-                                         int n_valid, float (&pacc)[GM][X]) {
-  float pn[GM];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) pn[h] = p_wave[r * GM + h];
-#pragma unroll
-  for (int i = 0; i < NPASS; ++i) {
-    const int tok = i * R + r;
-    float pc[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) pc[h] = pn[h];
-    if (i + 1 < NPASS) {
-#pragma unroll
-      for (int h = 0; h < GM; ++h) pn[h] = p_wave[(tok + R) * GM + h];
-    }
-    const uint32_t keep = tok < n_valid ? 0xffffffffu : 0u;
-    const u32x4 vw = {vr[i][0] & keep, vr[i][1] & keep, vr[i][2] & keep, vr[i][3] & keep};
-    float vf[X];
-    unpack16<KVT>(vw, vf);
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int e = 0; e < X; ++e) pacc[h][e] = fmaf(pc[h], vf[e], pacc[h][e]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// X consecutive outputs of one row, converted to DT and stored with 16-byte stores
-template <int DT, int X>
-__device__ __forceinline__ void store_row(uint8_t* __restrict__ out, size_t elem_idx,
-                                          const float* v) {
-  if constexpr (DT == DT_F32) {
-    u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<float*>(out) + elem_idx);
-#pragma unroll
-    for (int k = 0; k < X / 4; ++k) {
-      const u32x4 w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
-      p[k] = w;
-    }
-  } else {
-    u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + elem_idx);
-#pragma unroll
-    for (int k = 0; k < X / 8; ++k) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = v[8 * k + 2 * i], b = v[8 * k + 2 * i + 1];
-        const uint32_t lo = DT == DT_BF16 ? f32_to_bf16_bits(a) : f32_to_f16_bits(a);
-        const uint32_t hi = DT == DT_BF16 ? f32_to_bf16_bits(b) : f32_to_f16_bits(b);
-        w[i] = lo | (hi << 16);
-      }
-      p[k] = u32x4{w[0], w[1], w[2], w[3]};
-    }
+    const u32x2 w = dt == DT_BF16 ? u32x2{pack2<DT_BF16>(v[0], v[1]), pack2<DT_BF16>(v[2], v[3])}
+                                  : u32x2{pack2<DT_F16>(v[0], v[1]), pack2<DT_F16>(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(out + idx * 2) = w;
   }
 }
 
@@ -239,29 +187,386 @@ __device__ __forceinline__ int clamp_block(int phys, int num_blocks) {
   return phys < 0 ? 0 : (phys >= num_blocks ? num_blocks - 1 : phys);
 }
 
+// ---- per-instantiation geometry ----------------------------------------------------
+// KVT = pool element type, CT = product type (the query's type), D = head dim.
+template <int KVT, int CT, int D>
+struct Cfg {
+  static constexpr int Dim = D;
+  static constexpr int EB = Elem<KVT>::bytes;
+  static constexpr int E = 16 / EB;           // elements per 16-byte piece (the pool's X)
+  static constexpr int NC = D / E;            // pieces per K row
+  static constexpr int NPL = NC / 4;          // K pieces per lane per token (lane group g
+                                              // takes pieces 4 q + g)
+  static constexpr bool F32 = (CT == DT_F32);
+  static constexpr int SPP = F32 ? E : E / 8; // MFMA k-steps per K piece
+  static constexpr int NQ = NPL * SPP;        // q operands
+  static constexpr int NDT = D / 16;          // dim tiles of O^T
+  static constexpr int NK = 4 * NPL;          // K pieces per lane per chunk: [T][q]
+  static constexpr int NV = NDT * 4;          // V pieces per lane per chunk: [dt][T]
+  static constexpr int QEB = F32 ? 4 : 2;     // bytes per q element
+  // chunk buffers in the balanced kernel's software pipeline (a third does not
+  // fit the 256 architectural registers: the compiler parks buffers in AGPRs)
+  static constexpr int NBUF = 2;
+  using QOp = std::conditional_t<F32, float, u32x4>;
+  // a V piece: four consecutive tokens of one dim
+  using VPiece = std::conditional_t<EB == 4, u32x4, std::conditional_t<EB == 2, u32x2, uint32_t>>;
+  static_assert(NPL >= 1, "head_dim too small for four lane groups");
+  static_assert((KVT == DT_F32) == F32, "f32 pools pair with f32 queries only");
+};
+
+template <class C>
+struct Chunk {
+  u32x4 k[C::NK];                // [T][q]: pieces 4 q + g of token 16 T + n
+  typename C::VPiece v[C::NV];  // [dt][T]: dim 16 dt + n, tokens 16 T + 4 g + (0..3)
+};
+
+// per-lane softmax state: head n; m is shared by the four lane groups, l is the
+// lane's own share of the exp-sum
+template <class C>
+struct State {
+  f32x4 acc[C::NDT];
+  float m, l;
+};
+
+template <class C>
+__device__ __forceinline__ void state_init(State<C>& st) {
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) st.acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.m = -INFINITY;
+  st.l = 0.0f;
+}
+
+// q operands (B of S^T = K . Q^T) for the kv head's G query heads.  Lanes of
+// heads >= G load head 0's row; q_live() zeroes those columns afterwards (kept
+// apart so that a prefetch of the next pair's q does not wait on its own load).
+// Operand (pq, h) of lane group g covers the dims of K piece c = 4 pq + g, step h.
+template <class C>
+__device__ __forceinline__ void load_q(typename C::QOp (&qop)[C::NQ],
+                                       const uint8_t* __restrict__ q, int s, int kvh,
+                                       const DecodeScalars& sc, int n, int g) {
+  const bool live = n < sc.G;
+  const uint8_t* row =
+      q + ((size_t)s * sc.Hq + (size_t)kvh * sc.G + (live ? n : 0)) * C::Dim * C::QEB;
+#pragma unroll
+  for (int pq = 0; pq < C::NPL; ++pq) {
+    const int c = 4 * pq + g;
+    if constexpr (C::F32) {  // four dims per piece, one per step
+      const u32x4 w = *reinterpret_cast<const u32x4*>(row + (size_t)c * 16);
+#pragma unroll
+      for (int h = 0; h < C::SPP; ++h) qop[pq * C::SPP + h] = as_f32(w[h]);
+    } else {  // eight dims per step: [c E + 8 h, c E + 8 h + 8)
+#pragma unroll
+      for (int h = 0; h < C::SPP; ++h)
+        qop[pq * C::SPP + h] = *reinterpret_cast<const u32x4*>(row + ((size_t)c * C::E + 8 * h) * 2);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void q_live(typename C::QOp (&dst)[C::NQ],
+                                       const typename C::QOp (&src)[C::NQ], bool live) {
+#pragma unroll
+  for (int k = 0; k < C::NQ; ++k) {
+    if constexpr (C::F32)
+      dst[k] = live ? src[k] : 0.0f;
+    else
+      dst[k] = live ? src[k] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// ---- loads of one chunk (block_size >= 16) ------------------------------------------
+// Tile T's tokens 16 T .. 16 T + 15 lie in one block, so the chunk needs four
+// wave-uniform table entries.  Tiles at or past `end` are clamped onto the last
+// visible block (their values are masked).
+struct Pages {
+  int b[4];
+};
+
+__device__ __forceinline__ Pages pages_of(const int32_t* __restrict__ trow, int base, int end,
+                                          const DecodeScalars& sc) {
+  Pages pg;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int t = uniform(min(base + 16 * T, end - 1));
+    pg.b[T] = uniform(clamp_block(trow[t >> sc.blog2], sc.num_blocks));
+  }
+  return pg;
+}
+
+template <class C>
+__device__ __forceinline__ void issue_k(u32x4 (&kr)[C::NK], const uint8_t* __restrict__ k_pool,
+                                        const Pages& pg, int kvh, const DecodeScalars& sc, int n,
+                                        int g) {
+  const int B = 1 << sc.blog2;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B +
+                      ((16 * T) & (B - 1)) + n + (size_t)g * B;
+#pragma unroll
+    for (int pq = 0; pq < C::NPL; ++pq) kr[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
+                                        const uint8_t* __restrict__ v_pool, const Pages& pg,
+                                        int kvh, const DecodeScalars& sc, int n, int g) {
+  using VP = typename C::VPiece;
+  const int B = 1 << sc.blog2;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
+    const uint8_t* vp = v_pool + ((page * C::Dim + n) * B + ((16 * T) & (B - 1)) + 4 * g) * C::EB;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+      vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * B * C::EB);
+  }
+}
+
+// fp8 page scales of the chunk's tiles
+__device__ __forceinline__ void page_scales(float (&ks)[4], float (&vs)[4],
+                                            const float* __restrict__ k_scale,
+                                            const float* __restrict__ v_scale, const Pages& pg,
+                                            int kvh, const DecodeScalars& sc) {
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
+    ks[T] = k_scale[page];
+    vs[T] = v_scale[page];
+  }
+}
+
+// ---- loads of one chunk (block_size < 16): every token looks up its own block -----
+template <class C>
+__device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float (&vs)[16],
+                                           const uint8_t* __restrict__ k_pool,
+                                           const uint8_t* __restrict__ v_pool,
+                                           const float* __restrict__ k_scale,
+                                           const float* __restrict__ v_scale,
+                                           const int32_t* __restrict__ trow, int base, int end,
+                                           int kvh, const DecodeScalars& sc, int n, int g) {
+  const int B = 1 << sc.blog2;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int t = min(base + 16 * T + n, end - 1);
+    const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
+    const u32x4* kp =
+        reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B + (t & (B - 1)) + (size_t)g * B;
+#pragma unroll
+    for (int pq = 0; pq < C::NPL; ++pq) ch.k[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
+  }
+  uint32_t w[C::NV][4];
+#pragma unroll
+  for (int a = 0; a < C::NV; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w[a][b] = 0u;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * T + e;  // the lane's score index of this token
+      const int t = min(base + 16 * T + 4 * g + e, end - 1);
+      const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
+      if constexpr (C::EB == 1) {
+        ks[i] = k_scale[page];
+        vs[i] = v_scale[page];
+      } else {
+        ks[i] = vs[i] = 1.0f;
+      }
+      const size_t e0 = (page * C::Dim + n) * B + (t & (B - 1));  // element of dim n
+      const int word = e * C::EB / 4, sh = (e * C::EB % 4) * 8;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const size_t el = e0 + (size_t)16 * dt * B;
+        uint32_t x;
+        if constexpr (C::EB == 4)
+          x = reinterpret_cast<const uint32_t*>(v_pool)[el];
+        else if constexpr (C::EB == 2)
+          x = reinterpret_cast<const uint16_t*>(v_pool)[el];
+        else
+          x = v_pool[el];
+        w[dt * 4 + T][word] |= x << sh;
+      }
+    }
+#pragma unroll
+  for (int a = 0; a < C::NV; ++a) {
+    if constexpr (C::EB == 4)
+      ch.v[a] = u32x4{w[a][0], w[a][1], w[a][2], w[a][3]};
+    else if constexpr (C::EB == 2)
+      ch.v[a] = u32x2{w[a][0], w[a][1]};
+    else
+      ch.v[a] = w[a][0];
+  }
+}
+
+// ---- the two products and the online softmax of one chunk ------------------------
+template <class C, int KVT, int CT>
+__device__ __forceinline__ void chunk_qk(f32x4 (&S)[4], const u32x4 (&kr)[C::NK],
+                                         const typename C::QOp (&qop)[C::NQ]) {
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int pq = 0; pq < C::NPL; ++pq) {
+      const u32x4 piece = kr[T * C::NPL + pq];
+#pragma unroll
+      for (int h = 0; h < C::SPP; ++h) {
+        if constexpr (C::F32)
+          acc = mma_f32(as_f32(piece[h]), qop[pq * C::SPP + h], acc);
+        else if constexpr (KVT == DT_FP8)
+          acc = mma16<CT>(fp8x8<CT>(piece[2 * h], piece[2 * h + 1]), qop[pq * C::SPP + h], acc);
+        else
+          acc = mma16<CT>(piece, qop[pq], acc);
+      }
+    }
+    S[T] = acc;
+  }
+}
+
+// zero the V elements of masked tokens (0xFF-filled or stale slots may hold NaN,
+// and 0 * NaN would poison the product).  Piece [dt][T] holds tokens
+// 16 T + 4 g + e, e < 4; a token is visible when below nvalid.
+template <class C>
+__device__ __forceinline__ void mask_v(typename C::VPiece (&vr)[C::NV], int nvalid, int g) {
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int t0 = 16 * T + 4 * g;
+      auto& x = vr[dt * 4 + T];
+      if constexpr (C::EB == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = t0 + e < nvalid ? x[e] : 0u;
+      } else if constexpr (C::EB == 2) {
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd) {
+          const uint32_t m = (t0 + 2 * wd < nvalid ? 0x0000ffffu : 0u) |
+                             (t0 + 2 * wd + 1 < nvalid ? 0xffff0000u : 0u);
+          x[wd] &= m;
+        }
+      } else {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m |= t0 + e < nvalid ? (0xffu << (8 * e)) : 0u;
+        x &= m;
+      }
+    }
+}
+
+// Scores x[4 T + r] belong to token 16 T + 4 g + r.  NS = scale values per lane:
+// 4 (one page per tile, block_size >= 16) or 16 (one per token).
+template <class C, int KVT, int CT, int NS>
+__device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[4],
+                                                 typename C::VPiece (&vr)[C::NV], float zscale,
+                                                 const float (&ks)[NS], const float (&vs)[NS],
+                                                 int nvalid, int g) {
+  constexpr bool kFp8 = (KVT == DT_FP8);
+  float x[16];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * T + r;
+      x[i] = S[T][r] * (kFp8 ? zscale * ks[NS == 4 ? T : i] : zscale);
+    }
+  if (nvalid < 64) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * T + r] = 16 * T + 4 * g + r < nvalid ? x[4 * T + r] : -INFINITY;
+    mask_v<C>(vr, nvalid, g);
+  }
+  float cm = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) cm = fmaxf(cm, x[i]);
+  cm = max_groups(cm);  // finite: token 0 of every chunk is visible
+  const float mn = fmaxf(st.m, cm);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+  st.m = mn;
+  float p[16], ps = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[i] - mn);
+    ps += p[i];
+  }
+  st.l = st.l * alpha + ps;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) st.acc[dt] *= alpha;
+  }
+  if constexpr (C::F32) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const u32x4 piece = vr[dt * 4 + T];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.acc[dt] = mma_f32(as_f32(piece[r]), p[4 * T + r], st.acc[dt]);
+      }  // the f32 pool: VPiece is u32x4
+  } else {
+    // P = hi + lo, both in CT: the pair carries about twice CT's significand, so
+    // the weights reach the product essentially unrounded (a single 16-bit P
+    // would cost up to 2^-9 relative per term, visible where outputs cancel)
+    u32x4 phi[2], plo[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int i0 = 8 * s2 + 2 * wd;
+        float a = p[i0], b = p[i0 + 1];
+        if constexpr (kFp8) {
+          a *= vs[NS == 4 ? (i0 >> 2) : i0];
+          b *= vs[NS == 4 ? (i0 >> 2) : i0 + 1];
+        }
+        wh[wd] = pack2<CT>(a, b);
+        const f32x2 h = unpack2<CT>(wh[wd]);
+        wl[wd] = pack2<CT>(a - h[0], b - h[1]);
+      }
+      phi[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+      plo[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        // slots 0-3: tokens 32 s2 + 4 g + (0..3) (tile 2 s2); 4-7: tile 2 s2 + 1
+        u32x4 a;
+        if constexpr (kFp8) {
+          a = fp8x8<CT>(vr[dt * 4 + 2 * s2], vr[dt * 4 + 2 * s2 + 1]);
+        } else {
+          const u32x2 lo = vr[dt * 4 + 2 * s2], hi = vr[dt * 4 + 2 * s2 + 1];
+          a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        st.acc[dt] = mma16<CT>(a, phi[s2], st.acc[dt]);
+        st.acc[dt] = mma16<CT>(a, plo[s2], st.acc[dt]);
+      }
+  }
+}
+
 // =================================================================================
 // Kernel A: one workgroup per (partition, kv head, sequence)
 // =================================================================================
-template <int KVT, int QDT, int D, int GM>
-__global__ __launch_bounds__(kThreads) void paged_decode_kernel(
+template <int KVT, int CT, int D, bool SMALLB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out,
     float* __restrict__ part_out, float* __restrict__ part_max, float* __restrict__ part_sum,
     const DecodeScalars sc) {
-  using SH = Shape<KVT, QDT, D>;
-  constexpr int X = SH::X, ES = SH::ES, NC = SH::NC, R = SH::R, NPASS = SH::NPASS;
+  using C = Cfg<KVT, CT, D>;
   constexpr bool kFp8 = (KVT == DT_FP8);
 
-  __shared__ float p_lds[kWaves][64 * GM];
-  __shared__ float c_acc[kWaves][GM][D];
-  __shared__ float c_m[kWaves][GM];
-  __shared__ float c_l[kWaves][GM];
+  __shared__ float c_acc[kWaves][16][D];
+  __shared__ float c_m[kWaves][16];
+  __shared__ float c_l[kWaves][16];
 
   const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int B = 1 << sc.blog2;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
 
   int ctx = context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > sc.ctx_cap ? sc.ctx_cap : ctx);
@@ -277,84 +582,76 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     return;
   }
 
-  const uint8_t* qrow[GM];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    int hq = kvh * sc.G + (h < sc.G ? h : sc.G - 1);
-    qrow[h] = q + ((size_t)s * sc.Hq + hq) * D * SH::QES;
-  }
-
-  float m_run[GM], l_lane[GM];
-  float pacc[GM][X];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    m_run[h] = -INFINITY;
-    l_lane[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < X; ++e) pacc[h][e] = 0.0f;
-  }
-
-  const int r = lane / NC, col = lane % NC;
+  typename C::QOp qop[C::NQ];
+  load_q<C>(qop, q, s, kvh, sc, n, g);
+  q_live<C>(qop, qop, n < sc.G);
+  State<C> st;
+  state_init(st);
   const int32_t* trow = block_table + (size_t)s * sc.W;
-  float* pw = p_lds[wave];
+  const int nch = (t_end - t_begin + 63) >> 6;
+  const int cnt = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;  // chunks wave, wave+4, ...
+  auto base_of = [&](int i) { return t_begin + 64 * (wave + kWaves * min(i, cnt - 1)); };
 
-  for (int cbase = t_begin + wave * 64; cbase < t_end; cbase += kThreads) {
-    const int t = cbase + lane;
-    const bool valid = t < t_end;
-    const int tt = valid ? t : cbase;  // masked lanes address a valid token
-    const int phys = clamp_block(trow[tt >> sc.blog2], sc.num_blocks);
-    const size_t page = (size_t)phys * sc.Hkv + kvh;
-    const int off = tt & (B - 1);
-    const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + (page * NC * B + off);
-    const uint32_t vrow = (uint32_t)(page * B + off);
-
-    u32x4 kr[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = kp[(size_t)c * B];
-    u32x4 vr[NPASS];
-#pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      uint32_t rowi = (uint32_t)__builtin_amdgcn_ds_bpermute((i * R + r) << 2, (int)vrow);
-      vr[i] = *(reinterpret_cast<const u32x4*>(v_pool + (size_t)rowi * (D * ES)) + col);
+  if constexpr (SMALLB) {
+    for (int i = 0; i < cnt; ++i) {
+      const int base = base_of(i);
+      Chunk<C> ch;
+      float ks[16], vs[16];
+      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g);
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, ch.k, qop);
+      chunk_softmax_pv<C, KVT, CT, 16>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g);
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) materialize(kr[c]);
-
-    float acc[GM];
-    chunk_scores<KVT, QDT, D, GM>(kr, qrow, acc);
-    float zscale = sc.scale_log2, vs = 1.0f;
-    if constexpr (kFp8) {
-      zscale *= k_scale[page];
-      vs = v_scale[page];
+  } else if (cnt > 0) {
+    // Single-buffered pipeline: chunk i+1's K pieces are requested as soon as
+    // chunk i's scores are computed and its V pieces as soon as chunk i's P.V is
+    // done; the table entries run one chunk further ahead.  The load order keeps
+    // every wait on the in-order memory counter narrow (K(i) never waits for
+    // V(i), and so on).
+    Chunk<C> R;
+    float ks0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vs0[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    {
+      const Pages p0 = pages_of(trow, base_of(0), t_end, sc);
+      issue_k<C>(R.k, k_pool, p0, kvh, sc, n, g);
+      if constexpr (kFp8) page_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc);
+      issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
     }
-    chunk_softmax<X, GM, kFp8>(acc, valid, zscale, vs, m_run, l_lane, pacc, pw + lane * GM);
-    wave_lds_sync();
-    chunk_pv<KVT, GM, X, R, NPASS>(vr, pw, r, t_end - cbase, pacc);
-    wave_lds_sync();  // p_lds is rewritten by the next chunk
+    Pages p1 = pages_of(trow, base_of(1), t_end, sc);
+    for (int i = 0; i < cnt; ++i) {
+      const int b0 = base_of(i);
+      const bool more = i + 1 < cnt;
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, R.k, qop);
+      issue_point();
+      float ks1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vs1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      Pages p2 = p1;
+      if (more) {
+        issue_k<C>(R.k, k_pool, p1, kvh, sc, n, g);
+        if constexpr (kFp8) page_scales(ks1, vs1, k_scale, v_scale, p1, kvh, sc);
+        p2 = pages_of(trow, base_of(i + 2), t_end, sc);
+      }
+      issue_point();
+      chunk_softmax_pv<C, KVT, CT, 4>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0), g);
+      issue_point();
+      if (more) issue_v<C>(R.v, v_pool, p1, kvh, sc, n, g);
+      issue_point();
+      p1 = p2;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        ks0[T] = ks1[T];
+        vs0[T] = vs1[T];
+      }
+    }
   }
 
-  // ---- combine the rows of each wave, then the waves --------------------------
+  // ---- merge the four waves' states in LDS ------------------------------------------
+  const float lw = sum_groups(st.l);
 #pragma unroll
-  for (int h = 0; h < GM; ++h)
-#pragma unroll
-    for (int e = 0; e < X; ++e)
-#pragma unroll
-      for (int o = NC; o < 64; o <<= 1) pacc[h][e] += __shfl_xor(pacc[h][e], o);
-  float lw[GM];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) lw[h] = wave_sum(l_lane[h]);
-  if (lane < NC) {
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int e = 0; e < X; ++e) c_acc[wave][h][col * X + e] = pacc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      c_m[wave][h] = m_run[h];
-      c_l[wave][h] = lw[h];
-    }
+  for (int dt = 0; dt < C::NDT; ++dt)
+    *reinterpret_cast<f32x4*>(&c_acc[wave][n][16 * dt + 4 * g]) = st.acc[dt];
+  if (g == 0) {
+    c_m[wave][n] = st.m;
+    c_l[wave][n] = lw;
   }
   __syncthreads();
 
@@ -470,77 +767,67 @@ __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch,
 }
 
 // One wavefront merges the partial states of a shared pair (pieces of workers wa..wb,
-// log2-domain maxima) in a single online pass: every piece's (m, l, o) for all heads
-// is loaded together (device-scope loads) and pieces are unrolled, so the merge
-// costs a few memory round trips, not two per head.
-template <int QDT, int D, int GM>
+// log2-domain maxima) in a single online pass over the pieces.  Lane (n, g) takes
+// head n and dims 16 dt + 4 g + r, the layout the pieces were written in.  Reads
+// are device-scope loads, matching the device-scope stores of the writers.
+template <int QDT, int D>
 __device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict__ out,
                            const DecodeScalars& sc, int s, int kvh, int u0, int wa, int wb,
-                           int U, int NWe, int lane) {
-  constexpr int PER = D / 64;
+                           int U, int NWe, int n, int g) {
+  constexpr int NDT = D / 16;
   const int first_slot = worker_start(wa, U, NWe) != u0 ? 2 * wa + 1 : 2 * wa;
-  const int stride = sc.G * D;
-  float M[GM], L[GM], O[GM][PER];
+  const int hh = n < sc.G ? n : sc.G - 1;
+  float M = -INFINITY, L = 0.0f;
+  f32x4 O[NDT];
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    M[h] = -INFINITY;
-    L[h] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) O[h][k] = 0.0f;
-  }
-#pragma unroll 4
+  for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int w = wa; w <= wb; ++w) {
     const int slot = w == wa ? first_slot : 2 * w;
-    float m[GM], l[GM], o[GM][PER];
+    float* ml = slot_ml + ((size_t)slot * sc.G + hh) * 2;
+    const float m = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float l = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float* so = slot_out + ((size_t)slot * sc.G + hh) * D + 4 * g;
+    f32x4 o[NDT];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const int hh = h < sc.G ? h : sc.G - 1;
-      float* ml = slot_ml + ((size_t)slot * sc.G + hh) * 2;
-      m[h] = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      l[h] = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      float* so = slot_out + (size_t)slot * stride + hh * D + lane;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int k = 0; k < PER; ++k)
-        o[h][k] = __hip_atomic_load(so + 64 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+      for (int r = 0; r < 4; ++r)
+        o[dt][r] = __hip_atomic_load(so + 16 * dt + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mn = fmaxf(M, m);
+    const float a_old = __builtin_amdgcn_exp2f(M - mn);
+    const float a_new = __builtin_amdgcn_exp2f(m - mn) * l;
+    L = L * a_old + a_new;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float mn = fmaxf(M[h], m[h]);
-      const float a_old = __builtin_amdgcn_exp2f(M[h] - mn);
-      const float a_new = __builtin_amdgcn_exp2f(m[h] - mn) * l[h];
-      L[h] = L[h] * a_old + a_new;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) O[h][k] = O[h][k] * a_old + a_new * o[h][k];
-      M[h] = mn;
-    }
+    for (int dt = 0; dt < NDT; ++dt) O[dt] = O[dt] * a_old + o[dt] * a_new;
+    M = mn;
   }
+  if (n < sc.G) {
+    const float inv = 1.0f / L;
+    const size_t orow = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + n) * D + 4 * g;
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < sc.G) {
-      const float inv = 1.0f / L[h];
-      const size_t orow = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + h) * D;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) store_any(out, QDT, orow + lane + 64 * k, O[h][k] * inv);
-    }
+    for (int dt = 0; dt < NDT; ++dt) store4(out, QDT, orow + 16 * dt, O[dt] * inv);
   }
 }
 
-template <int KVT, int QDT, int D, int GM>
-// two resident waves per SIMD: the pipeline needs the second wave to cover its gaps
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// where a worker is in the unit stream: unit u = chunk j of pair (s, kvh), the
+// k-th unit of the worker's share
+struct Pos {
+  int u, s, kvh, j, nch, ctx, k;
+};
+
+template <int KVT, int CT, int D, bool SMALLB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_balanced_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
     const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out, float* slot_out,
     float* slot_ml, unsigned long long* counters, const DecodeScalars sc) {
-  using SH = Shape<KVT, QDT, D>;
-  constexpr int X = SH::X, ES = SH::ES, NC = SH::NC, R = SH::R, NPASS = SH::NPASS;
+  using C = Cfg<KVT, CT, D>;
   constexpr bool kFp8 = (KVT == DT_FP8);
 
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
-  __shared__ float p_lds[kWaves][64 * GM];
 
   unit_prefix(context_lens, sc.S, sc.ctx_cap, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
@@ -548,197 +835,258 @@ paged_decode_balanced_kernel(
     for (int s0 = 0; s0 < sc.S; ++s0) {
       if (prefix[s0 + 1] != prefix[s0]) continue;
       for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads)
-        store_any(out, QDT, (size_t)s0 * sc.Hq * D + i, 0.0f);
+        store_any(out, CT, (size_t)s0 * sc.Hq * D + i, 0.0f);
     }
   }
   const int NWe = min(sc.num_workers, U);
-  // wave-uniform values are passed through readfirstlane so that the compiler
-  // keeps them (and every address derived from them, q's in particular) scalar
+  // wave-uniform values go through readfirstlane so that the compiler keeps them,
+  // and the addresses derived from them, scalar
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
   const int w = blockIdx.x * kWaves + wave;
   if (w >= NWe) return;  // no barrier below this point
   const int u_begin = worker_start(w, U, NWe);
   const int u_end = worker_start(w + 1, U, NWe);
 
-  const int B = 1 << sc.blog2;
-  const int r = lane / NC, col = lane % NC;
-  float* pw = p_lds[wave];
-  const int slot_stride = sc.G * D;
-
-  int u = u_begin;
-  bool first_piece = true;
-  while (u < u_end) {
-    // ---- locate the (sequence, kv head) pair of unit u and this worker's piece of it
-    const int s = uniform(find_seq(prefix, sc.S, u));
-    const int pfx = uniform(prefix[s]);
-    const int seg_units = uniform((prefix[s + 1] - pfx) / sc.Hkv);  // chunks per kv head
+  auto clamp_ctx = [&](int s) {
+    const int c = context_lens[s];
+    return uniform(c < 0 ? 0 : (c > sc.ctx_cap ? sc.ctx_cap : c));
+  };
+  auto locate = [&](int u) {
+    Pos p;
+    p.u = u;
+    p.s = uniform(find_seq(prefix, sc.S, u));
+    const int pfx = uniform(prefix[p.s]);
+    p.nch = uniform((prefix[p.s + 1] - pfx) / sc.Hkv);
     const int rel = u - pfx;
-    const int kvh = rel / seg_units;
-    const int j0 = rel - kvh * seg_units;
-    const int seg_first = pfx + kvh * seg_units;
-    const int j1 = min(seg_units, u_end - seg_first);
-    int ctx = context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > sc.ctx_cap ? sc.ctx_cap : ctx);
+    p.kvh = rel / p.nch;
+    p.j = rel - p.kvh * p.nch;
+    p.ctx = clamp_ctx(p.s);
+    return p;
+  };
+  // the unit after p, or p itself at the end of the share (its loads are then
+  // repeated and never used)
+  const int n_units = u_end - u_begin;
+  auto first_pos = [&]() {
+    Pos p = locate(u_begin);
+    p.k = 0;
+    return p;
+  };
+  // the unit after p, or p itself after the last one (its loads are then never
+  // issued)
+  auto advance = [&](Pos p) {
+    if (p.k + 1 >= n_units) return p;
+    ++p.u;
+    ++p.k;
+    if (++p.j < p.nch) return p;
+    p.j = 0;
+    if (++p.kvh < sc.Hkv) return p;
+    p.kvh = 0;
+    do {
+      ++p.s;
+    } while (prefix[p.s + 1] == prefix[p.s]);  // stops: unit p.u exists
+    p.s = uniform(p.s);
+    p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
+    p.ctx = clamp_ctx(p.s);
+    return p;
+  };
+  // a piece ends at the last chunk of its pair or of the worker's share
+  auto piece_ends = [&](const Pos& p) { return p.j == p.nch - 1 || p.k + 1 >= n_units; };
+  auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W; };
 
-    const uint8_t* qrow[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      int hq = kvh * sc.G + (h < sc.G ? h : sc.G - 1);
-      qrow[h] = q + ((size_t)s * sc.Hq + hq) * D * SH::QES;
-    }
-    const int32_t* trow = block_table + (size_t)s * sc.W;
+  State<C> st;
+  state_init(st);
+  typename C::QOp qop[C::NQ];
+  Pos pc = first_pos();
+  load_q<C>(qop, q, pc.s, pc.kvh, sc, n, g);
+  q_live<C>(qop, qop, n < sc.G);
+  int piece_j0 = pc.j, piece_u0 = pc.u;
 
-    float m_run[GM], l_lane[GM];
-    float pacc[GM][X];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      m_run[h] = -INFINITY;
-      l_lane[h] = 0.0f;
-#pragma unroll
-      for (int e = 0; e < X; ++e) pacc[h][e] = 0.0f;
-    }
+  // Shared pairs whose piece this worker has published but not yet counted: at
+  // most the first and the last piece of the share.  A piece is counted only
+  // after its stores have completed; the wait for that comes at the end of the
+  // share, where no prefetched chunk is in flight (the vector-memory counter
+  // covers loads and stores alike, so an earlier wait would drain the pipeline).
+  int pend_s0 = 0, pend_k0 = 0, pend_n0 = 0, pend_s1 = 0, pend_k1 = 0, pend_n1 = 0;
+  int n_pend = 0;
+  auto claim = [&](int ps, int pk, int pn) {
+    ps = uniform(ps);
+    pk = uniform(pk);
+    pn = uniform(pn);
+    const int seg_first = uniform(prefix[ps]) + pk * pn;
+    const int wa = worker_of(seg_first, U, NWe);
+    const int wb = worker_of(seg_first + pn - 1, U, NWe);
+    int last = 0;
+    if (lane == 0)
+      last = claim_last(counters + (size_t)ps * sc.Hkv + pk, sc.epoch, (uint32_t)(wb - wa + 1));
+    last = uniform(last);  // lane 0's answer
+    if (last) merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
+  };
+  auto claim_pending = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);  // every store of the pieces has completed
+    if (n_pend > 0) claim(pend_s0, pend_k0, pend_n0);
+    if (n_pend > 1) claim(pend_s1, pend_k1, pend_n1);
+    n_pend = 0;
+  };
 
-    // token-lane addressing of chunk j: masked lanes address the chunk's first token
-    auto lane_token = [&](int j) {
-      const int t = j * 64 + lane;
-      return t < ctx ? t : j * 64;
-    };
-    // ---- prologue: table entry and K rows of the first chunk
-    int tt = lane_token(j0);
-    int phys = clamp_block(trow[tt >> sc.blog2], sc.num_blocks);
-    u32x4 kr[NC];
-    {
-      const size_t page = (size_t)phys * sc.Hkv + kvh;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + (page * NC * B + (tt & (B - 1)));
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kr[c] = kp[(size_t)c * B];
-    }
-
-    // Chunk j; chunk j+1's table entry is fetched during the scores and its K
-    // rows during P.V, overwriting kr only after K(j) is dead.  On the piece's
-    // last chunk the "next" chunk is the same one (a re-read, never used).
-    for (int j = j0; j < j1; ++j) {
-      const size_t page = (size_t)phys * sc.Hkv + kvh;
-      const int off = tt & (B - 1);
-      const bool valid = j * 64 + lane < ctx;
-      u32x4 vr[NPASS];
-      if (B >= R) {
-        // The R rows of pass i are consecutive tokens of one page (R divides B), so the
-        // page is wave-uniform: its table entry comes through the scalar cache and the
-        // lane's byte offset inside the pass is just lane*16.  Passes wholly past the
-        // context re-read the last valid group of rows (selected out later).
-#pragma unroll
-        for (int i = 0; i < NPASS; ++i) {
-          const int tok0 = j * 64 + i * R;
-          const int tokc = uniform(tok0 < ctx ? tok0 : ((ctx - 1) & ~(R - 1)));
-          const int pv = clamp_block(trow[tokc >> sc.blog2], sc.num_blocks);
-          const size_t row0 = ((size_t)pv * sc.Hkv + kvh) * B + (tokc & (B - 1));
-          vr[i] = *reinterpret_cast<const u32x4*>(v_pool + row0 * (D * ES) + lane * 16);
-        }
-      } else {
-        const uint32_t vrow = (uint32_t)(page * B + off);
-#pragma unroll
-        for (int i = 0; i < NPASS; ++i) {
-          uint32_t rowi = (uint32_t)__builtin_amdgcn_ds_bpermute((i * R + r) << 2, (int)vrow);
-          vr[i] = *(reinterpret_cast<const u32x4*>(v_pool + (size_t)rowi * (D * ES)) + col);
-        }
-      }
-      const int jn = uniform(j + 1 < j1 ? j + 1 : j);
-      const int tt_next = lane_token(jn);
-      const int phys_next_raw = trow[tt_next >> sc.blog2];
-      float zscale = sc.scale_log2, vs = 1.0f;
-      if constexpr (kFp8) {
-        zscale *= k_scale[page];
-        vs = v_scale[page];
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) materialize(kr[c]);
-      issue_point();
-
-      float acc[GM];
-      chunk_scores<KVT, QDT, D, GM>(kr, qrow, acc);
-      chunk_softmax<X, GM, kFp8>(acc, valid, zscale, vs, m_run, l_lane, pacc, pw + lane * GM);
-      issue_point();  // K(j) is dead from here on
-
-      phys = clamp_block(phys_next_raw, sc.num_blocks);
-      tt = tt_next;
-      {
-        const size_t pg = (size_t)phys * sc.Hkv + kvh;
-        const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + (pg * NC * B + (tt & (B - 1)));
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kr[c] = kp[(size_t)c * B];
-      }
-      wave_lds_sync();
-      chunk_pv<KVT, GM, X, R, NPASS>(vr, pw, r, ctx - j * 64, pacc);
-      wave_lds_sync();
-    }
-
-    // ---- finish the piece ------------------------------------------------------
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int e = 0; e < X; ++e)
-#pragma unroll
-        for (int o = NC; o < 64; o <<= 1) pacc[h][e] += __shfl_xor(pacc[h][e], o);
-    float lw[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) lw[h] = wave_sum(l_lane[h]);
-
-    const bool whole = (j0 == 0 && j1 == seg_units);
+  // close the piece that ends with chunk pc: whole pairs go straight to `out`,
+  // shared ones to this worker's slot, merged by the last of their workers
+  auto finish_piece = [&](const Pos& p) {
+    const float lw = sum_groups(st.l);
+    const bool whole = (piece_j0 == 0 && p.j == p.nch - 1);
     if (whole) {
-      if (lane < NC) {
+      if (n < sc.G) {
+        const float inv = 1.0f / lw;
+        const size_t orow = ((size_t)p.s * sc.Hq + (size_t)p.kvh * sc.G + n) * D + 4 * g;
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h < sc.G) {
-            const size_t o = ((size_t)s * sc.Hq + kvh * sc.G + h) * D + col * X;
-            const float inv = 1.0f / lw[h];
-            float v[X];
-#pragma unroll
-            for (int e = 0; e < X; ++e) v[e] = pacc[h][e] * inv;
-            store_row<QDT, X>(out, o, v);
-          }
-        }
+        for (int dt = 0; dt < C::NDT; ++dt) store4(out, CT, orow + 16 * dt, st.acc[dt] * inv);
       }
     } else {
       // Publish the partial state with device-scope stores (coherent across the
-      // XCDs' L2 caches without whole-cache write-back), wait until they have
-      // completed, and only then count the piece.  The merging worker reads with
-      // device-scope loads.  No cache-wide fence is needed on either side.
-      const int slot = 2 * w + (first_piece ? 0 : 1);
-      if (lane < NC) {
+      // XCDs' L2 caches without a cache-wide write-back); no cache-wide fence is
+      // needed on either side.
+      // slot 2w: the piece that starts the worker's share; 2w+1: the one that ends it
+      const int slot = 2 * w + (piece_u0 == u_begin ? 0 : 1);
+      if (n < sc.G) {
+        const float inv = 1.0f / lw;
+        float* so = slot_out + ((size_t)slot * sc.G + n) * D + 4 * g;
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h < sc.G) {
-            const float inv = 1.0f / lw[h];
-            float* so = slot_out + (size_t)slot * slot_stride + h * D + col * X;
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-            for (int e = 0; e < X; ++e)
-              __hip_atomic_store(so + e, pacc[h][e] * inv, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-          }
+          for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(so + 16 * dt + r, st.acc[dt][r] * inv, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (g == 0) {
+          float* ml = slot_ml + ((size_t)slot * sc.G + n) * 2;
+          __hip_atomic_store(ml, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // log2
+          __hip_atomic_store(ml + 1, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      if (lane == 0) {
-        for (int h = 0; h < sc.G && h < GM; ++h) {
-          float* ml = slot_ml + ((size_t)slot * sc.G + h) * 2;
-          __hip_atomic_store(ml, m_run[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // log2
-          __hip_atomic_store(ml + 1, lw[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+      // counted at the end of the share (claim_pending)
+      if (n_pend == 0) {
+        pend_s0 = p.s;
+        pend_k0 = p.kvh;
+        pend_n0 = p.nch;
+      } else {
+        pend_s1 = p.s;
+        pend_k1 = p.kvh;
+        pend_n1 = p.nch;
       }
-      __builtin_amdgcn_s_waitcnt(0);  // every store above has completed
-      // ---- the last worker to finish a piece of this pair merges all of them
-      const int wa = worker_of(seg_first, U, NWe);
-      const int wb = worker_of(seg_first + seg_units - 1, U, NWe);
-      int last = 0;
-      if (lane == 0)
-        last = claim_last(counters + (size_t)s * sc.Hkv + kvh, sc.epoch, (uint32_t)(wb - wa + 1));
-      last = uniform(last);  // lane 0's answer
-      if (last)
-        merge_pair<QDT, D, GM>(slot_out, slot_ml, out, sc, s, kvh, seg_first, wa, wb, U, NWe, lane);
+      ++n_pend;
     }
-    first_piece = false;
-    u = seg_first + j1;
+    state_init(st);
+  };
+
+  if constexpr (SMALLB) {
+    while (true) {
+      const Pos pn = advance(pc);
+      Chunk<C> ch;
+      float ks[16], vs[16];
+      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow_of(pc), 64 * pc.j, pc.ctx,
+                    pc.kvh, sc, n, g);
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, ch.k, qop);
+      chunk_softmax_pv<C, KVT, CT, 16>(st, S, ch.v, sc.scale_log2, ks, vs,
+                                       min(64, pc.ctx - 64 * pc.j), g);
+      const bool done = pc.k + 1 >= n_units;
+      if (done || piece_ends(pc)) {
+        finish_piece(pc);
+        if (done) break;
+        if (pn.s != pc.s || pn.kvh != pc.kvh) {
+          load_q<C>(qop, q, pn.s, pn.kvh, sc, n, g);
+          q_live<C>(qop, qop, n < sc.G);
+        }
+        piece_j0 = pn.j;
+        piece_u0 = pn.u;
+      }
+      pc = pn;
+    }
+  } else {
+    // Software pipeline over a ring of NBUF chunk buffers: on entry to a stage
+    // the loads of the next NBUF-2 chunks are in flight; the stage requests
+    // chunk +NBUF-1 into the buffer freed by the previous stage, then computes
+    // the current one.  The table entries run one chunk ahead of the requests.
+    // The next pair's q is loaded into qop right after the current pair's last
+    // scores have consumed it.
+    constexpr int NB = C::NBUF;
+    Chunk<C> R[NB];
+    Pos pp[NB];          // pp[k]: position of the chunk k stages ahead of pc
+    float ksr[NB][4], vsr[NB][4];
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int T = 0; T < 4; ++T) ksr[k][T] = vsr[k][T] = 1.0f;
+    pp[0] = pc;
+    auto issue = [&](Chunk<C>& dst, const Pos& p, const Pages& pg, float (&ks)[4], float (&vs)[4]) {
+      issue_k<C>(dst.k, k_pool, pg, p.kvh, sc, n, g);
+      issue_v<C>(dst.v, v_pool, pg, p.kvh, sc, n, g);
+      if constexpr (kFp8) page_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc);
+    };
+    auto pages_at = [&](const Pos& p) { return pages_of(trow_of(p), 64 * p.j, p.ctx, sc); };
+#pragma unroll
+    for (int k = 0; k + 1 < NB; ++k) {
+      if (k > 0) pp[k] = advance(pp[k - 1]);
+      issue(R[k], pp[k], pages_at(pp[k]), ksr[k], vsr[k]);
+    }
+    pp[NB - 1] = advance(pp[NB - 2]);
+    Pages en = pages_at(pp[NB - 1]);
+    bool q_raw = false;  // qop holds a fresh load whose dead columns are not yet zeroed
+    bool done = false;
+    // stage: chunk pp[0] sits in R[c]; chunk pp[NB-1] goes to R[f]
+    auto stage = [&](Chunk<C>& cur, Chunk<C>& fill, int c, int f) {
+      if (q_raw) {
+        q_live<C>(qop, qop, n < sc.G);
+        q_raw = false;
+      }
+      const Pos& p0 = pp[0];
+      const bool last = p0.k + 1 >= n_units;
+      const bool fetch = pp[NB - 1].k != pp[NB - 2].k;  // a chunk that is not a repeat
+      Pages en2 = en;
+      Pos pnext = pp[NB - 1];
+      if (fetch) {
+        issue(fill, pp[NB - 1], en, ksr[f], vsr[f]);
+        pnext = advance(pp[NB - 1]);
+        en2 = pages_at(pnext);
+      }
+      issue_point();
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, cur.k, qop);
+      issue_point();
+      const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
+      if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
+      issue_point();
+      chunk_softmax_pv<C, KVT, CT, 4>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
+                                      min(64, p0.ctx - 64 * p0.j), g);
+      issue_point();
+      if (last || piece_ends(p0)) {
+        finish_piece(p0);
+        piece_j0 = pp[1].j;
+        piece_u0 = pp[1].u;
+        q_raw = new_pair;
+      }
+      done = last;
+#pragma unroll
+      for (int k = 0; k + 1 < NB; ++k) pp[k] = pp[k + 1];
+      pp[NB - 1] = pnext;
+      en = en2;
+    };
+    while (true) {
+      if constexpr (NB == 3) {
+        stage(R[0], R[2], 0, 2);
+        if (done) break;
+        stage(R[1], R[0], 1, 0);
+        if (done) break;
+        stage(R[2], R[1], 2, 1);
+        if (done) break;
+      } else {
+        stage(R[0], R[1], 0, 1);
+        if (done) break;
+        stage(R[1], R[0], 1, 0);
+        if (done) break;
+      }
+    }
   }
+  if (n_pend) claim_pending();
 }
 
 // =================================================================================
@@ -809,40 +1157,35 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
 // ---------------------------------------------------------------------------------
 namespace {
 
-template <int KVT, int QDT, int D, int GM>
+template <int KVT, int CT, int D, bool SMALLB>
 int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
   if (p.balanced) {
     const size_t lds = ((size_t)p.num_seqs + 1) * sizeof(int);
     dim3 grid((sc.num_workers + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((paged_decode_balanced_kernel<KVT, QDT, D, GM>), grid, dim3(kThreads), lds,
-                       st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
+    hipLaunchKernelGGL((paged_decode_balanced_kernel<KVT, CT, D, SMALLB>), grid, dim3(kThreads),
+                       lds, st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
                        (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
                        p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.counters, sc);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
-  hipLaunchKernelGGL((paged_decode_kernel<KVT, QDT, D, GM>), grid, dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB>), grid, dim3(kThreads), 0, st,
                      (const uint8_t*)p.q, (const uint8_t*)p.k_pool, (const uint8_t*)p.v_pool,
                      p.k_scale, p.v_scale, p.block_table, p.context_lens, (uint8_t*)p.out,
                      p.part_out, p.part_max, p.part_sum, sc);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-template <int KVT, int QDT, int D>
-int pick_g(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
-  const int G = sc.G;
-  if (G <= 1) return launch_t<KVT, QDT, D, 1>(p, sc, st);
-  if (G <= 2) return launch_t<KVT, QDT, D, 2>(p, sc, st);
-  if (G <= 4) return launch_t<KVT, QDT, D, 4>(p, sc, st);
-  if (G <= 8) return launch_t<KVT, QDT, D, 8>(p, sc, st);
-  if (G <= 16) return launch_t<KVT, QDT, D, 16>(p, sc, st);
-  return -3;
+template <int KVT, int CT, int D>
+int pick_b(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
+  return p.block_size >= 16 ? launch_t<KVT, CT, D, false>(p, sc, st)
+                            : launch_t<KVT, CT, D, true>(p, sc, st);
 }
 
-template <int KVT, int QDT>
+template <int KVT, int CT>
 int pick_d(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
-  if (p.head_dim == 64) return pick_g<KVT, QDT, 64>(p, sc, st);
-  if (p.head_dim == 128) return pick_g<KVT, QDT, 128>(p, sc, st);
+  if (p.head_dim == 64) return pick_b<KVT, CT, 64>(p, sc, st);
+  if (p.head_dim == 128) return pick_b<KVT, CT, 128>(p, sc, st);
   return -3;
 }
 
@@ -871,7 +1214,7 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
   sc.num_workers = p.num_workers;
   sc.epoch = p.epoch;
   sc.scale_log2 = p.scale * kLog2e;
-  if (sc.blog2 < 0 || p.block_size > 64) return -3;
+  if (sc.blog2 < 0 || p.block_size > 64 || sc.G > 16) return -3;
   const int kv = p.kv_dtype, qd = p.q_dtype;
   if (kv == DT_F32 && qd == DT_F32) return pick_d<DT_F32, DT_F32>(p, sc, st);
   if (kv == DT_F16 && qd == DT_F16) return pick_d<DT_F16, DT_F16>(p, sc, st);
@@ -884,12 +1227,12 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
 // ---- resident-worker capacity (device property x kernel occupancy), cached -------
 namespace {
 
-template <int KVT, int QDT, int D, int GM>
+template <int KVT, int CT, int D, bool SMALLB>
 int blocks_per_cu() {
   static const int v = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<KVT, QDT, D, GM>),
+            &n, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<KVT, CT, D, SMALLB>),
             kThreads, 4096) != hipSuccess || n < 1)
       n = 1;
     return n;
@@ -897,18 +1240,10 @@ int blocks_per_cu() {
   return v;
 }
 
-template <int KVT, int QDT, int D>
-int bpc_g(int G) {
-  if (G <= 1) return blocks_per_cu<KVT, QDT, D, 1>();
-  if (G <= 2) return blocks_per_cu<KVT, QDT, D, 2>();
-  if (G <= 4) return blocks_per_cu<KVT, QDT, D, 4>();
-  if (G <= 8) return blocks_per_cu<KVT, QDT, D, 8>();
-  return blocks_per_cu<KVT, QDT, D, 16>();
-}
-
-template <int KVT, int QDT>
-int bpc_d(int D, int G) {
-  return D == 64 ? bpc_g<KVT, QDT, 64>(G) : bpc_g<KVT, QDT, 128>(G);
+template <int KVT, int CT>
+int bpc(int D, int B) {
+  if (D == 64) return B >= 16 ? blocks_per_cu<KVT, CT, 64, false>() : blocks_per_cu<KVT, CT, 64, true>();
+  return B >= 16 ? blocks_per_cu<KVT, CT, 128, false>() : blocks_per_cu<KVT, CT, 128, true>();
 }
 
 int device_cus() {
@@ -929,14 +1264,14 @@ int device_cus() {
 
 }  // namespace
 
-int balanced_worker_capacity(int kv, int qd, int D, int G) {
-  int bpc = 1;
-  if (kv == DT_F32) bpc = bpc_d<DT_F32, DT_F32>(D, G);
-  else if (kv == DT_F16) bpc = bpc_d<DT_F16, DT_F16>(D, G);
-  else if (kv == DT_BF16) bpc = bpc_d<DT_BF16, DT_BF16>(D, G);
-  else if (qd == DT_F16) bpc = bpc_d<DT_FP8, DT_F16>(D, G);
-  else bpc = bpc_d<DT_FP8, DT_BF16>(D, G);
-  return device_cus() * bpc * kWaves;
+int balanced_worker_capacity(int kv, int qd, int D, int block_size) {
+  int n = 1;
+  if (kv == DT_F32) n = bpc<DT_F32, DT_F32>(D, block_size);
+  else if (kv == DT_F16) n = bpc<DT_F16, DT_F16>(D, block_size);
+  else if (kv == DT_BF16) n = bpc<DT_BF16, DT_BF16>(D, block_size);
+  else if (qd == DT_F16) n = bpc<DT_FP8, DT_F16>(D, block_size);
+  else n = bpc<DT_FP8, DT_BF16>(D, block_size);
+  return device_cus() * n * kWaves;
 }
 
 int launch_split_reduce(const ReduceLaunch& p, hipStream_t st) {

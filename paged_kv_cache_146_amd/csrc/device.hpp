@@ -167,10 +167,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // dwordx4 request in flight.
 __device__ __forceinline__ void materialize(u32x4& v) { asm volatile("" : "+v"(v)); }
 
-// Compiler-only fence: memory operations are not moved across it.  Used to pin
-// where a software-pipelined loop issues its next loads, so that two buffers
-// of the same operand are never live at once.
-__device__ __forceinline__ void issue_point() { asm volatile("" ::: "memory"); }
+// Compiler-only fence: no instruction is moved across it (neither memory
+// operations nor arithmetic; a plain memory clobber would still let matrix-core
+// products float above the loads).  Pins where a software-pipelined loop issues
+// its next loads relative to the products that consume the current ones.
+__device__ __forceinline__ void issue_point() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // order this wave's LDS writes before its later LDS reads (wave-local exchange)
 __device__ __forceinline__ void wave_lds_sync() {

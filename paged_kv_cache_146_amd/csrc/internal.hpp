@@ -36,7 +36,7 @@ struct DecodeLaunch {
 
 // Wavefront workers the balanced decode can keep resident on the current device
 // for this instantiation (CUs x resident waves per CU), computed once per device.
-int balanced_worker_capacity(int kv_dtype, int q_dtype, int head_dim, int group);
+int balanced_worker_capacity(int kv_dtype, int q_dtype, int head_dim, int block_size);
 
 // returns a PKV_* status
 int launch_decode(const DecodeLaunch& p, hipStream_t stream);

@@ -53,7 +53,9 @@ def logical_k(k_bytes: np.ndarray, nb, B, H, D, dtype) -> np.ndarray:
 
 
 def logical_v(v_bytes: np.ndarray, nb, B, H, D, dtype) -> np.ndarray:
-    return np.ascontiguousarray(v_bytes).view(STORAGE[dtype]).reshape(nb, H, B, D)
+    """V pool bytes in the library layout [nb][H][D][B] -> logical [nb][H][B][D] bits."""
+    a = np.ascontiguousarray(v_bytes).view(STORAGE[dtype]).reshape(nb, H, D, B)
+    return np.ascontiguousarray(a.transpose(0, 1, 3, 2))
 
 
 class GpuCase:
