@@ -46,7 +46,26 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a 512 MiB device copy five times (a kernel of known HBM "
+                         "traffic) so that rocprofv3's FETCH_SIZE/WRITE_SIZE can be scaled")
     return ap.parse_args()
+
+
+def calibrate():
+    """Five copies of 512 MiB between two 1 GiB-apart buffers: each copy reads and writes
+    exactly 536870912 bytes of HBM, the reference for the byte counters."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    pad = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")  # evicts src/dst between copies
+    for _ in range(5):
+        pad.sum()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": 5}), flush=True)
 
 
 DEFAULT_PARTITION = -1  # balanced split-KV
@@ -70,6 +89,9 @@ def write_bytes(wl) -> int:
 
 def main():
     a = parse()
+    if a.calibrate:
+        calibrate()
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
