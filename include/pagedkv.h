@@ -238,9 +238,12 @@ int pkv_split_kv_reduce(const float* part_out, const float* part_max, const floa
  *   q: device [total_q][num_q_heads][head_dim] of q_dtype; out likewise.
  *   cu_seqlens_q: device int32 [num_seqs + 1], non-decreasing, last = total_q.
  *   max_q_len: host-known upper bound on n_s (sizes the grid).
- *   Supported: pool bf16 with q bf16; pool fp8 with q bf16 (fp8 -> bf16 is
- *   exact; K's scale multiplies the scores, V's scale the probabilities,
- *   which are rounded to bf16 for the P.V product); head_dim 128.
+ *   Supported: q bf16 with a bf16 or fp8 pool; head_dim 64 or 128; block_size
+ *   16..64 (a 16-token tile must lie in one block); group size G = H_q/H_kv
+ *   in {1, 2, 4, 8, 16}.  fp8 keys widen exactly to bf16 for QK^T and K's
+ *   scale multiplies the scores; fp8 values widen exactly to f16 and V's scale
+ *   multiplies the probabilities, which enter P.V as f16.  With a bf16 pool
+ *   the probabilities enter P.V as a hi + lo pair of bf16 values.
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
 int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
                       int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,

@@ -369,7 +369,12 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
   if (q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
   if (pool->kv_dtype != PKV_BF16 && pool->kv_dtype != PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
-  if (pool->head_dim != 128) return PKV_EUNSUPPORTED;
+  if (pool->head_dim != 128 && pool->head_dim != 64) return PKV_EUNSUPPORTED;
+  if (pool->block_size < 16) return PKV_EUNSUPPORTED;  // a 16-token tile sits in one block
+  {
+    const int group = num_q_heads / pool->num_kv_heads;
+    if (group > 16 || 16 % group != 0) return PKV_EUNSUPPORTED;
+  }
   if (num_seqs == 0 || total_q == 0) return PKV_OK;
   if (!q || !cu_seqlens_q || !k_pool || !v_pool || !block_table || !context_lens || !out)
     return PKV_EINVAL;

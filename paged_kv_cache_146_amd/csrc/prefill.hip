@@ -1,12 +1,442 @@
-// prefill.hip — chunked prefill over the paged cache (placeholder launcher).
+// prefill.hip — chunked prefill over the paged cache on the matrix cores.
+//
+// Method: "03 | PagedAttention and the KV-cache memory system", §4 — prefill
+// reuses flash-style tiling over the paged cache, handed the block table; a
+// query row i of an n-token chunk sits at position a = ctx - n + i and sees the
+// keys 0..a (the whole cache, causal inside the chunk).
+//
+// Work cut: one workgroup (4 waves) per (query block, kv head, sequence).  A
+// "row" is a (query token, query head) pair; a 16-row tile holds 16/G tokens x
+// the G heads of the kv head, so every K/V tile is reused by all G heads.  Each
+// wave owns four row tiles, the workgroup 256/G tokens.
+//
+// Per 64-key chunk the workgroup stages K and V once into LDS, widened to 16
+// bits (fp8 E4M3 -> bf16 for K, -> f16 for V; both exact), double-buffered,
+// with the pool loads issued two chunks ahead.  Then every wave computes, per
+// row tile, the same products as decode:
+//   S^T = K . Q^T   16x16x32 bf16 MFMA, K rows from LDS, q columns in registers;
+//   O^T = V^T . P^T 16x16x32 MFMA in the V staging type, P from the lane's own
+//                   scores (tile T row n is key 16 T + n, so S^T leaves lane
+//                   (n, g) the keys 16 T + 4 g + r, the k-slots P.V needs).
+// fp8 pools: K's page scale multiplies the scores, V's is folded into P, and
+// P.V runs in f16 (P keeps 11 significant bits).  bf16 pools: P.V in bf16 with
+// P split into hi + lo bf16 terms.
+//
+// LDS rows are XOR-swizzled in 16-byte units so that the 16 lanes reading one
+// K column block (or V row block) hit distinct banks.
 #include "device.hpp"
 #include "internal.hpp"
+#include "tile.hpp"
+
+#include <math.h>
 
 namespace pkv {
 
+struct PrefillScalars {
+  int W;           // max_blocks_per_seq
+  int S, Hq, Hkv, G;
+  int blog2, num_blocks, ctx_cap;
+  int causal;
+  float scale_log2;
+};
+
+constexpr int kPfThreads = 256;
+
+template <int KVT, int D>
+struct PCfg {
+  static constexpr int EB = Elem<KVT>::bytes;       // pool bytes per element
+  static constexpr int X = 16 / EB;                 // K dims per pool piece
+  static constexpr int NC = D / X;                  // K pieces per token
+  static constexpr int TP = 16 / EB;                // V tokens per pool piece
+  static constexpr int NKS = D / 32;                // k-steps of S^T
+  static constexpr int NDT = D / 16;                // dim tiles of O^T
+  static constexpr int NR = 2;                      // row tiles per wave
+  static constexpr int KUNITS = D * 2 / 16;         // 16-byte units per staged K row
+  static constexpr int KROW = D * 2;                // staged K row (one token, bf16)
+  static constexpr int VROW = 64 * 2;               // staged V row (one dim, 64 tokens)
+  static constexpr int KBUF = 64 * KROW;
+  static constexpr int VBUF = D * VROW;
+  static constexpr int PT = KVT == DT_FP8 ? DT_F16 : DT_BF16;  // type of the P.V product
+  static constexpr bool SPLIT = (PT == DT_BF16);               // P as hi + lo
+  static constexpr int KP = 64 * NC / kPfThreads;   // K pool pieces per thread per chunk
+  static constexpr int VP = D * (64 / TP) / kPfThreads;  // V pool pieces per thread
+  static_assert(KP >= 1 && VP >= 1, "chunk too small for the workgroup");
+};
+
+// pool bytes of one chunk held by a thread between its load and its staging
+template <class C>
+struct Raw {
+  u32x4 k[C::KP];
+  u32x4 v[C::VP];
+};
+
+// the chunk's four 16-token tiles each lie in one block (block_size >= 16);
+// tiles at or past `end` clamp onto the last visible block
+__device__ __forceinline__ void chunk_pages(int (&pg)[4], const int32_t* __restrict__ trow,
+                                            int base, int end, const PrefillScalars& ps) {
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int t = uniform(min(base + 16 * T, end - 1));
+    pg[T] = uniform(clamp_block(trow[t >> ps.blog2], ps.num_blocks));
+  }
+}
+
+__device__ __forceinline__ int pick4(const int (&v)[4], int i) {
+  return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+}
+
+// Issue the pool loads of the chunk at `base` (tokens clamped below `end`).
+// K piece kp: dims [c X, c X + X) of token kp % 64, c = kp / 64.
+// V piece vp: tokens [TP p, TP p + TP) of dim vp % D, p = vp / D.
+template <int KVT, int D>
+__device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* __restrict__ k_pool,
+                                           const uint8_t* __restrict__ v_pool, const int (&pg)[4],
+                                           int base, int end, int kvh, const PrefillScalars& ps) {
+  using C = PCfg<KVT, D>;
+  const int B = 1 << ps.blog2;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KP; ++i) {
+    const int kp = tid + kPfThreads * i;
+    const int c = kp >> 6, tok = kp & 63;
+    const int t = min(base + tok, end - 1);
+    const size_t page = (size_t)pick4(pg, tok >> 4) * ps.Hkv + kvh;
+    r.k[i] = reinterpret_cast<const u32x4*>(k_pool)[(page * C::NC + c) * B + (t & (B - 1))];
+  }
+#pragma unroll
+  for (int i = 0; i < C::VP; ++i) {
+    const int vp = tid + kPfThreads * i;
+    const int p = vp / D, d = vp % D;
+    const int t0 = p * C::TP;  // first token of the piece within the chunk
+    const size_t page = (size_t)pick4(pg, t0 >> 4) * ps.Hkv + kvh;
+    const int off = (min(base + t0, end - 1) & (B - 1)) & ~(C::TP - 1);
+    r.v[i] = *reinterpret_cast<const u32x4*>(v_pool + ((page * D + d) * B + off) * C::EB);
+  }
+}
+
+// Widen the thread's pieces to 16 bits and write them into the LDS buffers;
+// V tokens at or past `end` become zero (their slots may hold anything).
+template <int KVT, int D>
+__device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
+                                            uint8_t* vbuf, int base, int end) {
+  using C = PCfg<KVT, D>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C::KP; ++i) {
+    const int kp = tid + kPfThreads * i;
+    const int c = kp >> 6, tok = kp & 63;
+    uint8_t* row = kbuf + tok * C::KROW;
+    if constexpr (KVT == DT_FP8) {
+      const u32x4 w = r.k[i];
+      const u32x4 lo = fp8x8<DT_BF16>(w[0], w[1]), hi = fp8x8<DT_BF16>(w[2], w[3]);
+      const int u0 = 2 * c, u1 = 2 * c + 1;
+      *reinterpret_cast<u32x4*>(row + ((u0 ^ (tok & (C::KUNITS - 1))) << 4)) = lo;
+      *reinterpret_cast<u32x4*>(row + ((u1 ^ (tok & (C::KUNITS - 1))) << 4)) = hi;
+    } else {
+      *reinterpret_cast<u32x4*>(row + ((c ^ (tok & (C::KUNITS - 1))) << 4)) = r.k[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::VP; ++i) {
+    const int vp = tid + kPfThreads * i;
+    const int p = vp / D, d = vp % D;
+    const int t0 = p * C::TP;
+    const int lim = end - (base + t0);  // tokens of the piece below end
+    uint8_t* row = vbuf + d * C::VROW;
+    u32x4 w = r.v[i];
+    if (lim < C::TP) {  // the chunk's last piece: zero what lies past the context
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok_e = e / C::EB;
+        if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+      }
+    }
+    if constexpr (KVT == DT_FP8) {
+      const u32x4 lo = fp8x8<DT_F16>(w[0], w[1]), hi = fp8x8<DT_F16>(w[2], w[3]);
+      const int u0 = 2 * p, u1 = 2 * p + 1;
+      *reinterpret_cast<u32x4*>(row + ((u0 ^ (d & 7)) << 4)) = lo;
+      *reinterpret_cast<u32x4*>(row + ((u1 ^ (d & 7)) << 4)) = hi;
+    } else {
+      *reinterpret_cast<u32x4*>(row + ((p ^ (d & 7)) << 4)) = w;
+    }
+  }
+}
+
+// per-row online-softmax state of one row tile: lane (n, g) holds column n
+template <int D>
+struct RowState {
+  f32x4 acc[D / 16];
+  float m, l;
+};
+
+template <int KVT, int D>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
+                     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+                     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+                     const int32_t* __restrict__ block_table,
+                     const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out,
+                     const PrefillScalars ps) {
+  using C = PCfg<KVT, D>;
+  constexpr bool kFp8 = (KVT == DT_FP8);
+  constexpr int NR = C::NR;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][C::KBUF + C::VBUF];
+
+  const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int G = ps.G, tpr = 16 / G;           // tokens per row tile
+  const int tpw = NR * tpr, tpg = 4 * tpw;    // tokens per wave / per workgroup
+
+  const int q0 = cu_seqlens_q[s];
+  const int nq = cu_seqlens_q[s + 1] - q0;
+  const int tok0 = qb * tpg;
+  if (tok0 >= nq) return;
+  int ctx = context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > ps.ctx_cap ? ps.ctx_cap : ctx);
+  const int pos0 = ctx - nq;  // absolute position of query token 0
+  const int tok_end = min(nq, tok0 + tpg);
+  // keys the workgroup needs: [0, kend)
+  const int kend = ps.causal ? max(0, min(ctx, pos0 + tok_end)) : ctx;
+
+  // ---- this lane's rows: token and head of column n in each row tile
+  const int hq = kvh * G + n % G;
+  int rtok[NR];  // query token (chunk-relative) of column n, or -1 when past the chunk
+  int rlim[NR];  // keys [0, rlim) visible to that row
+  int tile_lim[NR];  // keys [0, tile_lim) visible to any row of the tile (wave-uniform)
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    const int t = tok0 + wave * tpw + rt * tpr + n / G;
+    rtok[rt] = t < nq ? t : -1;
+    rlim[rt] = rtok[rt] < 0 ? 0 : (ps.causal ? max(0, min(ctx, pos0 + t + 1)) : ctx);
+    const int tlast = min(nq, tok0 + wave * tpw + (rt + 1) * tpr) - 1;
+    tile_lim[rt] = uniform(tlast < tok0 + wave * tpw + rt * tpr
+                               ? 0
+                               : (ps.causal ? max(0, min(ctx, pos0 + tlast + 1)) : ctx));
+  }
+
+  // ---- q operands (B of S^T), one per row tile and k-step; dead rows are zero
+  u32x4 qop[NR][C::NKS];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    const int t = rtok[rt] < 0 ? 0 : rtok[rt];
+    const uint8_t* row = q + ((size_t)(q0 + t) * ps.Hq + hq) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(row + (32 * ks + 8 * g) * 2);
+      qop[rt][ks] = rtok[rt] < 0 ? u32x4{0u, 0u, 0u, 0u} : w;
+    }
+  }
+
+  RowState<D> st[NR];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    st[rt].m = -INFINITY;
+    st[rt].l = 0.0f;
+  }
+
+  const int nch = (kend + 63) >> 6;
+  if (nch > 0) {
+    const int32_t* trow = block_table + (size_t)s * ps.W;
+    // pages (and fp8 scales) of chunks j, j+1, j+2 — scalar, ahead of their use
+    int pg0[4], pg1[4], pg2[4];
+    chunk_pages(pg0, trow, 0, kend, ps);
+    chunk_pages(pg1, trow, min(64, 64 * (nch - 1)), kend, ps);
+    Raw<C> ra, rb;
+    chunk_load<KVT, D>(ra, k_pool, v_pool, pg0, 0, kend, kvh, ps);
+    if (nch > 1) chunk_load<KVT, D>(rb, k_pool, v_pool, pg1, 64, kend, kvh, ps);
+    chunk_pages(pg2, trow, min(128, 64 * (nch - 1)), kend, ps);
+    chunk_stage<KVT, D>(ra, lds[0], lds[0] + C::KBUF, 0, kend);
+    __syncthreads();
+
+    // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
+    // are staged after chunk j is computed
+    auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1) {
+      const int base = 64 * j;
+      if (j + 2 < nch) chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg2, base + 128, kend, kvh, ps);
+      float zs[4], vs[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        if constexpr (kFp8) {
+          const size_t page = (size_t)pg0[T] * ps.Hkv + kvh;
+          zs[T] = ps.scale_log2 * k_scale[page];
+          vs[T] = v_scale[page];
+        } else {
+          zs[T] = ps.scale_log2;
+          vs[T] = 1.0f;
+        }
+      }
+      const uint8_t* kbuf = lds[j & 1];
+      const uint8_t* vbuf = lds[j & 1] + C::KBUF;
+      issue_point();
+      // ---- S^T for all live row tiles
+      f32x4 S[NR][4];
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt)
+#pragma unroll
+        for (int T = 0; T < 4; ++T) S[rt][T] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      bool live[NR];
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) live[rt] = base < tile_lim[rt];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const int tok = 16 * T + n;
+        const uint8_t* krow = kbuf + tok * C::KROW;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          const int u = 4 * ks + g;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ((u ^ (tok & (C::KUNITS - 1))) << 4));
+#pragma unroll
+          for (int rt = 0; rt < NR; ++rt)
+            if (live[rt]) S[rt][T] = mma16<DT_BF16>(a, qop[rt][ks], S[rt][T]);
+        }
+      }
+      // ---- online softmax per row tile; P operands
+      u32x4 phi[NR][2], plo[NR][2];
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) {
+        if (!live[rt]) continue;
+        float x[16];
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = base + 16 * T + 4 * g + r;
+            x[4 * T + r] = key < rlim[rt] ? S[rt][T][r] * zs[T] : -INFINITY;
+          }
+        float cm = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) cm = fmaxf(cm, x[i]);
+        cm = max_groups(cm);
+        const float mn = fmaxf(st[rt].m, cm);
+        const float mref = mn == -INFINITY ? 0.0f : mn;  // rows that have seen no key yet
+        const float alpha = __builtin_amdgcn_exp2f(st[rt].m - mref);
+        st[rt].m = mn;
+        float p[16], psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+          psum += p[i];
+        }
+        st[rt].l = st[rt].l * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          uint32_t wh[4], wl[4];
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
+            const float a = p[i0] * vs[i0 >> 2], b = p[i0 + 1] * vs[i0 >> 2];
+            wh[wd] = pack2<C::PT>(a, b);
+            if constexpr (C::SPLIT) {
+              const f32x2 h = unpack2<C::PT>(wh[wd]);
+              wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
+            } else {
+              wl[wd] = 0u;
+            }
+          }
+          phi[rt][s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+          plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+        }
+      }
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d = 16 * dt + n;
+        const uint8_t* vrow = vbuf + d * C::VROW;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int u_a = 4 * s2 + (g >> 1), u_b = 4 * s2 + 2 + (g >> 1);
+          const u32x2 va = *reinterpret_cast<const u32x2*>(vrow + ((u_a ^ (d & 7)) << 4) + 8 * (g & 1));
+          const u32x2 vb = *reinterpret_cast<const u32x2*>(vrow + ((u_b ^ (d & 7)) << 4) + 8 * (g & 1));
+          const u32x4 a = {va[0], va[1], vb[0], vb[1]};
+#pragma unroll
+          for (int rt = 0; rt < NR; ++rt) {
+            if (!live[rt]) continue;
+            st[rt].acc[dt] = mma16<C::PT>(a, phi[rt][s2], st[rt].acc[dt]);
+            if constexpr (C::SPLIT) st[rt].acc[dt] = mma16<C::PT>(a, plo[rt][s2], st[rt].acc[dt]);
+          }
+        }
+      }
+      issue_point();
+      // ---- stage chunk j+1 into the other buffer; advance the page window
+      if (j + 1 < nch) chunk_stage<KVT, D>(nxt1, lds[(j + 1) & 1], lds[(j + 1) & 1] + C::KBUF, base + 64, kend);
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        pg0[T] = pg1[T];
+        pg1[T] = pg2[T];
+      }
+      chunk_pages(pg2, trow, min(base + 192, 64 * (nch - 1)), kend, ps);
+      __syncthreads();
+    };
+    // chunk j's raw pieces live in ra (j even) / rb (j odd) until staged
+    for (int j = 0; j < nch; j += 2) {
+      step(j, ra, rb);
+      if (j + 1 < nch) step(j + 1, rb, ra);
+    }
+  }
+
+  // ---- normalise and store the live rows
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    const float lw = sum_groups(st[rt].l);
+    if (rtok[rt] < 0) continue;
+    const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
+    const size_t orow = ((size_t)(q0 + rtok[rt]) * ps.Hq + hq) * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) store4(out, DT_BF16, orow + 16 * dt, st[rt].acc[dt] * inv);
+  }
+}
+
+namespace {
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
+template <int KVT, int D>
+int launch_pf(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) {
+  const int tpg = 4 * PCfg<KVT, D>::NR * (16 / ps.G);
+  dim3 grid((p.max_q_len + tpg - 1) / tpg, p.num_kv_heads, p.num_seqs);
+  hipLaunchKernelGGL((paged_prefill_kernel<KVT, D>), grid, dim3(kPfThreads), 0, st,
+                     (const uint8_t*)p.q, p.cu_seqlens_q, (const uint8_t*)p.k_pool,
+                     (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
+                     p.context_lens, (uint8_t*)p.out, ps);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace
+
 int launch_prefill(const PrefillLaunch& p, hipStream_t st) {
-  (void)p;
-  (void)st;
+  PrefillScalars ps;
+  ps.W = p.max_blocks_per_seq;
+  ps.S = p.num_seqs;
+  ps.Hq = p.num_q_heads;
+  ps.Hkv = p.num_kv_heads;
+  ps.G = p.num_q_heads / p.num_kv_heads;
+  ps.blog2 = log2_exact(p.block_size);
+  ps.num_blocks = p.num_blocks;
+  ps.ctx_cap = p.ctx_cap;
+  ps.causal = p.causal;
+  ps.scale_log2 = p.scale * kLog2e;
+  if (ps.blog2 < 4 || p.block_size > 64) return -3;  // a 16-token tile must sit in one block
+  if (ps.G < 1 || ps.G > 16 || (16 % ps.G) != 0) return -3;
+  if (p.q_dtype != DT_BF16) return -3;
+  if (p.max_q_len <= 0) return 0;
+  if (p.kv_dtype == DT_FP8) {
+    if (p.head_dim == 128) return launch_pf<DT_FP8, 128>(p, ps, st);
+    if (p.head_dim == 64) return launch_pf<DT_FP8, 64>(p, ps, st);
+  } else if (p.kv_dtype == DT_BF16) {
+    if (p.head_dim == 128) return launch_pf<DT_BF16, 128>(p, ps, st);
+    if (p.head_dim == 64) return launch_pf<DT_BF16, 64>(p, ps, st);
+  }
   return -3;
 }
 

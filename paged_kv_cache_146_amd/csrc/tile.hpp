@@ -1,0 +1,119 @@
+// tile.hpp — matrix-core and cross-lane helpers shared by the decode and prefill
+// kernels of this library (gfx950, wave64).
+#pragma once
+
+#include "device.hpp"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float as_f32(uint32_t w) {
+  float f;
+  __builtin_memcpy(&f, &w, 4);
+  return f;
+}
+
+// ---- matrix-core products ---------------------------------------------------------
+template <int CT>
+__device__ __forceinline__ f32x4 mma16(const u32x4 a, const u32x4 b, const f32x4 c) {
+  if constexpr (CT == DT_BF16) {
+    bf16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  } else {
+    f16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// two floats -> one packed pair of CT, round to nearest even
+template <int CT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  uint32_t w;
+  if constexpr (CT == DT_BF16) {
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    __builtin_memcpy(&w, &b, 4);
+  } else {
+    const f16x2 h = __builtin_convertvector(v, f16x2);
+    __builtin_memcpy(&w, &h, 4);
+  }
+  return w;
+}
+
+// one packed pair of CT -> two floats (exact)
+template <int CT>
+__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+  if constexpr (CT == DT_BF16) {
+    return f32x2{bf16_lo(w), bf16_hi(w)};
+  } else {
+    return f32x2{f16_lo(w), f16_hi(w)};
+  }
+}
+
+// eight E4M3 codes (two words) -> eight CT values; exact, as every E4M3 value is
+// representable in bf16 and in f16
+template <int CT>
+__device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  const u32x4 r = {pack2<CT>(a[0], a[1]), pack2<CT>(b[0], b[1]), pack2<CT>(c[0], c[1]),
+                   pack2<CT>(d[0], d[1])};
+  return r;
+}
+
+// max / sum over the four lane groups {L, L^16, L^32, L^48}; every lane of the
+// set gets the same bits (each swap hands both partners the same operand order)
+__device__ __forceinline__ float max_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+}
+__device__ __forceinline__ float sum_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = as_f32(a[0]) + as_f32(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return as_f32(b[0]) + as_f32(b[1]);
+}
+
+__device__ __forceinline__ void store_any(uint8_t* out, int dt, size_t idx, float x) {
+  if (dt == DT_F32)
+    reinterpret_cast<float*>(out)[idx] = x;
+  else if (dt == DT_BF16)
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(x);
+  else
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(x);
+}
+
+// four consecutive output elements starting at idx (a multiple of 4)
+__device__ __forceinline__ void store4(uint8_t* out, int dt, size_t idx, const f32x4 v) {
+  if (dt == DT_F32) {
+    *reinterpret_cast<f32x4*>(out + idx * 4) = v;
+  } else {
+    const u32x2 w = dt == DT_BF16 ? u32x2{pack2<DT_BF16>(v[0], v[1]), pack2<DT_BF16>(v[2], v[3])}
+                                  : u32x2{pack2<DT_F16>(v[0], v[1]), pack2<DT_F16>(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(out + idx * 2) = w;
+  }
+}
+
+__device__ __forceinline__ int clamp_block(int phys, int num_blocks) {
+  return phys < 0 ? 0 : (phys >= num_blocks ? num_blocks - 1 : phys);
+}
+
+}  // namespace pkv

@@ -169,3 +169,14 @@ def test_write_and_prefill_argument_errors_caught_on_host():
                                None, None, 8, None, 64, 0.1, 1, None, None) == -3  # f32 q
     assert L.pkv_paged_prefill(None, 2, None, 1, 1, 1, 30, ctypes.byref(desc), None, None, None,
                                None, None, 8, None, 64, 0.1, 1, None, None) == -1
+    # tiles of 16 tokens must sit in one block, and 16 query rows must hold whole groups
+    small_b = pkv.pool_desc(10, 8, 8, 128, "bf16")
+    assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 32, ctypes.byref(small_b), None, None, None,
+                               None, None, 8, None, 64, 0.1, 1, None, None) == -3
+    assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 24, ctypes.byref(desc), None, None, None,
+                               None, None, 8, None, 64, 0.1, 1, None, None) == -3  # G = 3
+    assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 256, ctypes.byref(desc), None, None, None,
+                               None, None, 8, None, 64, 0.1, 1, None, None) == -3  # G = 32
+    d64 = pkv.pool_desc(10, 16, 8, 64, "fp8")
+    assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 32, ctypes.byref(d64), None, None, None,
+                               None, None, 8, None, 64, 0.1, 1, None, None) == 0  # nothing to do
