@@ -27,6 +27,9 @@ COMMON = [
     # IEEE fp32 division (the fp8 write path divides by the scale)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math", "-ffp-contract=fast",
+    # keep matrix-core accumulators in ordinary VGPRs: the kernels rescale them with
+    # VALU code, and accumulators in AGPRs would be copied back and forth
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -22,8 +22,11 @@
 // P.V runs in f16 (P keeps 11 significant bits).  bf16 pools: P.V in bf16 with
 // P split into hi + lo bf16 terms.
 //
-// LDS rows are XOR-swizzled in 16-byte units so that the 16 lanes reading one
-// K column block (or V row block) hit distinct banks.
+// LDS rows are XOR-swizzled in 16-byte units (K rows by token mod 16, V rows by
+// dim / 2 mod 8) so that the lanes of one LDS cycle hit distinct banks, for the
+// staging writes and for the operand reads.  The chunk's block ids and fp8
+// scales come from a small LDS window, refilled every 32 chunks, so that no
+// scalar load is outstanding when the loop waits on LDS (both share a counter).
 #include "device.hpp"
 #include "internal.hpp"
 #include "tile.hpp"
@@ -58,6 +61,8 @@ struct PCfg {
   static constexpr int VBUF = D * VROW;
   static constexpr int PT = KVT == DT_FP8 ? DT_F16 : DT_BF16;  // type of the P.V product
   static constexpr bool SPLIT = (PT == DT_BF16);               // P as hi + lo
+  // two resident workgroups per CU where the registers allow it (LDS holds two)
+  static constexpr int WPE = (KVT == DT_BF16 && D == 128) ? 1 : 2;
   static constexpr int KP = 64 * NC / kPfThreads;   // K pool pieces per thread per chunk
   static constexpr int VP = D * (64 / TP) / kPfThreads;  // V pool pieces per thread
   static_assert(KP >= 1 && VP >= 1, "chunk too small for the workgroup");
@@ -69,17 +74,6 @@ struct Raw {
   u32x4 k[C::KP];
   u32x4 v[C::VP];
 };
-
-// the chunk's four 16-token tiles each lie in one block (block_size >= 16);
-// tiles at or past `end` clamp onto the last visible block
-__device__ __forceinline__ void chunk_pages(int (&pg)[4], const int32_t* __restrict__ trow,
-                                            int base, int end, const PrefillScalars& ps) {
-#pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    const int t = uniform(min(base + 16 * T, end - 1));
-    pg[T] = uniform(clamp_block(trow[t >> ps.blog2], ps.num_blocks));
-  }
-}
 
 __device__ __forceinline__ int pick4(const int (&v)[4], int i) {
   return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
@@ -151,13 +145,28 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
         if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
       }
     }
+    // 16-bit values of the piece's tokens t0 + i; a row keeps, per 16-byte unit
+    // u = 4 s2 + g, the keys 32 s2 + 4 g + (0..3) and 32 s2 + 16 + 4 g + (0..3)
+    // (the k-slots of one P.V operand), so key t sits at unit 4 (t / 32) + (t / 4) % 4,
+    // half (t / 16) % 2
+    uint32_t h16[C::TP / 2];
     if constexpr (KVT == DT_FP8) {
       const u32x4 lo = fp8x8<DT_F16>(w[0], w[1]), hi = fp8x8<DT_F16>(w[2], w[3]);
-      const int u0 = 2 * p, u1 = 2 * p + 1;
-      *reinterpret_cast<u32x4*>(row + ((u0 ^ (d & 7)) << 4)) = lo;
-      *reinterpret_cast<u32x4*>(row + ((u1 ^ (d & 7)) << 4)) = hi;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h16[k] = lo[k];
+        h16[4 + k] = hi[k];
+      }
     } else {
-      *reinterpret_cast<u32x4*>(row + ((p ^ (d & 7)) << 4)) = w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) h16[k] = w[k];
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < C::TP / 4; ++q4) {  // runs of four keys
+      const int t = t0 + 4 * q4;
+      const int u = 4 * (t >> 5) + ((t >> 2) & 3);
+      *reinterpret_cast<u32x2*>(row + ((u ^ ((d >> 1) & 7)) << 4) + 8 * ((t >> 4) & 1)) =
+          u32x2{h16[2 * q4], h16[2 * q4 + 1]};
     }
   }
 }
@@ -170,8 +179,8 @@ struct RowState {
 };
 
 template <int KVT, int D>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
+    PCfg<KVT, D>::WPE, PCfg<KVT, D>::WPE))) void paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
                      const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
                      const int32_t* __restrict__ block_table,
@@ -181,6 +190,10 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
   constexpr bool kFp8 = (KVT == DT_FP8);
   constexpr int NR = C::NR;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][C::KBUF + C::VBUF];
+  constexpr int kWinChunks = 32;
+  constexpr int kWinBlocks = (kWinChunks + 2) * 4;  // chunks of 64 tokens, blocks of >= 16
+  __shared__ int w_blk[kWinBlocks];
+  __shared__ float w_ks[kWinBlocks], w_vs[kWinBlocks];
 
   const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -237,17 +250,65 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
     st[rt].l = 0.0f;
   }
 
+  // keys [0, wave_min_lim) are visible to every live row of the wave; [0, wave_max_lim)
+  // to at least one (wave-uniform)
+  int wave_min_lim = kend, wave_max_lim = 0;
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) wave_max_lim = max(wave_max_lim, tile_lim[rt]);
+  {
+    const int t_first = tok0 + wave * tpw;
+    wave_min_lim = t_first >= nq ? 0
+                                 : uniform(ps.causal ? max(0, min(ctx, pos0 + t_first + 1)) : ctx);
+    if (tok0 + wave * tpw + tpw > nq) wave_min_lim = 0;  // the wave holds rows past the chunk
+  }
+  // this lane's LDS offsets (swizzled 16-byte units), the same for every chunk
+  int k_off[4], k_unit[C::NKS], v_off, v_unit[2];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) k_off[T] = (16 * T + n) * C::KROW;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) k_unit[ks] = ((4 * ks + g) ^ (n & (C::KUNITS - 1))) << 4;
+  v_off = n * C::VROW;
+  // rows d = 16 dt + n share (d >> 1) & 7 = (n >> 1) & 7 for every dt
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) v_unit[s2] = ((4 * s2 + g) ^ ((n >> 1) & 7)) << 4;
   const int nch = (kend + 63) >> 6;
   if (nch > 0) {
     const int32_t* trow = block_table + (size_t)s * ps.W;
-    // pages (and fp8 scales) of chunks j, j+1, j+2 — scalar, ahead of their use
-    int pg0[4], pg1[4], pg2[4];
-    chunk_pages(pg0, trow, 0, kend, ps);
-    chunk_pages(pg1, trow, min(64, 64 * (nch - 1)), kend, ps);
+    // window k holds the blocks of chunks [32 k, 32 k + 34) (two chunks of lookahead)
+    auto fill_window = [&](int wk) {
+      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+      const int last = (kend - 1) >> ps.blog2;
+      for (int t = threadIdx.x; t < kWinBlocks; t += kPfThreads) {
+        const int e = clamp_block(trow[min(blk0 + t, last)], ps.num_blocks);
+        w_blk[t] = e;
+        if constexpr (kFp8) {
+          const size_t page = (size_t)e * ps.Hkv + kvh;
+          w_ks[t] = ps.scale_log2 * k_scale[page];
+          w_vs[t] = v_scale[page];
+        }
+      }
+    };
+    // block ids of chunk c's four tiles from window wk (which must cover c)
+    auto win_pages = [&](int c, int wk, int (&pg)[4]) {
+      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const int t = min(64 * c + 16 * T, kend - 1);
+        pg[T] = uniform(w_blk[(t >> ps.blog2) - blk0]);
+      }
+    };
+    fill_window(0);
+    __syncthreads();
     Raw<C> ra, rb;
-    chunk_load<KVT, D>(ra, k_pool, v_pool, pg0, 0, kend, kvh, ps);
-    if (nch > 1) chunk_load<KVT, D>(rb, k_pool, v_pool, pg1, 64, kend, kvh, ps);
-    chunk_pages(pg2, trow, min(128, 64 * (nch - 1)), kend, ps);
+    {
+      int pg[4];
+      win_pages(0, 0, pg);
+      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, 0, kend, kvh, ps);
+      if (nch > 1) {
+        win_pages(1, 0, pg);
+        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, ps);
+      }
+    }
     chunk_stage<KVT, D>(ra, lds[0], lds[0] + C::KBUF, 0, kend);
     __syncthreads();
 
@@ -255,60 +316,64 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
     // are staged after chunk j is computed
     auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1) {
       const int base = 64 * j;
-      if (j + 2 < nch) chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg2, base + 128, kend, kvh, ps);
+      const int wk = j / kWinChunks;
+      if (j + 2 < nch) {
+        int pg[4];
+        win_pages(j + 2, wk, pg);
+        chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg, base + 128, kend, kvh, ps);
+      }
       float zs[4], vs[4];
+      {
+        const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        if constexpr (kFp8) {
-          const size_t page = (size_t)pg0[T] * ps.Hkv + kvh;
-          zs[T] = ps.scale_log2 * k_scale[page];
-          vs[T] = v_scale[page];
-        } else {
-          zs[T] = ps.scale_log2;
-          vs[T] = 1.0f;
+        for (int T = 0; T < 4; ++T) {
+          if constexpr (kFp8) {
+            const int i = (min(base + 16 * T, kend - 1) >> ps.blog2) - blk0;
+            zs[T] = w_ks[i];
+            vs[T] = w_vs[i];
+          } else {
+            zs[T] = ps.scale_log2;
+            vs[T] = 1.0f;
+          }
         }
       }
       const uint8_t* kbuf = lds[j & 1];
       const uint8_t* vbuf = lds[j & 1] + C::KBUF;
       issue_point();
-      // ---- S^T for all live row tiles
+      if (base < wave_max_lim) {  // some row of the wave sees a key of this chunk
+      // ---- S^T for every row tile (a tile past its rows' keys is masked below)
       f32x4 S[NR][4];
-#pragma unroll
-      for (int rt = 0; rt < NR; ++rt)
-#pragma unroll
-        for (int T = 0; T < 4; ++T) S[rt][T] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      bool live[NR];
-#pragma unroll
-      for (int rt = 0; rt < NR; ++rt) live[rt] = base < tile_lim[rt];
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
-        const int tok = 16 * T + n;
-        const uint8_t* krow = kbuf + tok * C::KROW;
+        const uint8_t* krow = kbuf + k_off[T];
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          const int u = 4 * ks + g;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ((u ^ (tok & (C::KUNITS - 1))) << 4));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + k_unit[ks]);
 #pragma unroll
           for (int rt = 0; rt < NR; ++rt)
-            if (live[rt]) S[rt][T] = mma16<DT_BF16>(a, qop[rt][ks], S[rt][T]);
+            S[rt][T] = mma16<DT_BF16>(a, qop[rt][ks], ks == 0 ? zero : S[rt][T]);
         }
       }
-      // ---- online softmax per row tile; P operands
+      // ---- online softmax per row tile; P operands.  Keys at or past a row's bound
+      // exist only in chunks that reach the wave's smallest bound.
+      const bool need_mask = base + 64 > wave_min_lim;
       u32x4 phi[NR][2], plo[NR][2];
 #pragma unroll
       for (int rt = 0; rt < NR; ++rt) {
-        if (!live[rt]) continue;
-        float x[16];
+        // scores in log2 units are S zs (zs > 0: the softmax scale times K's page
+        // scale); masked keys become -inf in place, which the same path turns into 0
+        if (need_mask) {
+          const int lim = rlim[rt] - base - 4 * g;  // keys 16 T + r below lim are visible
+#pragma unroll
+          for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[rt][T][r] = 16 * T + r < lim ? S[rt][T][r] : -INFINITY;
+        }
+        float cm = -INFINITY;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = base + 16 * T + 4 * g + r;
-            x[4 * T + r] = key < rlim[rt] ? S[rt][T][r] * zs[T] : -INFINITY;
-          }
-        float cm = x[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) cm = fmaxf(cm, x[i]);
+          cm = fmaxf(cm, fmaxf(fmaxf(S[rt][T][0], S[rt][T][1]), fmaxf(S[rt][T][2], S[rt][T][3])) * zs[T]);
         cm = max_groups(cm);
         const float mn = fmaxf(st[rt].m, cm);
         const float mref = mn == -INFINITY ? 0.0f : mn;  // rows that have seen no key yet
@@ -316,10 +381,11 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
         st[rt].m = mn;
         float p[16], psum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
-          psum += p[i];
-        }
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) psum += p[i];
         st[rt].l = st[rt].l * alpha + psum;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
@@ -331,7 +397,11 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) {
             const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
-            const float a = p[i0] * vs[i0 >> 2], b = p[i0 + 1] * vs[i0 >> 2];
+            float a = p[i0], b = p[i0 + 1];
+            if constexpr (kFp8) {
+              a *= vs[i0 >> 2];
+              b *= vs[i0 >> 2];
+            }
             wh[wd] = pack2<C::PT>(a, b);
             if constexpr (C::SPLIT) {
               const f32x2 h = unpack2<C::PT>(wh[wd]);
@@ -347,31 +417,25 @@ paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ 
       // ---- O^T += V^T . P^T
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
-        const int d = 16 * dt + n;
-        const uint8_t* vrow = vbuf + d * C::VROW;
+        const uint8_t* vrow = vbuf + v_off + dt * 16 * C::VROW;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int u_a = 4 * s2 + (g >> 1), u_b = 4 * s2 + 2 + (g >> 1);
-          const u32x2 va = *reinterpret_cast<const u32x2*>(vrow + ((u_a ^ (d & 7)) << 4) + 8 * (g & 1));
-          const u32x2 vb = *reinterpret_cast<const u32x2*>(vrow + ((u_b ^ (d & 7)) << 4) + 8 * (g & 1));
-          const u32x4 a = {va[0], va[1], vb[0], vb[1]};
+          const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + v_unit[s2]);
 #pragma unroll
           for (int rt = 0; rt < NR; ++rt) {
-            if (!live[rt]) continue;
             st[rt].acc[dt] = mma16<C::PT>(a, phi[rt][s2], st[rt].acc[dt]);
             if constexpr (C::SPLIT) st[rt].acc[dt] = mma16<C::PT>(a, plo[rt][s2], st[rt].acc[dt]);
           }
         }
       }
+      }
       issue_point();
       // ---- stage chunk j+1 into the other buffer; advance the page window
       if (j + 1 < nch) chunk_stage<KVT, D>(nxt1, lds[(j + 1) & 1], lds[(j + 1) & 1] + C::KBUF, base + 64, kend);
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        pg0[T] = pg1[T];
-        pg1[T] = pg2[T];
+      if ((j + 1) % kWinChunks == 0 && j + 1 < nch) {  // the next step starts a new window
+        __syncthreads();  // every wave has read the old window
+        fill_window((j + 1) / kWinChunks);
       }
-      chunk_pages(pg2, trow, min(base + 192, 64 * (nch - 1)), kend, ps);
       __syncthreads();
     };
     // chunk j's raw pieces live in ra (j even) / rb (j odd) until staged
