@@ -13,6 +13,12 @@ step (GB/s); `roofline` is the decode kernel's achieved bandwidth against the
 8 TB/s peak; `cpu_baseline` is the plain CPU oracle on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+
+`--workload prefill` measures the fp8 chunked-prefill configuration instead (16
+sequences, 4096 cached + 512 new tokens, H_q 32, H_kv 8, D 128, B 16, E4M3 KV with
+fp32 page scales, bf16 q): a step writes the 512 new tokens' K/V of every sequence
+and runs the causal prefill over the whole context; `value` is TFLOP/s and the
+roofline is the prefill kernel against the dense bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a 512 MiB device copy five times (a kernel of known HBM "
                          "traffic) so that rocprofv3's FETCH_SIZE/WRITE_SIZE can be scaled")
@@ -91,6 +98,9 @@ def main():
     a = parse()
     if a.calibrate:
         calibrate()
+        return
+    if a.gpus == 1 and a.workload == "prefill":
+        prefill_main(a)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -239,6 +249,162 @@ def main():
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(wl) -> float:
+    """4 H_q D flops per (query row, visible key): causal, key t <= ctx - n + i."""
+    nq = np.diff(wl.cu_seqlens_q)
+    vis = 0
+    for s in range(wl.num_seqs):
+        ctx, n = int(wl.context_lens[s]), int(nq[s])
+        vis += n * (ctx - n) + n * (n + 1) // 2
+    return 4.0 * wl.num_q_heads * wl.head_dim * vis
+
+
+def prefill_main(a):
+    import torch
+    import paged_kv_cache_146_amd as pkv
+    from paged_kv_cache_146_amd import workloads as W
+
+    wl = W.fp8_chunked_prefill(seed=5)
+    dev = "cuda"
+    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "fp8")
+    k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
+    ks = torch.from_numpy(wl.k_scale).to(dev)
+    vs = torch.from_numpy(wl.v_scale).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    cu = torch.from_numpy(wl.cu_seqlens_q).to(dev)
+    nq = np.diff(wl.cu_seqlens_q)
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # the cached tokens go in before timing; the step writes the new chunk's tokens
+    start = (wl.context_lens - nq)[wl.fill_seq]
+    old = np.nonzero(wl.fill_pos < start)[0]
+    new = np.nonzero(wl.fill_pos >= start)[0]
+    slab = 1 << 17
+    for o in range(0, len(old), slab):
+        r = old[o:o + slab]
+        sl = pkv.pkv_slot_mapping(bt, torch.from_numpy(wl.fill_seq[r]).to(dev),
+                                  torch.from_numpy(wl.fill_pos[r]).to(dev), wl.block_size)
+        pkv.pkv_kv_cache_write(sl, bits(wl.k_src[r]), bits(wl.v_src[r]), desc, k_pool, v_pool, ks,
+                               vs, src_dtype="bf16")
+    seq_new = torch.from_numpy(wl.fill_seq[new]).to(dev)
+    pos_new = torch.from_numpy(wl.fill_pos[new]).to(dev)
+    k_new, v_new = bits(wl.k_src[new]), bits(wl.v_src[new])
+    slots = torch.empty(len(new), dtype=torch.int64, device=dev)
+    q = bits(wl.q)
+    out = torch.empty_like(q)
+    flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        pkv.pkv_paged_prefill(q, cu, int(nq.max()), desc, k_pool, v_pool, bt, cl,
+                              wl.max_context_len, wl.scale, causal=True, k_scale=ks, v_scale=vs,
+                              out=out, q_dtype="bf16")
+
+    def step():
+        pkv.pkv_slot_mapping(bt, seq_new, pos_new, wl.block_size, out=slots)
+        pkv.pkv_kv_cache_write(slots, k_new, v_new, desc, k_pool, v_pool, ks, vs, src_dtype="bf16")
+        prefill()
+
+    def timed(fn, n):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            flush.sum()
+            starts[i].record()
+            fn()
+            ends[i].record()
+        torch.cuda.synchronize()
+        return np.array([x.elapsed_time(y) for x, y in zip(starts, ends)])
+
+    steps = min(a.steps, 20)
+    for _ in range(min(a.warmup, 3)):
+        flush.sum()
+        step()
+    step_ms = timed(step, steps)
+    pf_ms = timed(prefill, steps)
+
+    flops = prefill_flops(wl)
+    step_us = float(np.mean(step_ms) * 1e3)
+    pf_us = float(np.mean(pf_ms) * 1e3)
+    parity = None
+    try:
+        import oracle
+        opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "fp8")
+        opool.k_scale, opool.v_scale = wl.k_scale, wl.v_scale
+        osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
+        oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+        rows = np.array([0, int(wl.cu_seqlens_q[-1]) - 1], np.int64)
+        ref = oracle.paged_prefill(wl.q, "bf16", wl.cu_seqlens_q, opool, wl.block_table,
+                                   wl.context_lens, wl.scale, causal=True, rows=rows)
+        got = out.float().cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(got - ref)
+        parity = {"rows": rows.tolist(), "max_abs": float(err.max()),
+                  "within_tol": bool((err <= 2e-3 + 1e-2 * np.abs(ref)).all())}
+    except Exception as ex:
+        parity = {"error": repr(ex)}
+    res = {
+        "metric": "chunked prefill TFLOP/s (causal-exact flops) over the paged fp8 cache",
+        "value": round(flops / (step_us * 1e-6) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": min(a.warmup, 3),
+        "ms_per_step": round(step_us / 1e3, 4), "us_per_step": round(step_us, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp8 e4m3 KV)", "data": "synthetic",
+        "config": {"workload": "fp8 KV chunked prefill: 16 seqs x (4096 cached + 512 new), "
+                               "H_q 32, H_kv 8, D 128, B 16, causal, seed 5",
+                   "step": "slot_mapping + kv_cache_write (8192 tokens, fp8) + paged_prefill",
+                   "caches": "flushed before every step"},
+        "flops_per_step": flops,
+        "query_tokens_per_s": round(8192 / (step_us * 1e-6), 1),
+        "roofline": {"bound": "mfma", "kernel": "paged_prefill_kernel",
+                     "achieved": round(flops / (pf_us * 1e-6) / 1e12, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (pf_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_us": round(pf_us, 1)},
+        "parity_spot_check": parity,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(wl, budget_s):
+    """The oracle's prefill on this host's cores over a bounded sample of query rows
+    (every 37th row of the chunk, in turn, until the budget is spent)."""
+    import oracle
+    opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "fp8")
+    opool.k_scale, opool.v_scale = wl.k_scale, wl.v_scale
+    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
+    oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+    cu = wl.cu_seqlens_q
+    total = int(cu[-1])
+    t_used, flops, done = 0.0, 0.0, 0
+    for off in range(37):
+        rows = np.arange(off, total, 37, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.paged_prefill(wl.q, "bf16", cu, opool, wl.block_table, wl.context_lens, wl.scale,
+                             causal=True, rows=rows)
+        t_used += time.perf_counter() - t0
+        seq = np.searchsorted(cu, rows, side="right") - 1
+        n = cu[seq + 1] - cu[seq]
+        vis = wl.context_lens[seq] - n + (rows - cu[seq]) + 1
+        flops += 4.0 * wl.num_q_heads * wl.head_dim * float(vis.sum())
+        done += len(rows)
+        if t_used >= budget_s:
+            break
+    return {"value": round(flops / t_used / 1e12, 5), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of 8192 query rows (every 37th, %d passes), all heads, %.1f s"
+                      % (done, done * 37 // total, t_used)}
 
 
 def cpu_baseline(wl, budget_s):

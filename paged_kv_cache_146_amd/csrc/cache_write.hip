@@ -50,9 +50,11 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
   const long long total = (long long)num_tokens * Hkv * NC;
   const long long idx = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % NC);
-  const int h = (int)((idx / NC) % Hkv);
-  const long long i = idx / ((long long)NC * Hkv);
+  // token fastest: consecutive slots (a prefill chunk, a pool fill) give
+  // consecutive destinations in both pools
+  const long long i = idx % num_tokens;
+  const int c = (int)((idx / num_tokens) % NC);
+  const int h = (int)(idx / ((long long)num_tokens * NC));
   const long long slot = slot_mapping[i];
   if (slot < 0 || slot >= (long long)num_blocks * B) return;
   const long long blk = slot / B, off = slot % B;
@@ -89,9 +91,9 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
   const long long total = (long long)num_tokens * Hkv * NC;
   const long long idx = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % NC);
-  const int h = (int)((idx / NC) % Hkv);
-  const long long i = idx / ((long long)NC * Hkv);
+  const long long i = idx % num_tokens;  // token fastest, as above
+  const int c = (int)((idx / num_tokens) % NC);
+  const int h = (int)(idx / ((long long)num_tokens * NC));
   const long long slot = slot_mapping[i];
   if (slot < 0 || slot >= (long long)num_blocks * B) return;
   const long long blk = slot / B, off = slot % B;
