@@ -161,14 +161,13 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
  *     laid out as part_out float [S][H_q][P_max][D], then part_max float [S][H_q][P_max],
  *     then part_sum float [S][H_q][P_max] (the arrays pkv_split_kv_reduce takes).
  *   partition_size == PKV_PARTITION_BALANCED: enough for PKV_MAX_WORKERS workers,
- *     C + (2 * PKV_MAX_WORKERS + Q) * (num_q_heads / num_kv_heads) * (head_dim + 2) * 4
- *     with C = (num_seqs * num_kv_heads + 1) * 8 rounded up to a multiple of 256 and
- *     Q = num_seqs * num_kv_heads * ceil(max_context_len / 64) / 8 + 1; the layout is
- *     internal (a counter per (sequence, kv head) and a work-queue word, then the
- *     partial states of the pieces of pairs that several workers share).  It needs
- *     no initialisation: counters written by another call are recognised as stale,
- *     so the same workspace serves any number of calls (and graph replays); calls
- *     that share one workspace must not overlap in time.
+ *     C + 2 * PKV_MAX_WORKERS * (num_q_heads / num_kv_heads) * (head_dim + 2) * 4 with
+ *     C = num_seqs * num_kv_heads * 8 rounded up to a multiple of 256; the layout is
+ *     internal (a counter per (sequence, kv head), then the partial states of the
+ *     pairs that workers share).  It needs no initialisation: counters written by
+ *     another call are recognised as stale, and every call leaves its counters at
+ *     rest, so the same workspace serves any number of calls (and graph replays);
+ *     calls that share one workspace must not overlap in time.
  * Errors: PKV_EINVAL (negative sizes, num_q_heads % num_kv_heads != 0, any other
  * partition_size that is not a positive multiple of 64). */
 int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -193,16 +192,12 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
  *      of 64 = the context is split into partitions of that many tokens,
  *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]);
  *      PKV_PARTITION_BALANCED = the 64-token chunks of all (sequence, kv head)
- *      pairs form one stream; the first seven eighths are cut into equal
- *      contiguous shares, one per resident wavefront, and the rest is handed
- *      out chunk by chunk to whichever wavefront is free; the pairs that this
- *      splits are merged by log-sum-exp (same algebra; evenly loaded whatever
- *      the length mix or the speed of each part of the chip; num_seqs <= 16384).
+ *      pairs are cut into equal contiguous shares, one per resident wavefront,
+ *      and the pairs that shares split are merged by log-sum-exp (same
+ *      algebra; evenly loaded whatever the length mix; num_seqs <= 16384).
  *   workspace: device scratch of pkv_decode_workspace_bytes (NULL if 0 bytes);
  *      in balanced mode a smaller workspace just means fewer workers (it must
- *      hold the counters, the queue slots and one worker:
- *      C + (2 + Q') * G * (head_dim + 2) * 4 bytes, Q' as Q with max_context_len
- *      replaced by min(max_context_len, max_blocks_per_seq * block_size)).
+ *      hold the counters and one worker: C + 2 * G * (head_dim + 2) * 4 bytes).
  *      In balanced mode the pairs that several workers share are merged by the
  *      last of them to finish, inside the same kernel launch.
  *   out: device [num_seqs][num_q_heads][head_dim] of q_dtype (rounded to nearest).

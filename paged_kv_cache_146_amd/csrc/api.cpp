@@ -47,16 +47,11 @@ int check_desc(const pkv_pool_desc* d) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// balanced mode: one 8-byte counter per (sequence, kv head) and the queue word of
-// the dynamic units, rounded to 256 bytes
+// balanced mode: one 8-byte counter per (sequence, kv head), rounded to 256 bytes
 size_t balanced_counter_bytes(int num_seqs, int num_kv_heads) {
-  const size_t b = ((size_t)num_seqs * num_kv_heads + 1) * 8;
+  const size_t b = (size_t)num_seqs * num_kv_heads * 8;
   return (b + 255) / 256 * 256;
 }
-
-// balanced mode: partial-state slots beyond the two per worker, one per unit of
-// the dynamic tail (at most an eighth of the 64-token chunks, plus one)
-size_t balanced_dynamic_slots(int64_t units) { return (size_t)(units / 8) + 1; }
 
 // a fresh nonzero tag per balanced call (see the counter scheme in decode.hip)
 uint32_t next_epoch() {
@@ -200,10 +195,8 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
   }
   if (partition_size == PKV_PARTITION_BALANCED) {
     const size_t group = (size_t)(num_q_heads / num_kv_heads);
-    const int64_t units = (int64_t)num_seqs * num_kv_heads * (((int64_t)max_context_len + 63) / 64);
     *bytes = balanced_counter_bytes(num_seqs, num_kv_heads) +
-             (2 * (size_t)PKV_MAX_WORKERS + balanced_dynamic_slots(units)) * group *
-                 ((size_t)head_dim + 2) * sizeof(float);
+             2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
     return PKV_OK;
   }
   if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
@@ -268,25 +261,22 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
     const int group = num_q_heads / pool->num_kv_heads;
     const size_t slot_bytes = (size_t)group * ((size_t)pool->head_dim + 2) * sizeof(float);
     const size_t cnt_bytes = balanced_counter_bytes(num_seqs, pool->num_kv_heads);
-    const size_t dyn_slots = balanced_dynamic_slots(units);
-    if (!workspace || workspace_bytes < cnt_bytes + (2 + dyn_slots) * slot_bytes)
-      return PKV_EWORKSPACE;
+    if (!workspace || workspace_bytes < cnt_bytes + 2 * slot_bytes) return PKV_EWORKSPACE;
     if (!aligned16(workspace)) return PKV_EINVAL;
     int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim,
                                            pool->block_size);
     if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
-    const size_t fit = ((workspace_bytes - cnt_bytes) / slot_bytes - dyn_slots) / 2;
+    const size_t fit = (workspace_bytes - cnt_bytes) / (2 * slot_bytes);
     if ((size_t)nw > fit) nw = (int)fit;
-    const size_t slots = 2 * (size_t)nw + dyn_slots;
     char* base = static_cast<char*>(workspace);
     float* ws = reinterpret_cast<float*>(base + cnt_bytes);
     p.balanced = 1;
     p.split = 1;
     p.num_workers = nw;
-    p.counters = reinterpret_cast<unsigned long long*>(base);  // [S][H_kv], then the queue
+    p.counters = reinterpret_cast<unsigned long long*>(base);         // [S][H_kv]
     p.epoch = next_epoch();
-    p.part_out = ws;                                           // [slots][G][D]
-    p.part_max = ws + slots * group * pool->head_dim;          // [slots][G][2]
+    p.part_out = ws;                                                  // [2*nw][G][D]
+    p.part_max = ws + (size_t)2 * nw * group * pool->head_dim;        // [2*nw][G][2]
     rc = pkv::launch_decode(p, as_stream(stream));
     return rc == 0 ? PKV_OK : rc;
   }

@@ -657,66 +657,23 @@ __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch,
   }
 }
 
-// Work split of the balanced kernel.  Units [0, Us) are cut into equal static
-// shares, one per worker; units [Us, U) are handed out one at a time, in order,
-// to whichever worker asks next (workers run at different speeds: the XCDs do
-// not all reach HBM equally fast).  Every dynamic unit is a piece of its own.
-struct Split {
-  int U, Us, NWe;
-};
-
-__device__ __forceinline__ int static_units(int U, int NWe) {
-  return U >= 4 * NWe ? U - U / 8 : U;
-}
-
-// The pieces of pair [sf, sf + nch): the static workers wa..wb (when the pair
-// starts below Us), then one piece per dynamic unit.  Slot of a static piece:
-// 2w when it starts the worker's share, else 2w + 1; slot of dynamic unit u:
-// 2 NWe + (u - Us).
-struct PairPieces {
-  int wa, wb, nstat, d0, d1;  // dynamic units [d0, d1)
-};
-
-__device__ __forceinline__ PairPieces pair_pieces(const Split& sp, int sf, int nch) {
-  PairPieces pc;
-  const int se = sf + nch;
-  if (sf < sp.Us) {
-    pc.wa = worker_of(sf, sp.Us, sp.NWe);
-    pc.wb = worker_of(min(se, sp.Us) - 1, sp.Us, sp.NWe);
-    pc.nstat = pc.wb - pc.wa + 1;
-  } else {
-    pc.wa = pc.wb = 0;
-    pc.nstat = 0;
-  }
-  pc.d0 = max(sf, sp.Us);
-  pc.d1 = max(se, sp.Us);
-  return pc;
-}
-
-// One wavefront merges the partial states of a shared pair (log2-domain maxima)
-// in a single online pass over its pieces.  Lane (n, g) takes head n and dims
-// 16 dt + 4 g + r, the layout the pieces were written in.  Reads are
-// device-scope loads, matching the device-scope stores of the writers.
+// One wavefront merges the partial states of a shared pair (pieces of workers wa..wb,
+// log2-domain maxima) in a single online pass over the pieces.  Lane (n, g) takes
+// head n and dims 16 dt + 4 g + r, the layout the pieces were written in.  Reads
+// are device-scope loads, matching the device-scope stores of the writers.
 template <int QDT, int D>
 __device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict__ out,
-                           const DecodeScalars& sc, const Split& sp, int s, int kvh, int sf,
-                           int nch, int n, int g) {
+                           const DecodeScalars& sc, int s, int kvh, int u0, int wa, int wb,
+                           int U, int NWe, int n, int g) {
   constexpr int NDT = D / 16;
-  const PairPieces pc = pair_pieces(sp, sf, nch);
+  const int first_slot = worker_start(wa, U, NWe) != u0 ? 2 * wa + 1 : 2 * wa;
   const int hh = n < sc.G ? n : sc.G - 1;
   float M = -INFINITY, L = 0.0f;
   f32x4 O[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int total = pc.nstat + (pc.d1 - pc.d0);
-  for (int i = 0; i < total; ++i) {
-    int slot;
-    if (i < pc.nstat) {
-      const int w = pc.wa + i;
-      slot = (w == pc.wa && worker_start(w, sp.Us, sp.NWe) != sf) ? 2 * w + 1 : 2 * w;
-    } else {
-      slot = 2 * sp.NWe + (pc.d0 + i - pc.nstat - sp.Us);
-    }
+  for (int w = wa; w <= wb; ++w) {
+    const int slot = w == wa ? first_slot : 2 * w;
     float* ml = slot_ml + ((size_t)slot * sc.G + hh) * 2;
     const float m = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float l = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -743,44 +700,11 @@ __device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict_
   }
 }
 
-// The queue of dynamic units: one 64-bit word (epoch << 32 | next unit).  A grab
-// is an atomic max with (epoch << 32), which turns a word left by an earlier
-// call into (epoch, 0) and leaves a current one alone, then an atomic add of 1
-// that returns the unit; its value is used a pipeline stage later, so the wait
-// for it never drains the prefetched chunks.  A returned word of another epoch
-// (a fresh workspace holding garbage, or the epoch counter wrapped) falls back to
-// a compare-exchange loop that claims the next unit of this call exactly.
-__device__ __forceinline__ void queue_issue(unsigned long long* qw, uint32_t epoch,
-                                            unsigned long long& ticket) {
-  __hip_atomic_fetch_max(qw, (unsigned long long)epoch << 32, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  ticket = __hip_atomic_fetch_add(qw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t queue_resolve(unsigned long long* qw, uint32_t epoch,
-                                                  unsigned long long ticket) {
-  if ((uint32_t)(ticket >> 32) == epoch) return (uint32_t)ticket;
-  unsigned long long old = __hip_atomic_load(qw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const bool cur = (uint32_t)(old >> 32) == epoch;
-    const uint32_t got = cur ? (uint32_t)old : 0u;
-    const unsigned long long nw = ((unsigned long long)epoch << 32) | (got + 1u);
-    unsigned long long expected = old;
-    if (__hip_atomic_compare_exchange_strong(qw, &expected, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return got;
-    old = expected;
-  }
-}
-
-// where a worker is in the unit stream: unit u = chunk j of pair (s, kvh); dyn:
-// a unit of the dynamic queue; end: there is no unit here (the share is done)
+// where a worker is in the unit stream: unit u = chunk j of pair (s, kvh), the
+// k-th unit of the worker's share
 struct Pos {
   int u, s, kvh, j, nch, ctx, k;
-  int dyn, end;
 };
-
-constexpr int kMaxPending = 24;  // published pieces per worker counted at its end
 
 template <int KVT, int CT, int D, bool SMALLB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
@@ -795,7 +719,6 @@ paged_decode_balanced_kernel(
 
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
-  __shared__ int pend[kWaves][kMaxPending];  // pair index s * H_kv + kvh of unclaimed pieces
 
   unit_prefix(context_lens, sc.S, sc.ctx_cap, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
@@ -806,21 +729,15 @@ paged_decode_balanced_kernel(
         store_any(out, CT, (size_t)s0 * sc.Hq * D + i, 0.0f);
     }
   }
-  Split sp;
-  sp.U = U;
-  sp.NWe = min(sc.num_workers, U);
-  sp.Us = static_units(U, sp.NWe);
-  const int n_dyn = U - sp.Us;
-  unsigned long long* qword = counters + (size_t)sc.S * sc.Hkv;  // the dynamic queue
+  const int NWe = min(sc.num_workers, U);
   // wave-uniform values go through readfirstlane so that the compiler keeps them,
   // and the addresses derived from them, scalar
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int w = blockIdx.x * kWaves + wave;
-  if (w >= sp.NWe) return;  // no barrier below this point
-  const int u_begin = worker_start(w, sp.Us, sp.NWe);
-  const int u_end = worker_start(w + 1, sp.Us, sp.NWe);
-  const int n_units = u_end - u_begin;  // >= 1: NWe <= Us
+  if (w >= NWe) return;  // no barrier below this point
+  const int u_begin = worker_start(w, U, NWe);
+  const int u_end = worker_start(w + 1, U, NWe);
 
   auto clamp_ctx = [&](int s) {
     const int c = context_lens[s];
@@ -836,95 +753,74 @@ paged_decode_balanced_kernel(
     p.kvh = rel / p.nch;
     p.j = rel - p.kvh * p.nch;
     p.ctx = clamp_ctx(p.s);
+    return p;
+  };
+  // the unit after p, or p itself at the end of the share (its loads are then
+  // repeated and never used)
+  const int n_units = u_end - u_begin;
+  auto first_pos = [&]() {
+    Pos p = locate(u_begin);
     p.k = 0;
-    p.dyn = 0;
-    p.end = 0;
     return p;
   };
-  // ---- the dynamic queue: one grab outstanding at a time, issued a stage before
-  // its unit is needed
-  unsigned long long ticket = 0;
-  bool grab_out = false, exhausted = n_dyn == 0;
-  auto grab_issue = [&]() {
-    if (!grab_out && !exhausted) {
-      queue_issue(qword, sc.epoch, ticket);
-      grab_out = true;
-    }
-  };
-  // the unit after p in the worker's order, or p marked `end`
+  // the unit after p, or p itself after the last one (its loads are then never
+  // issued)
   auto advance = [&](Pos p) {
-    if (p.end) return p;
-    if (!p.dyn && p.k + 1 < n_units) {  // next unit of the static share
-      ++p.u;
-      ++p.k;
-      if (++p.j < p.nch) return p;
-      p.j = 0;
-      if (++p.kvh < sc.Hkv) return p;
-      p.kvh = 0;
-      do {
-        ++p.s;
-      } while (prefix[p.s + 1] == prefix[p.s]);  // stops: unit p.u exists
-      p.s = uniform(p.s);
-      p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
-      p.ctx = clamp_ctx(p.s);
-      return p;
-    }
-    grab_issue();  // normally issued a stage earlier; this waits for it only at the start
-    const uint32_t b = uniform((int)queue_resolve(qword, sc.epoch, ticket));
-    grab_out = false;
-    if ((int)b >= n_dyn) {
-      exhausted = true;
-      p.end = 1;
-      return p;
-    }
-    const int k = p.k + 1;
-    p = locate(sp.Us + (int)b);
-    p.k = k;
-    p.dyn = 1;
+    if (p.k + 1 >= n_units) return p;
+    ++p.u;
+    ++p.k;
+    if (++p.j < p.nch) return p;
+    p.j = 0;
+    if (++p.kvh < sc.Hkv) return p;
+    p.kvh = 0;
+    do {
+      ++p.s;
+    } while (prefix[p.s + 1] == prefix[p.s]);  // stops: unit p.u exists
+    p.s = uniform(p.s);
+    p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
+    p.ctx = clamp_ctx(p.s);
     return p;
   };
-  // after a position is known: when the unit after it comes from the queue,
-  // request it now
-  auto prefetch_grab = [&](const Pos& p) {
-    if (!p.end && (p.dyn || p.k + 1 >= n_units)) grab_issue();
-  };
-  // a piece ends at the last chunk of its pair, of the static share, and at
-  // every dynamic unit
-  auto piece_ends = [&](const Pos& p) { return p.dyn || p.j == p.nch - 1 || p.k + 1 >= n_units; };
+  // a piece ends at the last chunk of its pair or of the worker's share
+  auto piece_ends = [&](const Pos& p) { return p.j == p.nch - 1 || p.k + 1 >= n_units; };
   auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W; };
 
   State<C> st;
   state_init(st);
   typename C::QOp qop[C::NQ];
-  Pos pc = locate(u_begin);
+  Pos pc = first_pos();
   load_q<C>(qop, q, pc.s, pc.kvh, sc, n, g);
   q_live<C>(qop, qop, n < sc.G);
-  int piece_j0 = pc.j, piece_u0 = pc.u, piece_dyn = 0;
+  int piece_j0 = pc.j, piece_u0 = pc.u;
 
-  // Published pieces are counted only after their stores have completed; the
-  // wait for that comes at the end of the share, where no prefetched chunk is in
-  // flight (the vector-memory counter covers loads and stores alike, so an
-  // earlier wait would drain the pipeline).  The list spills early only if full.
+  // Shared pairs whose piece this worker has published but not yet counted: at
+  // most the first and the last piece of the share.  A piece is counted only
+  // after its stores have completed; the wait for that comes at the end of the
+  // share, where no prefetched chunk is in flight (the vector-memory counter
+  // covers loads and stores alike, so an earlier wait would drain the pipeline).
+  int pend_s0 = 0, pend_k0 = 0, pend_n0 = 0, pend_s1 = 0, pend_k1 = 0, pend_n1 = 0;
   int n_pend = 0;
+  auto claim = [&](int ps, int pk, int pn) {
+    ps = uniform(ps);
+    pk = uniform(pk);
+    pn = uniform(pn);
+    const int seg_first = uniform(prefix[ps]) + pk * pn;
+    const int wa = worker_of(seg_first, U, NWe);
+    const int wb = worker_of(seg_first + pn - 1, U, NWe);
+    int last = 0;
+    if (lane == 0)
+      last = claim_last(counters + (size_t)ps * sc.Hkv + pk, sc.epoch, (uint32_t)(wb - wa + 1));
+    last = uniform(last);  // lane 0's answer
+    if (last) merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
+  };
   auto claim_pending = [&]() {
     __builtin_amdgcn_s_waitcnt(0);  // every store of the pieces has completed
-    for (int i = 0; i < n_pend; ++i) {
-      const int pi = uniform(pend[wave][i]);
-      const int ps = pi / sc.Hkv, pk = pi - ps * sc.Hkv;
-      const int pfx = uniform(prefix[ps]);
-      const int pn = uniform((prefix[ps + 1] - pfx) / sc.Hkv);
-      const int sf = pfx + pk * pn;
-      const PairPieces pcs = pair_pieces(sp, sf, pn);
-      int last = 0;
-      if (lane == 0)
-        last = claim_last(counters + (size_t)pi, sc.epoch, (uint32_t)(pcs.nstat + pcs.d1 - pcs.d0));
-      last = uniform(last);  // lane 0's answer
-      if (last) merge_pair<CT, D>(slot_out, slot_ml, out, sc, sp, ps, pk, sf, pn, n, g);
-    }
+    if (n_pend > 0) claim(pend_s0, pend_k0, pend_n0);
+    if (n_pend > 1) claim(pend_s1, pend_k1, pend_n1);
     n_pend = 0;
   };
 
-  // close the piece that ends with chunk p: whole pairs go straight to `out`,
+  // close the piece that ends with chunk pc: whole pairs go straight to `out`,
   // shared ones to this worker's slot, merged by the last of their workers
   auto finish_piece = [&](const Pos& p) {
     const float lw = sum_groups(st.l);
@@ -940,8 +836,8 @@ paged_decode_balanced_kernel(
       // Publish the partial state with device-scope stores (coherent across the
       // XCDs' L2 caches without a cache-wide write-back); no cache-wide fence is
       // needed on either side.
-      const int slot = piece_dyn ? 2 * sp.NWe + (piece_u0 - sp.Us)
-                                 : 2 * w + (piece_u0 == u_begin ? 0 : 1);
+      // slot 2w: the piece that starts the worker's share; 2w+1: the one that ends it
+      const int slot = 2 * w + (piece_u0 == u_begin ? 0 : 1);
       if (n < sc.G) {
         const float inv = 1.0f / lw;
         float* so = slot_out + ((size_t)slot * sc.G + n) * D + 4 * g;
@@ -957,16 +853,19 @@ paged_decode_balanced_kernel(
           __hip_atomic_store(ml + 1, lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      if (n_pend == kMaxPending) claim_pending();
-      if (lane == 0) pend[wave][n_pend] = p.s * sc.Hkv + p.kvh;
+      // counted at the end of the share (claim_pending)
+      if (n_pend == 0) {
+        pend_s0 = p.s;
+        pend_k0 = p.kvh;
+        pend_n0 = p.nch;
+      } else {
+        pend_s1 = p.s;
+        pend_k1 = p.kvh;
+        pend_n1 = p.nch;
+      }
       ++n_pend;
     }
     state_init(st);
-  };
-  auto start_piece = [&](const Pos& p) {
-    piece_j0 = p.j;
-    piece_u0 = p.u;
-    piece_dyn = p.dyn;
   };
 
   if constexpr (SMALLB) {
@@ -980,61 +879,65 @@ paged_decode_balanced_kernel(
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
       chunk_softmax_pv<C, KVT, CT, 16>(st, S, ch.v, sc.scale_log2, ks, vs,
                                        min(64, pc.ctx - 64 * pc.j), g);
-      if (pn.end || piece_ends(pc)) {
+      const bool done = pc.k + 1 >= n_units;
+      if (done || piece_ends(pc)) {
         finish_piece(pc);
-        if (pn.end) break;
+        if (done) break;
         if (pn.s != pc.s || pn.kvh != pc.kvh) {
           load_q<C>(qop, q, pn.s, pn.kvh, sc, n, g);
           q_live<C>(qop, qop, n < sc.G);
         }
-        start_piece(pn);
+        piece_j0 = pn.j;
+        piece_u0 = pn.u;
       }
       pc = pn;
     }
   } else {
-    // Software pipeline over two chunk buffers: the stage requests the next
-    // chunk into the buffer freed by the previous stage, then computes the
-    // current one.  The table entries run one chunk ahead of the requests, the
-    // queue grab one stage ahead of its unit.  The next pair's q is loaded into
-    // qop right after the current pair's last scores have consumed it.
+    // Software pipeline over a ring of NBUF chunk buffers: on entry to a stage
+    // the loads of the next NBUF-2 chunks are in flight; the stage requests
+    // chunk +NBUF-1 into the buffer freed by the previous stage, then computes
+    // the current one.  The table entries run one chunk ahead of the requests.
+    // The next pair's q is loaded into qop right after the current pair's last
+    // scores have consumed it.
     constexpr int NB = C::NBUF;
-    static_assert(NB == 2, "the ring below is written for two buffers");
     Chunk<C> R[NB];
-    Pos pp[NB];  // pp[0]: the chunk computed this stage, pp[1]: the one requested
+    Pos pp[NB];          // pp[k]: position of the chunk k stages ahead of pc
     float ksr[NB][4], vsr[NB][4];
 #pragma unroll
     for (int k = 0; k < NB; ++k)
 #pragma unroll
       for (int T = 0; T < 4; ++T) ksr[k][T] = vsr[k][T] = 1.0f;
+    pp[0] = pc;
     auto issue = [&](Chunk<C>& dst, const Pos& p, const Pages& pg, float (&ks)[4], float (&vs)[4]) {
       issue_k<C>(dst.k, k_pool, pg, p.kvh, sc, n, g);
       issue_v<C>(dst.v, v_pool, pg, p.kvh, sc, n, g);
       if constexpr (kFp8) page_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc);
     };
     auto pages_at = [&](const Pos& p) { return pages_of(trow_of(p), 64 * p.j, p.ctx, sc); };
-    pp[0] = pc;
-    issue(R[0], pp[0], pages_at(pp[0]), ksr[0], vsr[0]);
-    prefetch_grab(pp[0]);
-    pp[1] = advance(pp[0]);
-    prefetch_grab(pp[1]);
-    Pages en = pages_at(pp[1]);
+#pragma unroll
+    for (int k = 0; k + 1 < NB; ++k) {
+      if (k > 0) pp[k] = advance(pp[k - 1]);
+      issue(R[k], pp[k], pages_at(pp[k]), ksr[k], vsr[k]);
+    }
+    pp[NB - 1] = advance(pp[NB - 2]);
+    Pages en = pages_at(pp[NB - 1]);
     bool q_raw = false;  // qop holds a fresh load whose dead columns are not yet zeroed
     bool done = false;
-    // stage: chunk pp[0] sits in R[c]; chunk pp[1] goes to R[f]
+    // stage: chunk pp[0] sits in R[c]; chunk pp[NB-1] goes to R[f]
     auto stage = [&](Chunk<C>& cur, Chunk<C>& fill, int c, int f) {
       if (q_raw) {
         q_live<C>(qop, qop, n < sc.G);
         q_raw = false;
       }
-      const Pos p0 = pp[0];
-      const bool last = pp[1].end;
+      const Pos& p0 = pp[0];
+      const bool last = p0.k + 1 >= n_units;
+      const bool fetch = pp[NB - 1].k != pp[NB - 2].k;  // a chunk that is not a repeat
       Pages en2 = en;
-      Pos pnext = pp[1];
-      if (!last) {
-        issue(fill, pp[1], en, ksr[f], vsr[f]);
-        pnext = advance(pp[1]);
-        prefetch_grab(pnext);
-        if (!pnext.end) en2 = pages_at(pnext);
+      Pos pnext = pp[NB - 1];
+      if (fetch) {
+        issue(fill, pp[NB - 1], en, ksr[f], vsr[f]);
+        pnext = advance(pp[NB - 1]);
+        en2 = pages_at(pnext);
       }
       issue_point();
       f32x4 S[4];
@@ -1048,19 +951,30 @@ paged_decode_balanced_kernel(
       issue_point();
       if (last || piece_ends(p0)) {
         finish_piece(p0);
-        start_piece(pp[1]);
+        piece_j0 = pp[1].j;
+        piece_u0 = pp[1].u;
         q_raw = new_pair;
       }
       done = last;
-      pp[0] = pp[1];
-      pp[1] = pnext;
+#pragma unroll
+      for (int k = 0; k + 1 < NB; ++k) pp[k] = pp[k + 1];
+      pp[NB - 1] = pnext;
       en = en2;
     };
     while (true) {
-      stage(R[0], R[1], 0, 1);
-      if (done) break;
-      stage(R[1], R[0], 1, 0);
-      if (done) break;
+      if constexpr (NB == 3) {
+        stage(R[0], R[2], 0, 2);
+        if (done) break;
+        stage(R[1], R[0], 1, 0);
+        if (done) break;
+        stage(R[2], R[1], 2, 1);
+        if (done) break;
+      } else {
+        stage(R[0], R[1], 0, 1);
+        if (done) break;
+        stage(R[1], R[0], 1, 0);
+        if (done) break;
+      }
     }
   }
   if (n_pend) claim_pending();

@@ -121,6 +121,63 @@ def test_split_reduce_standalone():
         assert_close(to_f64(out, dt), ref, "reduce " + dt)
 
 
+def _balanced_ws_bytes(wl, workers):
+    """Workspace of the balanced mode that holds exactly `workers` workers: one 8-byte
+    counter per (sequence, kv head), rounded to 256 bytes, then 2 * workers partial states
+    of G x (D + 2) floats."""
+    S, Hkv, D = wl.num_seqs, wl.num_kv_heads, wl.head_dim
+    G = wl.num_q_heads // Hkv
+    C = -(-S * Hkv * 8 // 256) * 256
+    return C + 2 * workers * G * (D + 2) * 4
+
+
+@pytest.mark.parametrize("workers", [1, 3, 8, 37])
+def test_balanced_few_workers(workers):
+    # Few workers give long shares that cut many pairs, and pairs that span several
+    # shares, so most of the output comes from merged pieces.  The workspace starts as
+    # 0xFF garbage and serves two calls in a row: the first call's counters must read
+    # as stale in the second.
+    import torch
+    wl = W.llama3_8b_decode(small=True)
+    case = GpuCase(wl)
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, oracle_pool(wl), wl.block_table,
+                              wl.context_lens, wl.scale)
+    ws = torch.full((_balanced_ws_bytes(wl, workers),), 0xFF, dtype=torch.uint8, device="cuda")
+    for call in range(2):
+        out = to_f64(case.decode(partition_size=-1, workspace=ws), wl.q_dtype)
+        print(assert_close(out, ref, "%s workers=%d call %d" % (wl.name, workers, call)))
+
+
+def test_balanced_graph_replay():
+    # A captured call reuses its epoch on every replay: the counters it uses must be
+    # back at rest when it ends.  An eager call between replays moves them to a newer
+    # epoch, which the replay must read as stale.
+    import torch
+    wl = W.llama3_8b_decode(small=True)
+    case = GpuCase(wl)
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, oracle_pool(wl), wl.block_table,
+                              wl.context_lens, wl.scale)
+    ws = torch.full((_balanced_ws_bytes(wl, 8),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = case.nan_out()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        case.decode(partition_size=-1, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        case.decode(partition_size=-1, workspace=ws, out=out)
+    for r in range(3):
+        out.view(torch.uint8).fill_(0xFF)
+        graph.replay()
+        torch.cuda.synchronize()
+        print(assert_close(to_f64(out, wl.q_dtype), ref, "replay %d" % r))
+        if r == 1:
+            eager = case.decode(partition_size=-1, workspace=ws)
+            print(assert_close(to_f64(eager, wl.q_dtype), ref, "eager between replays"))
+
+
 # ---- full-size workloads: write path bit-exact, sampled sequences vs the oracle ----------
 def test_llama3_8b_full_sampled():
     wl = W.llama3_8b_decode()

@@ -103,13 +103,10 @@ def test_decode_workspace_bytes():
     assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 512) == 64 * 32 * 8 * 130 * 4
     assert pkv.pkv_decode_workspace_bytes(8, 64, 8, 128, 131072, 512) == 8 * 64 * 256 * 130 * 4
     assert pkv.pkv_decode_workspace_bytes(2, 4, 2, 64, 0, 64) == 0
-    # balanced: one 8-byte counter per (sequence, kv head) and a queue word, rounded up to
-    # 256 bytes, then two partial states per worker and one per unit of the dynamic tail
-    # (an eighth of the 64-token chunk units, plus one), each G x (D + 2) floats
-    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == \
-        4352 + (2 * 4096 + 64 * 8 * 64 // 8 + 1) * 4 * 130 * 4
-    assert pkv.pkv_decode_workspace_bytes(3, 4, 2, 64, 100, -1) == \
-        256 + (2 * 4096 + 3 * 2 * 2 // 8 + 1) * 2 * 66 * 4
+    # balanced: one 8-byte counter per (sequence, kv head), rounded up to 256 bytes, then
+    # two partial states per worker, each G x (D + 2) floats
+    assert pkv.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, -1) == 4096 + 2 * 4096 * 4 * 130 * 4
+    assert pkv.pkv_decode_workspace_bytes(3, 4, 2, 64, 100, -1) == 256 + 2 * 4096 * 2 * 66 * 4
     with pytest.raises(pkv.PagedKVError):
         pkv.pkv_decode_workspace_bytes(2, 4, 2, 64, 100, 100)  # not a multiple of 64
     with pytest.raises(pkv.PagedKVError):
