@@ -242,8 +242,11 @@ int pkv_split_kv_reduce(const float* part_out, const float* part_max, const floa
  *   16..64 (a 16-token tile must lie in one block); group size G = H_q/H_kv
  *   in {1, 2, 4, 8, 16}.  fp8 keys widen exactly to bf16 for QK^T and K's
  *   scale multiplies the scores; fp8 values widen exactly to f16 and V's scale
- *   multiplies the probabilities, which enter P.V as f16.  With a bf16 pool
- *   the probabilities enter P.V as a hi + lo pair of bf16 values.
+ *   multiplies the probabilities, which enter P.V as f16 (the probabilities are
+ *   taken against a reference that trails the running max by less than a
+ *   factor 16, so v_scale must stay below 4096 for f16 to hold them; the
+ *   E4M3 values it scales then reach 1.8e6).  With a bf16 pool the
+ *   probabilities enter P.V as a hi + lo pair of bf16 values.
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
 int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
                       int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,

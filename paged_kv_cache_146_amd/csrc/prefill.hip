@@ -171,6 +171,10 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
   }
 }
 
+// Headroom of the lazily moved softmax reference, in log2 units: p <= 2^kLazyMax.
+// With the fp8 V scale folded into P (f16), scales up to 65504 / 2^kLazyMax keep P finite.
+constexpr float kLazyMax = 4.0f;
+
 // per-row online-softmax state of one row tile: lane (n, g) holds column n
 template <int D>
 struct RowState {
@@ -375,10 +379,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         for (int T = 0; T < 4; ++T)
           cm = fmaxf(cm, fmaxf(fmaxf(S[rt][T][0], S[rt][T][1]), fmaxf(S[rt][T][2], S[rt][T][3])) * zs[T]);
         cm = max_groups(cm);
-        const float mn = fmaxf(st[rt].m, cm);
-        const float mref = mn == -INFINITY ? 0.0f : mn;  // rows that have seen no key yet
-        const float alpha = __builtin_amdgcn_exp2f(st[rt].m - mref);
-        st[rt].m = mn;
+        // The reference max moves only when a chunk's max passes it by more than
+        // kLazyMax, so the accumulators are rescaled rarely (the softmax does not
+        // depend on the reference); p then stays below 2^kLazyMax.
+        const bool moves = cm > st[rt].m + kLazyMax;
+        if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+          const float mn = moves ? cm : st[rt].m;
+          const float alpha = __builtin_amdgcn_exp2f(st[rt].m - mn);  // 0 for a row's first keys
+          st[rt].m = mn;
+          st[rt].l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
+        }
+        const float mref = st[rt].m == -INFINITY ? 0.0f : st[rt].m;  // rows that have seen no key yet
         float p[16], psum = 0.0f;
 #pragma unroll
         for (int T = 0; T < 4; ++T)
@@ -386,11 +399,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
 #pragma unroll
         for (int i = 0; i < 16; ++i) psum += p[i];
-        st[rt].l = st[rt].l * alpha + psum;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
-        }
+        st[rt].l += psum;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           uint32_t wh[4], wl[4];

@@ -61,16 +61,25 @@ __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
 }
 
 // eight E4M3 codes (two words) -> eight CT values; exact, as every E4M3 value is
-// representable in bf16 and in f16
+// representable in bf16 and in f16.  The scaled conversion widens two codes per
+// instruction; it applies only the power-of-two part of its scale, so with 1.0
+// it is the plain widening (checked against every code, NaN included).
 template <int CT>
 __device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-  const u32x4 r = {pack2<CT>(a[0], a[1]), pack2<CT>(b[0], b[1]), pack2<CT>(c[0], c[1]),
-                   pack2<CT>(d[0], d[1])};
-  return r;
+  if constexpr (CT == DT_F16) {
+    const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+    return r;
+  } else {
+    static_assert(CT == DT_BF16, "fp8 widens to f16 or bf16");
+    const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+    return r;
+  }
 }
 
 // max / sum over the four lane groups {L, L^16, L^32, L^48}; every lane of the
