@@ -149,8 +149,10 @@ def main():
                                        wl.scale, partition_size=P, workspace=ws, out=out)
 
     def step():
-        pkv.pkv_slot_mapping(bt, seq_idx, pos_new, wl.block_size, out=slots)
-        pkv.pkv_kv_cache_write(slots, k_new, v_new, desc, k_pool, v_pool)
+        # slot mapping and scatter of the new tokens in one launch (the slots are
+        # written out too), then the decode
+        pkv.pkv_kv_cache_append(bt, seq_idx, pos_new, k_new, v_new, desc, k_pool, v_pool,
+                                slot_mapping_out=slots)
         decode()
 
     def timed(fn, n):
@@ -230,7 +232,7 @@ def main():
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
             "kv_dtype": "bf16", "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
-            "step": "slot_mapping + kv_cache_write + paged_attention_decode",
+            "step": "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) + paged_attention_decode",
         },
         "algorithmic_bytes_per_step": sbytes,
         "decode_tokens_per_s": round(wl.num_seqs / (step_us * 1e-6), 1),

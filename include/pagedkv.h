@@ -149,6 +149,20 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
                        void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
                        void* stream);
 
+/* [P1 §3, §4.1] Slot mapping and scatter in one launch: token i is written as by
+ * pkv_kv_cache_write at the slot pkv_slot_mapping computes for
+ * (seq_idx[i], positions[i]) through block_table (-1 cases skipped).  Same
+ * arguments and rules as those two calls; slot_mapping_out (device int64
+ * [num_tokens]) receives the slots when non-NULL.  For a decode step, where the
+ * one new token of each sequence needs no separate slot array.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
+int pkv_kv_cache_append(const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* seq_idx, const int32_t* positions, int32_t num_tokens,
+                        const void* k, const void* v, int32_t src_dtype,
+                        const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                        const float* k_scale, const float* v_scale, int64_t* slot_mapping_out,
+                        void* stream);
+
 /* partition_size value selecting balanced split-KV (see pkv_paged_attention_decode) */
 #define PKV_PARTITION_BALANCED (-1)
 /* upper bound on the wavefront workers of the balanced mode */

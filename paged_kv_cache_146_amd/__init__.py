@@ -28,7 +28,7 @@ STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ERANGE", -3: "PKV_EUNSUPPORTED
 
 EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_validate_block_table", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_decode_workspace_bytes", "pkv_paged_attention_decode", "pkv_split_kv_reduce",
+           "pkv_kv_cache_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode", "pkv_split_kv_reduce",
            "pkv_paged_prefill"]
 
 
@@ -74,6 +74,8 @@ def lib():
                     "pkv_validate_block_table": (ctypes.c_int, [P, I32, I32, P, I32, I32]),
                     "pkv_slot_mapping": (ctypes.c_int, [P, I32, I32, P, P, I32, I32, P, P]),
                     "pkv_kv_cache_write": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, P, P, P]),
+                    "pkv_kv_cache_append": (ctypes.c_int, [P, I32, I32, P, P, I32, P, P, I32, P,
+                                                           P, P, P, P, P, P]),
                     "pkv_decode_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, P]),
                     "pkv_paged_attention_decode": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P,
                                                                   P, I32, P, I32, F, I32, P, SZ,
@@ -220,6 +222,24 @@ def pkv_kv_cache_write(slot_mapping, k, v, desc: PoolDesc, k_pool, v_pool, k_sca
                                     _ptr(k_scale, "k_scale", allow_none=True),
                                     _ptr(v_scale, "v_scale", allow_none=True), _stream(stream)),
            "pkv_kv_cache_write")
+
+
+def pkv_kv_cache_append(block_table, seq_idx, positions, k, v, desc: PoolDesc, k_pool, v_pool,
+                        k_scale=None, v_scale=None, src_dtype=None, slot_mapping_out=None,
+                        stream=None):
+    T = int(seq_idx.numel())
+    S, W = (int(block_table.shape[0]), int(block_table.shape[1]))
+    sd = dtype_code(src_dtype if src_dtype is not None else k.dtype)
+    _check(lib().pkv_kv_cache_append(_ptr(block_table, "block_table"), S, W,
+                                     _ptr(seq_idx, "seq_idx"), _ptr(positions, "positions"), T,
+                                     _ptr(k, "k"), _ptr(v, "v"), sd, ctypes.byref(desc),
+                                     _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+                                     _ptr(k_scale, "k_scale", allow_none=True),
+                                     _ptr(v_scale, "v_scale", allow_none=True),
+                                     _ptr(slot_mapping_out, "slot_mapping_out", allow_none=True),
+                                     _stream(stream)),
+           "pkv_kv_cache_append")
+    return slot_mapping_out
 
 
 PARTITION_BALANCED = -1

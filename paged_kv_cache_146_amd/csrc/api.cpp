@@ -146,15 +146,17 @@ int pkv_slot_mapping(const int32_t* block_table, int32_t num_seqs, int32_t max_b
   return rc == 0 ? PKV_OK : rc;
 }
 
-int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
-                       const void* v, int32_t src_dtype, const pkv_pool_desc* pool,
-                       void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
-                       void* stream) {
+namespace {
+
+// argument checks shared by the write and the append
+int check_write(int32_t num_tokens, const void* k, const void* v, int32_t src_dtype,
+                const pkv_pool_desc* pool, void* k_pool, void* v_pool, const float* k_scale,
+                const float* v_scale) {
   int rc = check_desc(pool);
   if (rc != PKV_OK) return rc;
   if (num_tokens < 0) return PKV_EINVAL;
   if (num_tokens == 0) return PKV_OK;
-  if (!slot_mapping || !k || !v || !k_pool || !v_pool) return PKV_EINVAL;
+  if (!k || !v || !k_pool || !v_pool) return PKV_EINVAL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_EINVAL;
   if (elem_bytes(src_dtype) == 0 || src_dtype == PKV_FP8_E4M3) return PKV_EINVAL;
@@ -163,8 +165,13 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
   } else if (src_dtype != pool->kv_dtype) {
     return PKV_EINVAL;  // descriptor/dtype mismatch: no silent conversion
   }
-  pkv::WriteLaunch p;
-  p.slot_mapping = slot_mapping;
+  return PKV_OK;
+}
+
+pkv::WriteLaunch write_launch(int32_t num_tokens, const void* k, const void* v, int32_t src_dtype,
+                              const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                              const float* k_scale, const float* v_scale) {
+  pkv::WriteLaunch p{};
   p.num_tokens = num_tokens;
   p.k = k;
   p.v = v;
@@ -178,6 +185,46 @@ int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const vo
   p.num_kv_heads = pool->num_kv_heads;
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
+  return p;
+}
+
+}  // namespace
+
+int pkv_kv_cache_write(const int64_t* slot_mapping, int32_t num_tokens, const void* k,
+                       const void* v, int32_t src_dtype, const pkv_pool_desc* pool,
+                       void* k_pool, void* v_pool, const float* k_scale, const float* v_scale,
+                       void* stream) {
+  int rc = check_write(num_tokens, k, v, src_dtype, pool, k_pool, v_pool, k_scale, v_scale);
+  if (rc != PKV_OK || num_tokens == 0) return rc;
+  if (!slot_mapping) return PKV_EINVAL;
+  pkv::WriteLaunch p = write_launch(num_tokens, k, v, src_dtype, pool, k_pool, v_pool, k_scale,
+                                    v_scale);
+  p.slot_mapping = slot_mapping;
+  rc = pkv::launch_kv_cache_write(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_kv_cache_append(const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        const int32_t* seq_idx, const int32_t* positions, int32_t num_tokens,
+                        const void* k, const void* v, int32_t src_dtype,
+                        const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                        const float* k_scale, const float* v_scale, int64_t* slot_mapping_out,
+                        void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return PKV_EINVAL;
+  int rc = check_write(num_tokens, k, v, src_dtype, pool, k_pool, v_pool, k_scale, v_scale);
+  if (rc != PKV_OK || num_tokens == 0) return rc;
+  if (!seq_idx || !positions) return PKV_EINVAL;
+  if (num_seqs > 0 && max_blocks_per_seq > 0 && !block_table) return PKV_EINVAL;
+  pkv::WriteLaunch p = write_launch(num_tokens, k, v, src_dtype, pool, k_pool, v_pool, k_scale,
+                                    v_scale);
+  p.slot_mapping = nullptr;
+  const bool table = num_seqs > 0 && max_blocks_per_seq > 0;
+  p.block_table = table ? block_table : nullptr;
+  p.num_seqs = table ? num_seqs : 0;  // no table: every token is padding
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.seq_idx = seq_idx;
+  p.positions = positions;
+  p.slot_out = slot_mapping_out;
   rc = pkv::launch_kv_cache_write(p, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }

@@ -7,7 +7,8 @@
 // carry fp32 scales).  "KV Cache: capacity, layout, lifecycle", "Page-table
 // addressing": the cases where the reference raises become padding (-1) here.
 //
-// The scatter works in 16-byte source pieces: one thread moves one piece of
+// The fused append computes each token's slot in the scatter itself (one launch
+// for both steps).  The scatter works in 16-byte source pieces: one thread moves one piece of
 // one (token, kv head) row.  In the K pool ([block][head][D/X][B][X]) the piece
 // lands as one 16-byte store; in the V pool ([block][head][D][B], tokens
 // contiguous per dim) its elements go to D-strided slots, one store each.  Bit
@@ -21,29 +22,57 @@ namespace pkv {
 
 constexpr int kWriteThreads = 256;
 
+// slot of token i: table[s][pos / B] * B + pos mod B, or -1 (padding) wherever
+// the host reference raises (sequence out of range, negative position, logical
+// block past the table, negative table entry)
+__device__ __forceinline__ long long token_slot(const int32_t* __restrict__ block_table,
+                                                int num_seqs, int W,
+                                                const int32_t* __restrict__ seq_idx,
+                                                const int32_t* __restrict__ positions,
+                                                long long i, int B) {
+  const int s = seq_idx[i];
+  const int pos = positions[i];
+  if (s < 0 || s >= num_seqs || pos < 0) return -1;
+  const int j = pos / B;
+  if (j >= W) return -1;
+  const int phys = block_table[(size_t)s * W + j];
+  return phys >= 0 ? (long long)phys * B + (pos - j * B) : -1;
+}
+
 __global__ __launch_bounds__(kWriteThreads) void slot_mapping_kernel(
     const int32_t* __restrict__ block_table, int num_seqs, int W,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ positions, int num_tokens,
     int B, int64_t* __restrict__ slot_mapping) {
   const int i = blockIdx.x * kWriteThreads + threadIdx.x;
   if (i >= num_tokens) return;
-  const int s = seq_idx[i];
-  const int pos = positions[i];
-  long long slot = -1;
-  if (s >= 0 && s < num_seqs && pos >= 0) {
-    const int j = pos / B;
-    if (j < W) {
-      const int phys = block_table[(size_t)s * W + j];
-      if (phys >= 0) slot = (long long)phys * B + (pos - j * B);
-    }
-  }
-  slot_mapping[i] = slot;
+  slot_mapping[i] = token_slot(block_table, num_seqs, W, seq_idx, positions, i, B);
+}
+
+// Where the write kernels take each token's slot: a given slot mapping, or (the
+// fused append) computed from the block table, optionally written out too by the
+// thread that moves the token's first K piece.
+struct SlotSource {
+  const int64_t* slot_mapping;  // non-null: given slots
+  const int32_t* block_table;
+  const int32_t* seq_idx;
+  const int32_t* positions;
+  int num_seqs, W;
+  int64_t* slot_out;            // optional, computed slots only
+};
+
+__device__ __forceinline__ long long source_slot(const SlotSource& ss, long long i, int c, int h,
+                                                 int B) {
+  if (ss.slot_mapping) return ss.slot_mapping[i];
+  const long long slot =
+      token_slot(ss.block_table, ss.num_seqs, ss.W, ss.seq_idx, ss.positions, i, B);
+  if (ss.slot_out && c == 0 && h == 0 && blockIdx.y == 0) ss.slot_out[i] = slot;
+  return slot;
 }
 
 // Bit copy of one 16-byte piece (non-fp8 pools); ES = bytes per element.
 template <int ES>
 __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
-    const int64_t* __restrict__ slot_mapping, int num_tokens, const uint8_t* __restrict__ k,
+    const SlotSource ss, int num_tokens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     int num_blocks, int B, int Hkv, int D) {
   const int NC = D * ES / 16;  // pieces per row
@@ -55,7 +84,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
   const long long i = idx % num_tokens;
   const int c = (int)((idx / num_tokens) % NC);
   const int h = (int)(idx / ((long long)num_tokens * NC));
-  const long long slot = slot_mapping[i];
+  const long long slot = source_slot(ss, i, c, h, B);
   if (slot < 0 || slot >= (long long)num_blocks * B) return;
   const long long blk = slot / B, off = slot % B;
   const size_t src = ((size_t)i * Hkv + h) * NC + c;  // in 16-byte pieces
@@ -82,7 +111,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
 // fp8 pools: 16 source elements of SRC type -> one 16-byte piece of E4M3 codes.
 template <int SRC>
 __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
-    const int64_t* __restrict__ slot_mapping, int num_tokens, const uint8_t* __restrict__ k,
+    const SlotSource ss, int num_tokens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale, int num_blocks, int B,
     int Hkv, int D) {
@@ -94,7 +123,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
   const long long i = idx % num_tokens;  // token fastest, as above
   const int c = (int)((idx / num_tokens) % NC);
   const int h = (int)(idx / ((long long)num_tokens * NC));
-  const long long slot = slot_mapping[i];
+  const long long slot = source_slot(ss, i, c, h, B);
   if (slot < 0 || slot >= (long long)num_blocks * B) return;
   const long long blk = slot / B, off = slot % B;
   const bool isv = blockIdx.y != 0;
@@ -139,30 +168,38 @@ int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
   const long long blocks = (pieces + kWriteThreads - 1) / kWriteThreads;
   if (blocks > 0x7fffffffLL) return -3;
   dim3 grid((unsigned)blocks, 2);
+  SlotSource ss;
+  ss.slot_mapping = p.slot_mapping;
+  ss.block_table = p.block_table;
+  ss.seq_idx = p.seq_idx;
+  ss.positions = p.positions;
+  ss.num_seqs = p.num_seqs;
+  ss.W = p.max_blocks_per_seq;
+  ss.slot_out = p.slot_out;
   const uint8_t* k = (const uint8_t*)p.k;
   const uint8_t* v = (const uint8_t*)p.v;
   uint8_t* kp = (uint8_t*)p.k_pool;
   uint8_t* vp = (uint8_t*)p.v_pool;
   if (p.kv_dtype == DT_F32)
-    hipLaunchKernelGGL(kv_write_copy_kernel<4>, grid, dim3(kWriteThreads), 0, st, p.slot_mapping,
+    hipLaunchKernelGGL(kv_write_copy_kernel<4>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
                        p.head_dim);
   else if (p.kv_dtype == DT_F16 || p.kv_dtype == DT_BF16)
-    hipLaunchKernelGGL(kv_write_copy_kernel<2>, grid, dim3(kWriteThreads), 0, st, p.slot_mapping,
+    hipLaunchKernelGGL(kv_write_copy_kernel<2>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
                        p.head_dim);
   else if (p.src_dtype == DT_BF16)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_BF16>, grid, dim3(kWriteThreads), 0, st,
-                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
-                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_BF16>, grid, dim3(kWriteThreads), 0, st, ss,
+                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
+                       p.block_size, p.num_kv_heads, p.head_dim);
   else if (p.src_dtype == DT_F16)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F16>, grid, dim3(kWriteThreads), 0, st,
-                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
-                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F16>, grid, dim3(kWriteThreads), 0, st, ss,
+                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
+                       p.block_size, p.num_kv_heads, p.head_dim);
   else if (p.src_dtype == DT_F32)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F32>, grid, dim3(kWriteThreads), 0, st,
-                       p.slot_mapping, p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale,
-                       p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim);
+    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F32>, grid, dim3(kWriteThreads), 0, st, ss,
+                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
+                       p.block_size, p.num_kv_heads, p.head_dim);
   else
     return -3;
   return hipGetLastError() == hipSuccess ? 0 : -5;

@@ -57,7 +57,12 @@ int launch_slot_mapping(const int32_t* block_table, int num_seqs, int max_blocks
                         int block_size, int64_t* slot_mapping, hipStream_t stream);
 
 struct WriteLaunch {
-  const int64_t* slot_mapping;
+  const int64_t* slot_mapping;  // given slots, or null: computed from the fields below
+  const int32_t* block_table;
+  const int32_t* seq_idx;
+  const int32_t* positions;
+  int num_seqs, max_blocks_per_seq;
+  int64_t* slot_out;            // optional copy of the computed slots
   int num_tokens;
   const void* k;
   const void* v;

@@ -79,32 +79,75 @@ __device__ __forceinline__ int pick4(const int (&v)[4], int i) {
   return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
 }
 
+// Pieces of a chunk and who loads them.  Every wavefront loads from one 16-token
+// tile per piece index, so the page is wave-uniform: its base address is scalar
+// and each lane adds an offset that is the same for every chunk (recomputed only
+// in a chunk that runs past the context, whose tokens are clamped).
+//   K piece i of thread (w, l): token 16 w + l % 16, dims [c X, c X + X) with
+//     c = l / 16 + 4 i (tile w).
+//   V piece i: vp = 256 i + 64 w + l covers tokens [TP p, TP p + TP) of dim
+//     vp % D, p = vp / D (tile TP p / 16, the same for the whole wavefront as
+//     64 divides D).
+template <int KVT, int D>
+struct PieceMap {
+  using C = PCfg<KVT, D>;
+  int k_tok;               // chunk-relative token of this lane's K pieces
+  int k_c[C::KP];          // K piece index c
+  int v_p[C::VP], v_d[C::VP];
+  uint32_t k_off[C::KP];   // byte offset within the page, full chunks
+  uint32_t v_off[C::VP];
+
+  __device__ __forceinline__ PieceMap(int wave, int lane, int blog2) {
+    const int B = 1 << blog2;
+    k_tok = 16 * wave + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < C::KP; ++i) {
+      k_c[i] = (lane >> 4) + 4 * i;
+      k_off[i] = (uint32_t)((k_c[i] * B + (k_tok & (B - 1))) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VP; ++i) {
+      const int vp = kPfThreads * i + 64 * wave + lane;
+      v_p[i] = vp / D;
+      v_d[i] = vp % D;
+      v_off[i] = (uint32_t)((v_d[i] * B + ((v_p[i] * C::TP) & (B - 1))) * C::EB);
+    }
+  }
+};
+
 // Issue the pool loads of the chunk at `base` (tokens clamped below `end`).
-// K piece kp: dims [c X, c X + X) of token kp % 64, c = kp / 64.
-// V piece vp: tokens [TP p, TP p + TP) of dim vp % D, p = vp / D.
 template <int KVT, int D>
 __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* __restrict__ k_pool,
                                            const uint8_t* __restrict__ v_pool, const int (&pg)[4],
-                                           int base, int end, int kvh, const PrefillScalars& ps) {
+                                           int base, int end, int kvh, int wave,
+                                           const PieceMap<KVT, D>& pm, const PrefillScalars& ps) {
   using C = PCfg<KVT, D>;
   const int B = 1 << ps.blog2;
-  const int tid = threadIdx.x;
+  const bool full = base + 64 <= end;  // uniform
+  {
+    const size_t page = (size_t)pick4(pg, wave) * ps.Hkv + kvh;
+    const uint8_t* pb = k_pool + page * (C::NC * B * 16);
 #pragma unroll
-  for (int i = 0; i < C::KP; ++i) {
-    const int kp = tid + kPfThreads * i;
-    const int c = kp >> 6, tok = kp & 63;
-    const int t = min(base + tok, end - 1);
-    const size_t page = (size_t)pick4(pg, tok >> 4) * ps.Hkv + kvh;
-    r.k[i] = reinterpret_cast<const u32x4*>(k_pool)[(page * C::NC + c) * B + (t & (B - 1))];
+    for (int i = 0; i < C::KP; ++i) {
+      uint32_t off = pm.k_off[i];
+      if (!full) {
+        const int t = min(base + pm.k_tok, end - 1);
+        off = (uint32_t)((pm.k_c[i] * B + (t & (B - 1))) * 16);
+      }
+      r.k[i] = *reinterpret_cast<const u32x4*>(pb + off);
+    }
   }
 #pragma unroll
   for (int i = 0; i < C::VP; ++i) {
-    const int vp = tid + kPfThreads * i;
-    const int p = vp / D, d = vp % D;
-    const int t0 = p * C::TP;  // first token of the piece within the chunk
+    const int t0 = uniform(pm.v_p[i]) * C::TP;  // first token of the piece within the chunk
     const size_t page = (size_t)pick4(pg, t0 >> 4) * ps.Hkv + kvh;
-    const int off = (min(base + t0, end - 1) & (B - 1)) & ~(C::TP - 1);
-    r.v[i] = *reinterpret_cast<const u32x4*>(v_pool + ((page * D + d) * B + off) * C::EB);
+    const uint8_t* pb = v_pool + page * (D * B * C::EB);
+    uint32_t off = pm.v_off[i];
+    if (!full) {
+      const int t = (min(base + t0, end - 1) & (B - 1)) & ~(C::TP - 1);
+      off = (uint32_t)((pm.v_d[i] * B + t) * C::EB);
+    }
+    r.v[i] = *reinterpret_cast<const u32x4*>(pb + off);
   }
 }
 
@@ -112,13 +155,12 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
 // V tokens at or past `end` become zero (their slots may hold anything).
 template <int KVT, int D>
 __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
-                                            uint8_t* vbuf, int base, int end) {
+                                            uint8_t* vbuf, int base, int end,
+                                            const PieceMap<KVT, D>& pm) {
   using C = PCfg<KVT, D>;
-  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < C::KP; ++i) {
-    const int kp = tid + kPfThreads * i;
-    const int c = kp >> 6, tok = kp & 63;
+    const int c = pm.k_c[i], tok = pm.k_tok;
     uint8_t* row = kbuf + tok * C::KROW;
     if constexpr (KVT == DT_FP8) {
       const u32x4 w = r.k[i];
@@ -132,8 +174,7 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
   }
 #pragma unroll
   for (int i = 0; i < C::VP; ++i) {
-    const int vp = tid + kPfThreads * i;
-    const int p = vp / D, d = vp % D;
+    const int p = pm.v_p[i], d = pm.v_d[i];
     const int t0 = p * C::TP;
     const int lim = end - (base + t0);  // tokens of the piece below end
     uint8_t* row = vbuf + d * C::VROW;
@@ -303,17 +344,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     };
     fill_window(0);
     __syncthreads();
+    const PieceMap<KVT, D> pm(wave, lane, ps.blog2);
     Raw<C> ra, rb;
     {
       int pg[4];
       win_pages(0, 0, pg);
-      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, 0, kend, kvh, ps);
+      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, 0, kend, kvh, wave, pm, ps);
       if (nch > 1) {
         win_pages(1, 0, pg);
-        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, ps);
+        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, wave, pm, ps);
       }
     }
-    chunk_stage<KVT, D>(ra, lds[0], lds[0] + C::KBUF, 0, kend);
+    chunk_stage<KVT, D>(ra, lds[0], lds[0] + C::KBUF, 0, kend, pm);
     __syncthreads();
 
     // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
@@ -324,7 +366,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       if (j + 2 < nch) {
         int pg[4];
         win_pages(j + 2, wk, pg);
-        chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg, base + 128, kend, kvh, ps);
+        chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg, base + 128, kend, kvh, wave, pm, ps);
       }
       float zs[4], vs[4];
       {
@@ -440,7 +482,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       }
       issue_point();
       // ---- stage chunk j+1 into the other buffer; advance the page window
-      if (j + 1 < nch) chunk_stage<KVT, D>(nxt1, lds[(j + 1) & 1], lds[(j + 1) & 1] + C::KBUF, base + 64, kend);
+      if (j + 1 < nch)
+        chunk_stage<KVT, D>(nxt1, lds[(j + 1) & 1], lds[(j + 1) & 1] + C::KBUF, base + 64, kend, pm);
       if ((j + 1) % kWinChunks == 0 && j + 1 < nch) {  // the next step starts a new window
         __syncthreads();  // every wave has read the old window
         fill_window((j + 1) / kWinChunks);

@@ -100,3 +100,51 @@ def test_write_zero_tokens_is_a_no_op():
                            kp, vp)
     torch.cuda.synchronize()
     assert (kp == 0x5A).all() and (vp == 0x5A).all()
+
+
+@pytest.mark.parametrize("kv,src,D,B,H", [("bf16", "bf16", 128, 16, 8), ("fp8", "bf16", 128, 16, 8),
+                                          ("f16", "f16", 64, 32, 2), ("fp8", "f32", 64, 64, 3)])
+def test_kv_cache_append_bit_exact(kv, src, D, B, H):
+    # the fused append against the oracle's slot mapping followed by its scatter; the
+    # table is a permutation of the pool with holes, the tokens distinct (sequence,
+    # position) pairs plus padding cases (bad sequence, negative position, position past
+    # the table, hole in the table)
+    import torch
+    pkv = _pkv()
+    rng = np.random.default_rng([D, B, H, len(kv), 77])
+    S, W = 9, 7
+    NB = S * W + 5
+    bt = rng.permutation(NB)[:S * W].reshape(S, W).astype(np.int32)
+    bt[rng.random((S, W)) < 0.1] = -1
+    pairs = rng.permutation(S * W * B)[:400]
+    seq = (pairs // (W * B)).astype(np.int32)
+    pos = (pairs % (W * B)).astype(np.int32)
+    seq[:4] = [-1, S, 0, 1]
+    pos[:4] = [3, 3, -2, W * B + 5]
+    T = len(seq)
+    want_slots = oracle.slot_mapping(bt, seq, pos, B)
+    assert (want_slots < 0).sum() >= 4 and (want_slots >= 0).sum() > T // 2
+    x = rng.standard_normal((2, T, H, D)).astype(np.float32)
+    k = to_storage(x[0], src)
+    v = to_storage(x[1], src)
+    pool = oracle.Pool(NB, B, H, D, kv)
+    pool.k.view(np.uint8)[...] = 0xFF
+    pool.v.view(np.uint8)[...] = 0xFF
+    ks = vs = None
+    if kv == "fp8":
+        pool.k_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
+        pool.v_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
+        ks = torch.from_numpy(pool.k_scale).cuda()
+        vs = torch.from_numpy(pool.v_scale).cuda()
+    oracle.kv_cache_write(pool, want_slots, k, v, src)
+    desc = pkv.pool_desc(NB, B, H, D, kv)
+    kp, vp = pkv.alloc_pool(desc, fill_byte=0xFF)
+    slots_out = torch.full((T,), -7, dtype=torch.int64, device="cuda")
+    pkv.pkv_kv_cache_append(torch.from_numpy(bt).cuda(), torch.from_numpy(seq).cuda(),
+                            torch.from_numpy(pos).cuda(), torch_bits(k, src), torch_bits(v, src),
+                            desc, kp, vp, ks, vs, src_dtype=src, slot_mapping_out=slots_out)
+    assert np.array_equal(slots_out.cpu().numpy(), want_slots)
+    gk = logical_k(kp.cpu().numpy(), NB, B, H, D, kv)
+    gv = logical_v(vp.cpu().numpy(), NB, B, H, D, kv)
+    assert np.array_equal(gk.view(np.uint8), pool.k.view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), pool.v.view(np.uint8))

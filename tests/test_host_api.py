@@ -165,6 +165,17 @@ def test_write_and_prefill_argument_errors_caught_on_host():
     assert L.pkv_kv_cache_write(None, 0, None, None, 2, ctypes.byref(desc), None, None, None,
                                 None, None) == 0
     assert L.pkv_slot_mapping(None, 1, 1, None, None, 3, 0, None, None) == -1
+    # the fused append: the write's checks, plus its own table arguments
+    assert L.pkv_kv_cache_append(16, 1, 1, 16, 16, 4, 16, 16, 0, ctypes.byref(desc), 16, 16,
+                                 None, None, None, None) == -1  # dtype mismatch
+    assert L.pkv_kv_cache_append(16, 1, 1, None, 16, 4, 16, 16, 2, ctypes.byref(desc), 16, 16,
+                                 None, None, None, None) == -1  # no seq_idx
+    assert L.pkv_kv_cache_append(None, 1, 1, 16, 16, 4, 16, 16, 2, ctypes.byref(desc), 16, 16,
+                                 None, None, None, None) == -1  # no table
+    assert L.pkv_kv_cache_append(16, -1, 1, 16, 16, 4, 16, 16, 2, ctypes.byref(desc), 16, 16,
+                                 None, None, None, None) == -1
+    assert L.pkv_kv_cache_append(None, 0, 0, None, None, 0, None, None, 2, ctypes.byref(desc),
+                                 None, None, None, None, None, None) == 0
     assert L.pkv_paged_prefill(None, 0, None, 1, 1, 1, 32, ctypes.byref(desc), None, None, None,
                                None, None, 8, None, 64, 0.1, 1, None, None) == -3  # f32 q
     assert L.pkv_paged_prefill(None, 2, None, 1, 1, 1, 30, ctypes.byref(desc), None, None, None,
