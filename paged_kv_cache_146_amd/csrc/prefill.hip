@@ -8,7 +8,8 @@
 // Work cut: one workgroup (4 waves) per (query block, kv head, sequence).  A
 // "row" is a (query token, query head) pair; a 16-row tile holds 16/G tokens x
 // the G heads of the kv head, so every K/V tile is reused by all G heads.  Each
-// wave owns four row tiles, the workgroup 256/G tokens.
+// wave owns two row tiles, the workgroup 128/G tokens.  The query blocks of one
+// (sequence, kv head) pair run on one XCD, so their shared K/V hits in its L2.
 //
 // Per 64-key chunk the workgroup stages K and V once into LDS, widened to 16
 // bits (fp8 E4M3 -> bf16 for K, -> f16 for V; both exact), double-buffered,
@@ -40,8 +41,15 @@ struct PrefillScalars {
   int S, Hq, Hkv, G;
   int blog2, num_blocks, ctx_cap;
   int causal;
+  int nqb;         // query blocks per sequence (grid)
   float scale_log2;
 };
+
+// Workgroups are dealt to the XCDs round robin by id (id mod 8), and each XCD has
+// its own L2.  The query blocks of one (sequence, kv head) pair read the same K/V
+// chunks, so they are given ids of one residue mod 8: pair p lives on XCD p mod 8
+// as that XCD's (p / 8)-th pair, and its query blocks take consecutive slots there.
+constexpr int kXcds = 8;
 
 constexpr int kPfThreads = 256;
 
@@ -216,6 +224,9 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
 // With the fp8 V scale folded into P (f16), scales up to 65504 / 2^kLazyMax keep P finite.
 constexpr float kLazyMax = 4.0f;
 
+// LDS operand reads in flight ahead of the MFMA that uses them
+constexpr int kPrefetch = 4;
+
 // per-row online-softmax state of one row tile: lane (n, g) holds column n
 template <int D>
 struct RowState {
@@ -234,13 +245,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
   using C = PCfg<KVT, D>;
   constexpr bool kFp8 = (KVT == DT_FP8);
   constexpr int NR = C::NR;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][C::KBUF + C::VBUF];
+  // two chunk buffers as separate arrays, so that the staging writes into one are
+  // provably independent of the operand reads from the other
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::KBUF + C::VBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::KBUF + C::VBUF];
   constexpr int kWinChunks = 32;
   constexpr int kWinBlocks = (kWinChunks + 2) * 4;  // chunks of 64 tokens, blocks of >= 16
   __shared__ int w_blk[kWinBlocks];
   __shared__ float w_ks[kWinBlocks], w_vs[kWinBlocks];
 
-  const int qb = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int xcd = blockIdx.x % kXcds, xslot = blockIdx.x / kXcds;
+  const int pair = (xslot / ps.nqb) * kXcds + xcd, qb = xslot % ps.nqb;
+  if (pair >= ps.S * ps.Hkv) return;  // the grid is rounded up to whole XCD rows
+  const int s = pair / ps.Hkv, kvh = pair - s * ps.Hkv;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int G = ps.G, tpr = 16 / G;           // tokens per row tile
@@ -355,12 +372,12 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, wave, pm, ps);
       }
     }
-    chunk_stage<KVT, D>(ra, lds[0], lds[0] + C::KBUF, 0, kend, pm);
+    chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, 0, kend, pm);
     __syncthreads();
 
     // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
     // are staged after chunk j is computed
-    auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1) {
+    auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1, uint8_t* cur_buf, uint8_t* nxt_buf) {
       const int base = 64 * j;
       const int wk = j / kWinChunks;
       if (j + 2 < nch) {
@@ -383,24 +400,42 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
-      const uint8_t* kbuf = lds[j & 1];
-      const uint8_t* vbuf = lds[j & 1] + C::KBUF;
+      const uint8_t* kbuf = cur_buf;
+      const uint8_t* vbuf = cur_buf + C::KBUF;
       issue_point();
       if (base < wave_max_lim) {  // some row of the wave sees a key of this chunk
-      // ---- S^T for every row tile (a tile past its rows' keys is masked below)
+      // ---- S^T for every row tile (a tile past its rows' keys is masked below).
+      // The matrix phases run at raised wave priority: of the two waves on a SIMD,
+      // the one with MFMAs ready issues first while the other works on its softmax.
+      __builtin_amdgcn_s_setprio(2);
       f32x4 S[NR][4];
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      // K operands (i = T * NKS + ks) are read kPrefetch ahead of their MFMAs, so the
+      // LDS latency hides behind the products of the operands before them
+      {
+        constexpr int NI = 4 * C::NKS;
+        auto rd = [&](int i) {
+          return *reinterpret_cast<const u32x4*>(kbuf + k_off[i / C::NKS] + k_unit[i % C::NKS]);
+        };
+        u32x4 kop[kPrefetch + 1];
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const uint8_t* krow = kbuf + k_off[T];
+        for (int i = 0; i < kPrefetch; ++i) kop[i] = rd(i);
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + k_unit[ks]);
+        for (int i = 0; i < NI; ++i) {
+          if (i + kPrefetch < NI) kop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
+          const int T = i / C::NKS, ks = i % C::NKS;
 #pragma unroll
           for (int rt = 0; rt < NR; ++rt)
-            S[rt][T] = mma16<DT_BF16>(a, qop[rt][ks], ks == 0 ? zero : S[rt][T]);
+            S[rt][T] = mma16<DT_BF16>(kop[i % (kPrefetch + 1)], qop[rt][ks], ks == 0 ? zero : S[rt][T]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, NR, 1);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- online softmax per row tile; P operands.  Keys at or past a row's bound
       // exist only in chunks that reach the wave's smallest bound.
       const bool need_mask = base + 64 > wave_min_lim;
@@ -465,25 +500,46 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
         }
       }
-      // ---- O^T += V^T . P^T
+      // ---- stage chunk j+1 into the other buffer (free since the last barrier)
+      // while the matrix cores run O^T += V^T . P^T: the conversions and LDS writes
+      // fill the issue slots between the MFMAs
+      if (j + 1 < nch) chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm);
+      __builtin_amdgcn_s_setprio(2);
+      {
+        // V operands (i = 2 dt + s2), read kPrefetch ahead as the K operands above
+        constexpr int NI = 2 * C::NDT;
+        constexpr int MPI = NR * (C::SPLIT ? 2 : 1);  // MFMAs per operand
+        auto rd = [&](int i) {
+          return *reinterpret_cast<const u32x4*>(vbuf + v_off + (i / 2) * 16 * C::VROW +
+                                                 v_unit[i % 2]);
+        };
+        u32x4 vop[kPrefetch + 1];
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const uint8_t* vrow = vbuf + v_off + dt * 16 * C::VROW;
+        for (int i = 0; i < kPrefetch; ++i) vop[i] = rd(i);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + v_unit[s2]);
+        for (int i = 0; i < NI; ++i) {
+          if (i + kPrefetch < NI) vop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
+          const int dt = i / 2, s2 = i % 2;
+          const u32x4 a = vop[i % (kPrefetch + 1)];
 #pragma unroll
           for (int rt = 0; rt < NR; ++rt) {
             st[rt].acc[dt] = mma16<C::PT>(a, phi[rt][s2], st[rt].acc[dt]);
             if constexpr (C::SPLIT) st[rt].acc[dt] = mma16<C::PT>(a, plo[rt][s2], st[rt].acc[dt]);
           }
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+          __builtin_amdgcn_sched_group_barrier(0x008, MPI, 2);
+        }
       }
+      __builtin_amdgcn_s_setprio(0);
+      } else if (j + 1 < nch) {  // no key of this chunk for the wave: only the staging
+        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm);
       }
       issue_point();
-      // ---- stage chunk j+1 into the other buffer; advance the page window
-      if (j + 1 < nch)
-        chunk_stage<KVT, D>(nxt1, lds[(j + 1) & 1], lds[(j + 1) & 1] + C::KBUF, base + 64, kend, pm);
+      // ---- advance the page window
       if ((j + 1) % kWinChunks == 0 && j + 1 < nch) {  // the next step starts a new window
         __syncthreads();  // every wave has read the old window
         fill_window((j + 1) / kWinChunks);
@@ -492,8 +548,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     };
     // chunk j's raw pieces live in ra (j even) / rb (j odd) until staged
     for (int j = 0; j < nch; j += 2) {
-      step(j, ra, rb);
-      if (j + 1 < nch) step(j + 1, rb, ra);
+      step(j, ra, rb, lds0, lds1);
+      if (j + 1 < nch) step(j + 1, rb, ra, lds1, lds0);
     }
   }
 
@@ -520,11 +576,17 @@ int log2_exact(int x) {
 template <int KVT, int D>
 int launch_pf(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) {
   const int tpg = 4 * PCfg<KVT, D>::NR * (16 / ps.G);
-  dim3 grid((p.max_q_len + tpg - 1) / tpg, p.num_kv_heads, p.num_seqs);
+  PrefillScalars q = ps;
+  q.nqb = (p.max_q_len + tpg - 1) / tpg;
+  const long long pairs = (long long)p.num_seqs * p.num_kv_heads;
+  const long long per_xcd = (pairs + kXcds - 1) / kXcds;
+  const long long blocks = per_xcd * kXcds * q.nqb;
+  if (blocks > 0x7fffffffLL) return -3;
+  dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL((paged_prefill_kernel<KVT, D>), grid, dim3(kPfThreads), 0, st,
                      (const uint8_t*)p.q, p.cu_seqlens_q, (const uint8_t*)p.k_pool,
                      (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
-                     p.context_lens, (uint8_t*)p.out, ps);
+                     p.context_lens, (uint8_t*)p.out, q);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
