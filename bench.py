@@ -311,8 +311,8 @@ def prefill_main(a):
                               out=out, q_dtype="bf16")
 
     def step():
-        pkv.pkv_slot_mapping(bt, seq_new, pos_new, wl.block_size, out=slots)
-        pkv.pkv_kv_cache_write(slots, k_new, v_new, desc, k_pool, v_pool, ks, vs, src_dtype="bf16")
+        pkv.pkv_kv_cache_append(bt, seq_new, pos_new, k_new, v_new, desc, k_pool, v_pool, ks, vs,
+                                src_dtype="bf16", slot_mapping_out=slots)
         prefill()
 
     def timed(fn, n):
@@ -363,7 +363,7 @@ def prefill_main(a):
         "dtype": "bf16 (fp8 e4m3 KV)", "data": "synthetic",
         "config": {"workload": "fp8 KV chunked prefill: 16 seqs x (4096 cached + 512 new), "
                                "H_q 32, H_kv 8, D 128, B 16, causal, seed 5",
-                   "step": "slot_mapping + kv_cache_write (8192 tokens, fp8) + paged_prefill",
+                   "step": "kv_cache_append (8192 tokens, fp8, one launch) + paged_prefill",
                    "caches": "flushed before every step"},
         "flops_per_step": flops,
         "query_tokens_per_s": round(8192 / (step_us * 1e-6), 1),
