@@ -328,7 +328,7 @@ def prefill_main(a):
         return np.array([x.elapsed_time(y) for x, y in zip(starts, ends)])
 
     steps = min(a.steps, 20)
-    for _ in range(min(a.warmup, 3)):
+    for _ in range(min(a.warmup, 10)):
         flush.sum()
         step()
     step_ms = timed(step, steps)
