@@ -10,7 +10,9 @@
  *        after consumers finish; §8.1 FP8 KV with FP32 scales.
  *   [P2] "KV Cache: capacity, layout, lifecycle" (wineandchord)
  *        "Page-table addressing" (physical_slot and its errors), "Physical
- *        layout", "Correctness contract" (reject a mismatched descriptor).
+ *        layout", "Correctness contract" (reject a mismatched descriptor),
+ *        "Lifecycle and ownership" and "Reference counting and tail-block
+ *        COW" (the block allocator).
  *
  * General conventions
  *   - Every pointer named *device* is device memory the CALLER owns.  The
@@ -29,7 +31,8 @@
  *     outside the caller's buffers.
  *   - All entry points are thread-safe.  The only process-wide state is a
  *     per-device cache of device properties and an atomic call counter that
- *     tags balanced-mode calls.
+ *     tags balanced-mode calls.  The block allocator (pkv_alloc_*) is host
+ *     bookkeeping with one lock per allocator.
  *
  * Physical pool layout (owned by this library; one pool for K, one for V, per
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
@@ -71,7 +74,8 @@ enum {
   PKV_ERANGE = -2,       /* position / block id outside the table or the pool */
   PKV_EUNSUPPORTED = -3, /* valid request with no kernel instantiation here */
   PKV_EWORKSPACE = -4,   /* workspace too small */
-  PKV_EHIP = -5          /* HIP runtime reported an error while launching */
+  PKV_EHIP = -5,         /* HIP runtime reported an error while launching */
+  PKV_ENOBLOCKS = -6     /* block allocator: no free block (nothing was changed) */
 };
 
 /* Descriptor of one layer's paged pool ([P1 §3.1]; [P2 "Correctness contract"]:
@@ -269,6 +273,77 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
                       int32_t max_blocks_per_seq, const int32_t* context_lens,
                       int32_t max_context_len, float scale, int32_t causal, void* out,
                       void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Block allocator (host) and block copies.  [P2] "Lifecycle and ownership",
+ * "Reference counting and tail-block COW"; [P1] §5 (free queue, reference
+ * counts, fork of shared prefixes).
+ *
+ * A physical block is free, exclusive (refcount 1) or shared read-only
+ * (refcount > 1); a block's refcount is the number of live sequences whose
+ * table holds it.  The allocator keeps each sequence's block table and its
+ * committed length.  Free blocks form a stack: the block pushed last is handed
+ * out first.
+ *   fork: the child starts with a copy of the parent's table and length; every
+ *     block gains a reference.  Full blocks stay shared: nobody writes them.
+ *   append: claims the slot of the sequence's next token and commits it (table
+ *     and length change together).  A token that opens a block takes a fresh
+ *     block.  A token that lands in a partly filled tail shared with another
+ *     sequence first moves this sequence onto a fresh block (copy on write):
+ *     the old block loses one reference and the call reports the pair
+ *     (cow_src, cow_dst), whose committed K/V and scales the caller copies with
+ *     pkv_copy_blocks on the stream BEFORE any kernel reads the new table or
+ *     writes the slot.  No copy: both are -1.
+ *   free: releases each block of the sequence once.  A block whose refcount
+ *     drops to 0 goes back on the free stack right away, or, given an event
+ *     recorded after the last GPU work that touches the sequence, only once
+ *     that event has completed (checked whenever a fresh block is needed and by
+ *     pkv_alloc_free_blocks), so queued GPU work never sees a block reused.
+ *     Released blocks are pushed in reverse table order: the sequence's first
+ *     block is handed out next.
+ * Device block tables are the caller's to upload (pkv_alloc_block_table
+ * exports one sequence's row).  Errors: PKV_EINVAL (bad argument, unknown or
+ * already released sequence), PKV_ERANGE (capacity too small, block id out of
+ * range), PKV_ENOBLOCKS (no free block; the allocator is unchanged).
+ * -------------------------------------------------------------------------*/
+typedef struct pkv_alloc pkv_alloc;
+
+/* free_order: HOST int32 [num_free], the initial free stack bottom to top (its
+ * last entry is handed out first); ids must be distinct and in [0, num_blocks);
+ * blocks left out are never handed out (a padding block, say).  NULL: every
+ * block, handed out as 0, 1, 2, ...  *out receives the allocator. */
+int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                     int32_t num_free, pkv_alloc** out);
+void pkv_alloc_destroy(pkv_alloc* alloc);
+/* a new empty sequence; *seq receives its id */
+int pkv_alloc_add_seq(pkv_alloc* alloc, int32_t* seq);
+int pkv_alloc_fork(pkv_alloc* alloc, int32_t parent, int32_t* child);
+/* *slot = table[length / B] * B + length % B for the token being committed */
+int pkv_alloc_append(pkv_alloc* alloc, int32_t seq, int64_t* slot, int32_t* cow_src,
+                     int32_t* cow_dst);
+/* event: a hipEvent_t recorded after the sequence's last GPU use, or NULL; it
+ * must stay valid until its blocks are back on the free stack (or the allocator
+ * is destroyed) */
+int pkv_alloc_free_seq(pkv_alloc* alloc, int32_t seq, void* event);
+/* table: HOST int32 [capacity] (may be NULL to query the sizes only) */
+int pkv_alloc_block_table(pkv_alloc* alloc, int32_t seq, int32_t* table, int32_t capacity,
+                          int32_t* num_blocks, int64_t* length);
+int pkv_alloc_refcount(pkv_alloc* alloc, int32_t block, int32_t* refcount);
+/* the free stack bottom to top (after reclaiming blocks whose events completed) */
+int pkv_alloc_free_blocks(pkv_alloc* alloc, int32_t* free_order, int32_t capacity,
+                          int32_t* num_free);
+
+/* [P2] "Reference counting and tail-block COW": copy whole blocks.
+ *   pairs: device int32 [num_pairs][2] of (src, dst) block ids.  For each pair,
+ *   every byte of block src in both pools (all kv heads) and, for fp8 pools,
+ *   its scales k_scale[src][:], v_scale[src][:] are copied to dst.  Pairs with
+ *   an id outside [0, num_blocks), or src == dst, are skipped; destinations
+ *   must be distinct and must not be the source of another pair (else the
+ *   copies race).  k_scale, v_scale: device float [num_blocks][num_kv_heads],
+ *   fp8 pools only (else ignored).  Errors: PKV_EINVAL, PKV_EUNSUPPORTED,
+ *   PKV_EHIP. */
+int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc* pool,
+                    void* k_pool, void* v_pool, float* k_scale, float* v_scale, void* stream);
 
 #ifdef __cplusplus
 }

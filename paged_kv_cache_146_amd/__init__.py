@@ -24,12 +24,16 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_NAMES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
 ELEM_BYTES = {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}
 STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ERANGE", -3: "PKV_EUNSUPPORTED",
-          -4: "PKV_EWORKSPACE", -5: "PKV_EHIP"}
+          -4: "PKV_EWORKSPACE", -5: "PKV_EHIP", -6: "PKV_ENOBLOCKS"}
+PKV_ENOBLOCKS = -6
 
 EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_validate_block_table", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_kv_cache_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode", "pkv_split_kv_reduce",
-           "pkv_paged_prefill"]
+           "pkv_kv_cache_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
+           "pkv_split_kv_reduce", "pkv_paged_prefill", "pkv_alloc_create", "pkv_alloc_destroy",
+           "pkv_alloc_add_seq", "pkv_alloc_fork", "pkv_alloc_append", "pkv_alloc_free_seq",
+           "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
+           "pkv_copy_blocks"]
 
 
 class PagedKVError(RuntimeError):
@@ -84,6 +88,16 @@ def lib():
                                                            I32, P]),
                     "pkv_paged_prefill": (ctypes.c_int, [P, I32, P, I32, I32, I32, I32, P, P, P,
                                                          P, P, P, I32, P, I32, F, I32, P, P]),
+                    "pkv_alloc_create": (ctypes.c_int, [I32, I32, P, I32, P]),
+                    "pkv_alloc_destroy": (None, [P]),
+                    "pkv_alloc_add_seq": (ctypes.c_int, [P, P]),
+                    "pkv_alloc_fork": (ctypes.c_int, [P, I32, P]),
+                    "pkv_alloc_append": (ctypes.c_int, [P, I32, P, P, P]),
+                    "pkv_alloc_free_seq": (ctypes.c_int, [P, I32, P]),
+                    "pkv_alloc_block_table": (ctypes.c_int, [P, I32, P, I32, P, P]),
+                    "pkv_alloc_refcount": (ctypes.c_int, [P, I32, P]),
+                    "pkv_alloc_free_blocks": (ctypes.c_int, [P, P, I32, P]),
+                    "pkv_copy_blocks": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
                 }
                 for name, (res, args) in sigs.items():
                     fn = getattr(L, name)
@@ -240,6 +254,93 @@ def pkv_kv_cache_append(block_table, seq_idx, positions, k, v, desc: PoolDesc, k
                                      _stream(stream)),
            "pkv_kv_cache_append")
     return slot_mapping_out
+
+
+class BlockAllocator:
+    """Host block allocator (pkv_alloc_*): free stack, refcounts, fork, tail copy on
+    write, deferred release.  Argument marshalling only; the logic is in the library."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.block_size = int(block_size)
+        h = ctypes.c_void_p()
+        if free_order is None:
+            _check(lib().pkv_alloc_create(int(num_blocks), int(block_size), None, 0,
+                                          ctypes.byref(h)), "pkv_alloc_create")
+        else:
+            arr = (ctypes.c_int32 * len(free_order))(*[int(b) for b in free_order])
+            _check(lib().pkv_alloc_create(int(num_blocks), int(block_size), arr, len(free_order),
+                                          ctypes.byref(h)), "pkv_alloc_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().pkv_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
+
+    def add_seq(self) -> int:
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_add_seq(self._h, ctypes.byref(out)), "pkv_alloc_add_seq")
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_fork(self._h, int(parent), ctypes.byref(out)), "pkv_alloc_fork")
+        return out.value
+
+    def append(self, seq: int):
+        """(slot, cow_src, cow_dst) of the sequence's next token; cow_* are -1 without a copy."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pkv_alloc_append(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
+                                      ctypes.byref(dst)), "pkv_alloc_append")
+        return slot.value, src.value, dst.value
+
+    def free_seq(self, seq: int, event=None):
+        """event: a torch.cuda.Event recorded after the sequence's last GPU use, or None."""
+        ev = ctypes.c_void_p(event.cuda_event) if event is not None else None
+        _check(lib().pkv_alloc_free_seq(self._h, int(seq), ev), "pkv_alloc_free_seq")
+
+    def table(self, seq: int):
+        """(block table as a list, committed length)"""
+        n, length = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().pkv_alloc_block_table(self._h, int(seq), None, 0, ctypes.byref(n),
+                                           ctypes.byref(length)), "pkv_alloc_block_table")
+        arr = (ctypes.c_int32 * max(1, n.value))()
+        _check(lib().pkv_alloc_block_table(self._h, int(seq), arr, n.value, ctypes.byref(n),
+                                           ctypes.byref(length)), "pkv_alloc_block_table")
+        return [arr[i] for i in range(n.value)], length.value
+
+    def refcount(self, block: int) -> int:
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_refcount(self._h, int(block), ctypes.byref(out)),
+               "pkv_alloc_refcount")
+        return out.value
+
+    def free_blocks(self):
+        """the free stack, bottom to top (the last entry is handed out next)"""
+        n = ctypes.c_int32()
+        _check(lib().pkv_alloc_free_blocks(self._h, None, 0, ctypes.byref(n)),
+               "pkv_alloc_free_blocks")
+        arr = (ctypes.c_int32 * max(1, n.value))()
+        _check(lib().pkv_alloc_free_blocks(self._h, arr, n.value, ctypes.byref(n)),
+               "pkv_alloc_free_blocks")
+        return [arr[i] for i in range(n.value)]
+
+
+def pkv_copy_blocks(pairs, desc: PoolDesc, k_pool, v_pool, k_scale=None, v_scale=None,
+                    stream=None):
+    """pairs: device int32 [n][2] of (src, dst) block ids"""
+    n = int(pairs.shape[0]) if pairs.numel() else 0
+    _check(lib().pkv_copy_blocks(_ptr(pairs, "pairs", allow_none=(n == 0)), n, ctypes.byref(desc),
+                                 _ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool"),
+                                 _ptr(k_scale, "k_scale", allow_none=True),
+                                 _ptr(v_scale, "v_scale", allow_none=True), _stream(stream)),
+           "pkv_copy_blocks")
 
 
 PARTITION_BALANCED = -1

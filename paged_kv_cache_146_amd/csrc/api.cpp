@@ -75,6 +75,7 @@ const char* pkv_strerror(int status) {
     case PKV_EUNSUPPORTED: return "no kernel for this configuration";
     case PKV_EWORKSPACE: return "workspace too small";
     case PKV_EHIP: return "HIP runtime error while launching";
+    case PKV_ENOBLOCKS: return "no free block";
     default: return "unknown status";
   }
 }
@@ -226,6 +227,22 @@ int pkv_kv_cache_append(const int32_t* block_table, int32_t num_seqs, int32_t ma
   p.positions = positions;
   p.slot_out = slot_mapping_out;
   rc = pkv::launch_kv_cache_write(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc* pool,
+                    void* k_pool, void* v_pool, float* k_scale, float* v_scale, void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_pairs < 0) return PKV_EINVAL;
+  if (num_pairs == 0) return PKV_OK;
+  if (num_pairs > 0x7fffffff / 2) return PKV_EINVAL;
+  if (!pairs || !k_pool || !v_pool || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_EINVAL;
+  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  rc = pkv::launch_copy_blocks(pairs, num_pairs, k_pool, v_pool, k_scale, v_scale,
+                               pool->num_blocks, pool->block_size, pool->num_kv_heads,
+                               pool->head_dim, pool->kv_dtype, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }
 

@@ -151,6 +151,46 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
   }
 }
 
+// Whole-block copies for copy on write ("KV Cache: capacity, layout,
+// lifecycle", "Reference counting and tail-block COW": the committed K/V and
+// the quantisation scales of the old tail block are copied before the new table
+// is published).  One block is contiguous in each pool ([block][head][...]), so
+// a copy is one run of H_kv pages per pool; workgroup (pair, pool, part) moves
+// a slice of it in 16-byte pieces, and part 0 of each pool also copies the fp8
+// scales of the block.
+__global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
+    const int32_t* __restrict__ pairs, int num_pairs, uint8_t* k_pool, uint8_t* v_pool,
+    float* k_scale, float* v_scale, int num_blocks, int Hkv, long long block_pieces) {
+  const int pr = blockIdx.x;
+  const int src = pairs[2 * pr], dst = pairs[2 * pr + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  const bool isv = blockIdx.y != 0;
+  u32x4* pool = reinterpret_cast<u32x4*>(isv ? v_pool : k_pool);
+  const u32x4* from = pool + (size_t)src * block_pieces;
+  u32x4* to = pool + (size_t)dst * block_pieces;
+  for (long long i = (long long)blockIdx.z * kWriteThreads + threadIdx.x; i < block_pieces;
+       i += (long long)gridDim.z * kWriteThreads)
+    to[i] = from[i];
+  float* sc = isv ? v_scale : k_scale;
+  if (sc && blockIdx.z == 0)
+    for (int h = threadIdx.x; h < Hkv; h += kWriteThreads)
+      sc[(size_t)dst * Hkv + h] = sc[(size_t)src * Hkv + h];
+}
+
+int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* v_pool,
+                       float* k_scale, float* v_scale, int num_blocks, int block_size, int Hkv,
+                       int head_dim, int kv_dtype, hipStream_t st) {
+  if (num_pairs == 0) return 0;
+  const int ES = kv_dtype == DT_F32 ? 4 : (kv_dtype == DT_FP8 ? 1 : 2);
+  const long long pieces = (long long)Hkv * head_dim * block_size * ES / 16;  // per pool
+  const long long parts = (pieces + 4 * kWriteThreads - 1) / (4 * kWriteThreads);
+  dim3 grid((unsigned)num_pairs, 2, (unsigned)(parts < 1 ? 1 : (parts > 64 ? 64 : parts)));
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kWriteThreads), 0, st, pairs, num_pairs,
+                     (uint8_t*)k_pool, (uint8_t*)v_pool, kv_dtype == DT_FP8 ? k_scale : nullptr,
+                     kv_dtype == DT_FP8 ? v_scale : nullptr, num_blocks, Hkv, pieces);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 int launch_slot_mapping(const int32_t* block_table, int num_seqs, int W, const int32_t* seq_idx,
                         const int32_t* positions, int num_tokens, int B, int64_t* slot_mapping,
                         hipStream_t st) {

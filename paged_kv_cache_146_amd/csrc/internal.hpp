@@ -75,6 +75,10 @@ struct WriteLaunch {
 };
 int launch_kv_cache_write(const WriteLaunch& p, hipStream_t stream);
 
+int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* v_pool,
+                       float* k_scale, float* v_scale, int num_blocks, int block_size, int Hkv,
+                       int head_dim, int kv_dtype, hipStream_t stream);
+
 struct PrefillLaunch {
   const void* q;
   int q_dtype;
