@@ -19,6 +19,11 @@ sequences, 4096 cached + 512 new tokens, H_q 32, H_kv 8, D 128, B 16, E4M3 KV wi
 fp32 page scales, bf16 q): a step writes the 512 new tokens' K/V of every sequence
 and runs the causal prefill over the whole context; `value` is TFLOP/s and the
 roofline is the prefill kernel against the dense bf16 MFMA peak.
+
+`--workload copy` measures the copy-on-write block copy: 2048 (src, dst) pairs of
+distinct random blocks of the decode layer's pool (bf16, 8 kv heads, B 16, D 128:
+32 KB per block and pool) in one pkv_copy_blocks launch; `value` is GB/s of
+algorithmic traffic (every block read once and written once).
 """
 from __future__ import annotations
 
@@ -45,14 +50,14 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size (0 = unsplit, -1 = balanced; default balanced)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "copy"], default="decode")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a 512 MiB device copy five times (a kernel of known HBM "
                          "traffic) so that rocprofv3's FETCH_SIZE/WRITE_SIZE can be scaled")
@@ -101,6 +106,9 @@ def main():
         return
     if a.gpus == 1 and a.workload == "prefill":
         prefill_main(a)
+        return
+    if a.gpus == 1 and a.workload == "copy":
+        copy_main(a)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -377,6 +385,83 @@ def prefill_main(a):
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(wl, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def copy_main(a):
+    """pkv_copy_blocks over 2048 block pairs of the decode layer's pool shape."""
+    import torch
+    import paged_kv_cache_146_amd as pkv
+
+    NB, B, H, D = 10776, 16, 8, 128
+    n_pairs = 2048
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(NB)[:2 * n_pairs].astype(np.int32)
+    pairs_np = ids.reshape(n_pairs, 2)
+    desc = pkv.pool_desc(NB, B, H, D, "bf16")
+    k_pool, v_pool = pkv.alloc_pool(desc)
+    k_pool.copy_(torch.randint(0, 256, k_pool.shape, dtype=torch.uint8, device="cuda"))
+    v_pool.copy_(torch.randint(0, 256, v_pool.shape, dtype=torch.uint8, device="cuda"))
+    pairs = torch.from_numpy(pairs_np).cuda()
+    flush = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
+    block_bytes = B * H * D * 2  # per pool
+    alg = 2 * n_pairs * block_bytes * 2  # both pools, read once + written once
+    steps = min(a.steps, 50)
+    for _ in range(min(a.warmup, 20)):
+        flush.sum()
+        pkv.pkv_copy_blocks(pairs, desc, k_pool, v_pool)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.sum()
+        starts[i].record()
+        pkv.pkv_copy_blocks(pairs, desc, k_pool, v_pool)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = np.array([x.elapsed_time(y) for x, y in zip(starts, ends)])
+    us = float(ms.mean() * 1e3)
+    kb = k_pool.view(NB, -1)
+    ok = bool(torch.equal(kb[pairs[:, 1].long()], kb[pairs[:, 0].long()]))
+    gbs = alg / (us * 1e-6) / 1e9
+    res = {
+        "metric": "copy-on-write block copy GB/s (pkv_copy_blocks)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(a.warmup, 20), "ms_per_step": round(us / 1e3, 5),
+        "us_per_step": round(us, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "2048 random (src, dst) block pairs of a 10776-block pool, "
+                               "bf16, 8 kv heads, B 16, D 128 (64 KB per pair)",
+                   "caches": "flushed before every copy"},
+        "algorithmic_bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(us, 2)},
+        "copies_match": ok,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_copy(pairs_np, block_bytes)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_copy(pairs_np, block_bytes):
+    """The oracle's block copy on host arrays holding just the blocks the pairs touch
+    (the same bytes per block), repeated until ~2 s are spent."""
+    import oracle
+    ids = np.unique(pairs_np)
+    remap = np.full(int(ids.max()) + 1, -1, np.int64)
+    remap[ids] = np.arange(len(ids))
+    local = remap[pairs_np]
+    k = np.ones((len(ids), block_bytes), np.uint8)
+    v = np.ones((len(ids), block_bytes), np.uint8)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < 2.0:
+        oracle.copy_blocks(k, v, None, None, local)
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    alg = 2 * len(pairs_np) * block_bytes * 2
+    return {"value": round(alg / dt / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "the same 2048 pairs on host copies of the touched blocks, %d runs" % n}
 
 
 def cpu_baseline_prefill(wl, budget_s):

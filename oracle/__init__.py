@@ -270,3 +270,20 @@ def paged_prefill(q, q_dtype: str, cu_seqlens_q, pool: Pool, block_table, contex
     if rc != 0:
         raise ValueError("invalid prefill arguments")
     return out
+
+
+def copy_blocks(k_pool, v_pool, k_scale, v_scale, pairs):
+    """["KV Cache: capacity, layout, lifecycle", "Reference counting and tail-block COW"]
+    copy on write copies the old tail block's committed K/V and its quantisation scales.
+    Here every byte of block src goes to block dst, in place, pair by pair; pairs with
+    an id outside the pool, or src == dst, are skipped.  k_pool, v_pool: numpy arrays
+    whose first axis is the block; k_scale, v_scale: [num_blocks][H_kv] or None."""
+    nb = k_pool.shape[0]
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        if not (0 <= src < nb and 0 <= dst < nb) or src == dst:
+            continue
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]
+        if k_scale is not None:
+            k_scale[dst] = k_scale[src]
+            v_scale[dst] = v_scale[src]

@@ -39,13 +39,7 @@ def test_copy_blocks_bit_exact(kv):
     want_v = vp.cpu().numpy().reshape(NB, -1).copy()
     want_ks = ks.cpu().numpy().copy() if ks is not None else None
     want_vs = vs.cpu().numpy().copy() if vs is not None else None
-    for s, d in pairs:
-        if 0 <= s < NB and 0 <= d < NB and s != d:
-            want_k[d] = want_k[s]
-            want_v[d] = want_v[s]
-            if ks is not None:
-                want_ks[d] = want_ks[s]
-                want_vs[d] = want_vs[s]
+    oracle.copy_blocks(want_k, want_v, want_ks, want_vs, pairs)
     pkv.pkv_copy_blocks(torch.tensor(pairs, dtype=torch.int32, device="cuda"), desc, kp, vp,
                         ks, vs)
     assert np.array_equal(kp.cpu().numpy().reshape(NB, -1), want_k)
