@@ -27,8 +27,11 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
-_NP_STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "int8": 4}
+_NP_STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+               "int8": np.int8}
+# where a quantised element's scale lives: [block][head], one for the tensor, [block][head][token]
+SCALE_MODES = {"block": 0, "tensor": 1, "token": 2}
 
 ORC_OK, ORC_EVALUE, ORC_EINDEX = 0, 1, 2
 
@@ -52,7 +55,7 @@ class _Pool(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
         ("num_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
-        ("kv_dtype", ctypes.c_int),
+        ("kv_dtype", ctypes.c_int), ("scale_mode", ctypes.c_int),
     ]
 
 
@@ -72,7 +75,9 @@ def _load():
                 "orc_e4m3_encode": (ctypes.c_uint8, [ctypes.c_float]),
                 "orc_decode_n": (None, [P, I32, I64, P]),
                 "orc_e4m3_encode_n": (None, [P, I64, P]),
-                "orc_kv_cache_write": (I32, [P, I64, P, P, I32, I64, I64, I64, I64, I32, P, P, P, P]),
+                "orc_int8_encode_n": (None, [P, I64, P]),
+                "orc_kv_cache_write": (I32, [P, I64, P, P, I32, I64, I64, I64, I64, I32, P, P, P, P,
+                                              I32]),
                 "orc_paged_decode": (I32, [P, I32, I64, I64, P, P, I64, P, D, P, I64, P, P]),
                 "orc_decode_partials": (I32, [P, I32, I64, I64, P, P, I64, P, D, I64, I64, P, P, P]),
                 "orc_state_merge": (None, [D, D, P, D, D, P, I64, P, P, P]),
@@ -143,13 +148,22 @@ def e4m3_encode(x):
     return out.reshape(a.shape)
 
 
+def int8_encode(x):
+    """symmetric int8 codes of float32 x (already divided by the scale)"""
+    a = np.ascontiguousarray(x, np.float32)
+    out = np.empty(a.shape, np.int8)
+    _load().orc_int8_encode_n(_ptr(a), a.size, _ptr(out))
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # Pools
 # --------------------------------------------------------------------------------------
 class Pool:
     """Logical paged pool: K and V as [num_blocks][num_kv_heads][block_size][head_dim]."""
 
-    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, fill_bits=None):
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, fill_bits=None,
+                 scale_mode="block"):
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
         self.num_kv_heads, self.head_dim = int(num_kv_heads), int(head_dim)
         self.kv_dtype = kv_dtype
@@ -163,6 +177,12 @@ class Pool:
             self.v = np.full(shape, fill_bits, st)
         self.k_scale = None
         self.v_scale = None
+        self.scale_mode = scale_mode
+
+    def scale_shape(self):
+        """shape of one scale array of a quantised pool in its scale mode"""
+        return {"block": (self.num_blocks, self.num_kv_heads), "tensor": (1,),
+                "token": (self.num_blocks, self.num_kv_heads, self.block_size)}[self.scale_mode]
 
     def _struct(self):
         s = _Pool()
@@ -172,6 +192,7 @@ class Pool:
         s.num_blocks, s.block_size = self.num_blocks, self.block_size
         s.num_kv_heads, s.head_dim = self.num_kv_heads, self.head_dim
         s.kv_dtype = DTYPES[self.kv_dtype]
+        s.scale_mode = SCALE_MODES[self.scale_mode]
         return s
 
 
@@ -185,7 +206,8 @@ def kv_cache_write(pool: Pool, slots, k, v, src_dtype: str):
     rc = _load().orc_kv_cache_write(_ptr(sl), len(sl), _ptr(k), _ptr(v), DTYPES[src_dtype],
                                     pool.num_blocks, pool.block_size, pool.num_kv_heads,
                                     pool.head_dim, DTYPES[pool.kv_dtype], _ptr(pool.k),
-                                    _ptr(pool.v), _ptr(ks), _ptr(vs))
+                                    _ptr(pool.v), _ptr(ks), _ptr(vs),
+                                    SCALE_MODES[pool.scale_mode])
     if rc != 0:
         raise ValueError("unsupported type combination for the cache write")
 

@@ -119,14 +119,35 @@ uint8_t orc_e4m3_encode(float x) {
   return (uint8_t)(sign | best);
 }
 
+/* symmetric int8 of x (already divided by the scale): nearest integer, ties to
+ * even (rint under the default rounding mode), saturated to [-127, 127]; NaN -> 0 */
+int8_t orc_int8_encode(float x) {
+  if (isnan(x)) return 0;
+  double r = rint((double)x);
+  if (r > 127.0) r = 127.0;
+  if (r < -127.0) r = -127.0;
+  return (int8_t)r;
+}
+
 static size_t elem_size(int t) {
   switch (t) {
     case ORC_F32: return 4;
     case ORC_F16: return 2;
     case ORC_BF16: return 2;
     case ORC_FP8_E4M3: return 1;
+    case ORC_INT8: return 1;
     default: return 0;
   }
+}
+
+static int quantised(int t) { return t == ORC_FP8_E4M3 || t == ORC_INT8; }
+
+/* index of the scale of element (blk, kvh, off) */
+static int64_t scale_index(int mode, int64_t blk, int64_t kvh, int64_t off, int64_t num_kv_heads,
+                           int64_t block_size) {
+  if (mode == ORC_SCALE_TENSOR) return 0;
+  if (mode == ORC_SCALE_TOKEN) return (blk * num_kv_heads + kvh) * block_size + off;
+  return blk * num_kv_heads + kvh;
 }
 
 /* exact value of element i of an array of storage type t */
@@ -136,12 +157,17 @@ static double load_value(const void* p, int t, size_t i) {
     case ORC_F16: return orc_f16_decode(((const uint16_t*)p)[i]);
     case ORC_BF16: return orc_bf16_decode(((const uint16_t*)p)[i]);
     case ORC_FP8_E4M3: return orc_e4m3_decode(((const uint8_t*)p)[i]);
+    case ORC_INT8: return (double)((const int8_t*)p)[i];
     default: return NAN;
   }
 }
 
 void orc_decode_n(const void* p, int dtype, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = load_value(p, dtype, (size_t)i);
+}
+
+void orc_int8_encode_n(const float* x, int64_t n, int8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_int8_encode(x[i]);
 }
 
 void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* out) {
@@ -153,10 +179,12 @@ void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* out) {
 int orc_kv_cache_write(const int64_t* slot_mapping, int64_t num_tokens, const void* k,
                        const void* v, int src_dtype, int64_t num_blocks, int64_t block_size,
                        int64_t num_kv_heads, int64_t head_dim, int kv_dtype, void* k_pool,
-                       void* v_pool, const float* k_scale, const float* v_scale) {
+                       void* v_pool, const float* k_scale, const float* v_scale,
+                       int scale_mode) {
   if (elem_size(src_dtype) == 0 || elem_size(kv_dtype) == 0) return -1;
-  if (kv_dtype != ORC_FP8_E4M3 && src_dtype != kv_dtype) return -1;
-  if (kv_dtype == ORC_FP8_E4M3 && (src_dtype == ORC_FP8_E4M3 || !k_scale || !v_scale)) return -1;
+  if (!quantised(kv_dtype) && src_dtype != kv_dtype) return -1;
+  if (quantised(kv_dtype) && (quantised(src_dtype) || !k_scale || !v_scale)) return -1;
+  if (scale_mode < ORC_SCALE_BLOCK || scale_mode > ORC_SCALE_TOKEN) return -1;
   size_t es = elem_size(kv_dtype);
   size_t ss = elem_size(src_dtype);
   const void* src[2] = {k, v};
@@ -170,15 +198,18 @@ int orc_kv_cache_write(const int64_t* slot_mapping, int64_t num_tokens, const vo
       for (int64_t h = 0; h < num_kv_heads; ++h) {
         size_t src_row = ((size_t)i * num_kv_heads + h) * head_dim;
         size_t dst_row = (((size_t)blk * num_kv_heads + h) * block_size + off) * head_dim;
-        if (kv_dtype != ORC_FP8_E4M3) {
+        if (!quantised(kv_dtype)) {
           memcpy((char*)dst[which] + dst_row * es, (const char*)src[which] + src_row * ss,
                  head_dim * es);
         } else {
-          float s = scl[which][blk * num_kv_heads + h];
+          float s = scl[which][scale_index(scale_mode, blk, h, off, num_kv_heads, block_size)];
           for (int64_t d = 0; d < head_dim; ++d) {
             float x = (float)load_value(src[which], src_dtype, src_row + d); /* exact */
             float y = x / s; /* IEEE fp32 division, round to nearest even */
-            ((uint8_t*)dst[which])[dst_row + d] = orc_e4m3_encode(y);
+            if (kv_dtype == ORC_FP8_E4M3)
+              ((uint8_t*)dst[which])[dst_row + d] = orc_e4m3_encode(y);
+            else
+              ((int8_t*)dst[which])[dst_row + d] = orc_int8_encode(y);
           }
         }
       }
@@ -189,15 +220,16 @@ int orc_kv_cache_write(const int64_t* slot_mapping, int64_t num_tokens, const vo
 
 /* ---- [P1 §3, §4] gather one token's K or V row through the table ---------- */
 
-/* exact value of pool[blk][kvh][off][:] (times the page's scale for FP8) */
+/* exact value of pool[blk][kvh][off][:] (times its scale for a quantised pool) */
 static void load_row(const orc_pool* pool, int which, int64_t blk, int64_t kvh, int64_t off,
                      double* row) {
   const void* base = which == 0 ? pool->k_pool : pool->v_pool;
   size_t r = (((size_t)blk * pool->num_kv_heads + kvh) * pool->block_size + off) * pool->head_dim;
   double s = 1.0;
-  if (pool->kv_dtype == ORC_FP8_E4M3) {
+  if (quantised(pool->kv_dtype)) {
     const float* sc = which == 0 ? pool->k_scale : pool->v_scale;
-    s = (double)sc[blk * pool->num_kv_heads + kvh];
+    s = (double)sc[scale_index(pool->scale_mode, blk, kvh, off, pool->num_kv_heads,
+                               pool->block_size)];
   }
   for (int64_t d = 0; d < pool->head_dim; ++d)
     row[d] = load_value(base, pool->kv_dtype, r + d) * s;
@@ -243,7 +275,7 @@ static int check_pool(const orc_pool* pool, int64_t num_q_heads) {
   if (!pool || elem_size(pool->kv_dtype) == 0 || pool->block_size <= 0 || pool->head_dim <= 0 ||
       pool->num_kv_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
     return -1;
-  if (pool->kv_dtype == ORC_FP8_E4M3 && (!pool->k_scale || !pool->v_scale)) return -1;
+  if (quantised(pool->kv_dtype) && (!pool->k_scale || !pool->v_scale)) return -1;
   return 0;
 }
 
@@ -252,7 +284,7 @@ int orc_paged_decode(const void* q, int q_dtype, int64_t num_seqs, int64_t num_q
                      const orc_pool* pool, const int32_t* block_table,
                      int64_t max_blocks_per_seq, const int32_t* context_lens, double scale,
                      const int32_t* seqs, int64_t n_sel, double* out, double* lse) {
-  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || q_dtype == ORC_FP8_E4M3)
+  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || quantised(q_dtype))
     return -1;
   if (!seqs) n_sel = num_seqs;
   int64_t D = pool->head_dim, G = num_q_heads / pool->num_kv_heads;
@@ -292,7 +324,7 @@ int orc_decode_partials(const void* q, int q_dtype, int64_t num_seqs, int64_t nu
                         int64_t max_blocks_per_seq, const int32_t* context_lens, double scale,
                         int64_t partition_size, int64_t max_partitions, double* part_out,
                         double* part_max, double* part_sum) {
-  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || q_dtype == ORC_FP8_E4M3 ||
+  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || quantised(q_dtype) ||
       partition_size <= 0)
     return -1;
   int64_t D = pool->head_dim, G = num_q_heads / pool->num_kv_heads;
@@ -382,7 +414,7 @@ int orc_paged_prefill(const void* q, int q_dtype, const int32_t* cu_seqlens_q, i
                       int64_t num_q_heads, const orc_pool* pool, const int32_t* block_table,
                       int64_t max_blocks_per_seq, const int32_t* context_lens, double scale,
                       int causal, const int64_t* rows, int64_t n_rows, double* out) {
-  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || q_dtype == ORC_FP8_E4M3)
+  if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || quantised(q_dtype))
     return -1;
   int64_t total_q = cu_seqlens_q[num_seqs];
   if (!rows) n_rows = total_q;

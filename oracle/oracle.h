@@ -27,9 +27,17 @@
  *   - Decode: context_lens[s] counts every cached token including the one
  *     just written; no mask inside [0, ctx).
  *   - fp8 is OCP E4M3 (bias 7, no infinity, S.1111.111 = NaN, max 448);
- *     dequantised value = decode(code) * scale[block][kv_head]; encoding takes
- *     x / scale in IEEE fp32 and rounds to nearest, ties to even, saturating
- *     finite overflow (and infinities) to +-448; NaN -> 0x7F with the sign of x.
+ *     dequantised value = decode(code) * scale; encoding takes x / scale in IEEE
+ *     fp32 and rounds to nearest, ties to even, saturating finite overflow (and
+ *     infinities) to +-448; NaN -> 0x7F with the sign of x.
+ *   - int8 ([P1 §8.1] names per-token-head INT8 and nothing more): symmetric,
+ *     dequantised value = code * scale; encoding rounds x / scale (IEEE fp32) to
+ *     the nearest integer, ties to even, saturating to [-127, 127]; NaN -> 0.
+ *   - The scale of element (block, kv head, offset) ([P1 §8.1]: per-tensor
+ *     FP8, per-token-head INT8/FP8, the scales counted in the page size):
+ *       ORC_SCALE_BLOCK  scale[block * num_kv_heads + head]
+ *       ORC_SCALE_TENSOR scale[0]
+ *       ORC_SCALE_TOKEN  scale[(block * num_kv_heads + head) * block_size + offset]
  *   - A slot or slot-mapping entry that is negative is padding: skipped.
  *   - ctx = 0 gives an all-zero output and lse = -inf.
  *   - All arithmetic on decoded values is in IEEE double.
@@ -51,6 +59,12 @@ extern "C" {
 #define ORC_F16 1
 #define ORC_BF16 2
 #define ORC_FP8_E4M3 3
+#define ORC_INT8 4
+
+/* where the scale of a quantised element lives (see the conventions above) */
+#define ORC_SCALE_BLOCK 0
+#define ORC_SCALE_TENSOR 1
+#define ORC_SCALE_TOKEN 2
 
 /* results of orc_physical_slot, mirroring the page's exceptions */
 #define ORC_OK 0
@@ -79,6 +93,10 @@ uint8_t orc_e4m3_encode(float x);
 /* array forms of the codecs above (for the tests' exhaustive sweeps) */
 void orc_decode_n(const void* p, int dtype, int64_t n, double* out);
 void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* out);
+/* symmetric int8 code of x (already divided by its scale); pinned against numpy's
+ * rint (ties to even) and clip on ties, saturation and random values */
+int8_t orc_int8_encode(float x);
+void orc_int8_encode_n(const float* x, int64_t n, int8_t* out);
 
 /* [P1 §4.1, §8.1]: scatter the new tokens' K/V into the logical pools.
  * k, v: [num_tokens][num_kv_heads][head_dim] in src_dtype (f32/f16/bf16 bits).
@@ -89,16 +107,18 @@ void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* out);
 int orc_kv_cache_write(const int64_t* slot_mapping, int64_t num_tokens, const void* k,
                        const void* v, int src_dtype, int64_t num_blocks, int64_t block_size,
                        int64_t num_kv_heads, int64_t head_dim, int kv_dtype, void* k_pool,
-                       void* v_pool, const float* k_scale, const float* v_scale);
+                       void* v_pool, const float* k_scale, const float* v_scale,
+                       int scale_mode);
 
 /* Common description of a paged pool, as the oracle reads it. */
 typedef struct orc_pool {
   const void* k_pool;    /* logical layout [num_blocks][num_kv_heads][block_size][head_dim] */
   const void* v_pool;
-  const float* k_scale;  /* [num_blocks][num_kv_heads], FP8 only (else NULL) */
+  const float* k_scale;  /* quantised pools only (else NULL), indexed per scale_mode */
   const float* v_scale;
   int64_t num_blocks, block_size, num_kv_heads, head_dim;
   int kv_dtype;
+  int scale_mode;        /* ORC_SCALE_*, quantised pools only */
 } orc_pool;
 
 /* [P1 §4], [P3 §5]: decode attention.  For each selected sequence s and query

@@ -166,3 +166,49 @@ def test_fp8_write_quantises_within_half_spacing():
     # y is the fp32 quotient; allow its own rounding (2^-24 relative) on top
     assert np.all(np.abs(y - vdec)[inr] <= half[inr] + np.abs(y[inr]) * 2.0 ** -23)
     assert np.all(np.abs(vdec[~inr]) == 448)
+
+
+@pytest.mark.parametrize("kv,mode", [("int8", "token"), ("int8", "tensor"), ("fp8", "token")])
+def test_quantised_write_uses_each_tokens_scale(kv, mode):
+    """[P1 §8.1] per-token-head and per-tensor scales: codes that are exact integers
+    (int8) or exact e4m3 values (fp8) times the scale of their own (block, head, token)
+    slot, read back by logical slot, come back exactly; any other value lands within
+    half a code of x / scale."""
+    import torch
+
+    rng = np.random.default_rng(len(kv) * 10 + len(mode))
+    NB, B, H, D = 6, 4, 2, 16
+    pool = oracle.Pool(NB, B, H, D, kv, scale_mode=mode)
+    pool.k_scale = (2.0 ** rng.integers(-3, 4, size=pool.scale_shape())).astype(np.float32)
+    pool.v_scale = rng.uniform(0.01, 0.5, size=pool.scale_shape()).astype(np.float32)
+    T = NB * B
+    slots = rng.permutation(T).astype(np.int64)
+    blk, off = slots // B, slots % B
+
+    def per_slot(sc):  # [T][H] scale of each written row, by logical slot
+        if mode == "tensor":
+            return np.broadcast_to(sc[0], (T, H)).astype(np.float64)
+        return sc[blk, :, off].astype(np.float64)
+
+    if kv == "int8":
+        codes = rng.integers(-127, 128, size=(T, H, D)).astype(np.int8)
+        exact = codes.astype(np.float32)
+    else:
+        codes = rng.integers(0, 0x7F, size=(T, H, D)).astype(np.uint8) | (
+            rng.integers(0, 2, size=(T, H, D)).astype(np.uint8) << 7)
+        exact = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    kx = (exact * per_slot(pool.k_scale)[:, :, None]).astype(np.float32)
+    kbits = torch.from_numpy(kx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vx = rng.standard_normal((T, H, D)).astype(np.float32)
+    vbits = torch.from_numpy(vx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    oracle.kv_cache_write(pool, slots, kbits, vbits, "bf16")
+    assert np.array_equal(pool.k[blk, :, off, :], codes)
+    vin = torch.from_numpy(vbits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    y = vin / per_slot(pool.v_scale)[:, :, None]
+    vq = pool.v[blk, :, off, :]
+    if kv == "int8":
+        assert (np.abs(vq.astype(np.float64) - np.clip(y, -127, 127)) <= 0.5 + 1e-9).all()
+    else:
+        dec = torch.from_numpy(vq).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert (np.abs(dec - np.clip(y, -448, 448)) <= 2.0 ** (np.floor(np.log2(
+            np.maximum(np.abs(y), 2.0 ** -6))) - 3) / 2 + 1e-12).all()

@@ -10,6 +10,9 @@ of the OCP 8-bit floating point E4M3 format).  The encoder is checked
   - on a random sample of 2^22 fp32 bit patterns;
   - on hand-listed ties, subnormals, zero signs, saturation and NaN, where torch
     differs by design (it maps overflow to NaN; the reading here saturates).
+int8 decoding is checked on all 256 codes (numpy int8) and the symmetric int8
+encoder against numpy's rint (round half to even) and clip on ties, saturation,
+NaN and random values.
 """
 import numpy as np
 import torch
@@ -98,3 +101,22 @@ def test_e4m3_encode_hand_cases():
     assert f(float("inf")) == 0x7E and f(float("-inf")) == 0xFE and f(-1000.0) == 0xFE
     assert f(float("nan")) == 0x7F
     assert f(-float("nan")) == 0xFF
+
+
+def test_int8_decode_all_codes():
+    codes = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    assert np.array_equal(oracle.decode(codes, "int8"), codes.astype(np.float64))
+
+
+def test_int8_encode_vs_numpy():
+    rng = np.random.default_rng(8)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 60,
+        np.arange(-130.5, 131, 0.5, dtype=np.float32),            # every tie near the range
+        np.array([0.0, -0.0, 126.49, 126.5, 127.5, -127.5, -128.0, 1e9, -1e9, np.inf,
+                  -np.inf], np.float32)])
+    want = np.clip(np.rint(x.astype(np.float64)), -127, 127).astype(np.int8)
+    assert np.array_equal(oracle.int8_encode(x), want)
+    assert oracle.int8_encode(np.array([np.nan], np.float32))[0] == 0
+    assert list(oracle.int8_encode(np.array([0.5, 1.5, 2.5, -0.5, -2.5], np.float32))) == \
+        [0, 2, 2, 0, -2]
