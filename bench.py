@@ -58,6 +58,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
     ap.add_argument("--workload", choices=["decode", "prefill", "copy"], default="decode")
+    ap.add_argument("--kv", choices=["bf16", "fp8", "int8"], default="bf16",
+                    help="decode workload: pool element type (quantised pools store the "
+                         "same bf16 draws as codes with fp32 scales)")
+    ap.add_argument("--scale-mode", choices=["block", "tensor", "token"], default="block",
+                    help="decode workload with a quantised pool: where the scales live")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a 512 MiB device copy five times (a kernel of known HBM "
                          "traffic) so that rocprofv3's FETCH_SIZE/WRITE_SIZE can be scaled")
@@ -81,6 +86,7 @@ def calibrate():
 
 
 DEFAULT_PARTITION = -1  # balanced split-KV
+W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}  # pool bytes per element
 
 
 def decode_bytes(wl) -> int:
@@ -93,10 +99,13 @@ def decode_bytes(wl) -> int:
 
 
 def write_bytes(wl) -> int:
-    """Slot mapping (seq, pos, table entry in; slot out) + scatter (K/V rows in and out)."""
+    """Slot mapping (seq, pos, table entry in; slot out) + scatter (bf16 K/V rows in, pool
+    rows out, and for a quantised pool the K and V scale of every (token, kv head))."""
     S = wl.num_seqs
-    row = wl.num_kv_heads * wl.head_dim * 2
-    return S * (4 + 4 + 4 + 8) + S * (8 + 2 * row + 2 * row)
+    src_row = wl.num_kv_heads * wl.head_dim * 2
+    pool_row = wl.num_kv_heads * wl.head_dim * W_ELEM[wl.kv_dtype]
+    scales = 2 * wl.num_kv_heads * 4 if wl.kv_dtype in ("fp8", "int8") else 0
+    return S * (4 + 4 + 4 + 8) + S * (8 + 2 * src_row + 2 * pool_row + scales)
 
 
 def main():
@@ -119,10 +128,13 @@ def main():
     from paged_kv_cache_146_amd import workloads as W
 
     P = DEFAULT_PARTITION if a.partition is None else a.partition
-    wl = W.llama3_8b_decode(seed=2)
+    wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
     dev = "cuda"
-    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                         wl.scale_mode)
     k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
+    ks = torch.from_numpy(wl.k_scale).to(dev) if wl.k_scale is not None else None
+    vs = torch.from_numpy(wl.v_scale).to(dev) if wl.v_scale is not None else None
     bt = torch.from_numpy(wl.block_table).to(dev)
     cl = torch.from_numpy(wl.context_lens).to(dev)
 
@@ -136,7 +148,8 @@ def main():
         e = min(T, o + slab)
         sl = pkv.pkv_slot_mapping(bt, torch.from_numpy(wl.fill_seq[o:e]).to(dev),
                                   torch.from_numpy(wl.fill_pos[o:e]).to(dev), wl.block_size)
-        pkv.pkv_kv_cache_write(sl, bits(wl.k_src[o:e]), bits(wl.v_src[o:e]), desc, k_pool, v_pool)
+        pkv.pkv_kv_cache_write(sl, bits(wl.k_src[o:e]), bits(wl.v_src[o:e]), desc, k_pool, v_pool,
+                               ks, vs, src_dtype="bf16")
     q = bits(wl.q)
     rows = wl.decode_new_token_rows()
     k_new, v_new = bits(wl.k_src[rows]), bits(wl.v_src[rows])
@@ -154,13 +167,14 @@ def main():
 
     def decode():
         pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
-                                       wl.scale, partition_size=P, workspace=ws, out=out)
+                                       wl.scale, partition_size=P, k_scale=ks, v_scale=vs,
+                                       workspace=ws, out=out, q_dtype="bf16")
 
     def step():
         # slot mapping and scatter of the new tokens in one launch (the slots are
         # written out too), then the decode
         pkv.pkv_kv_cache_append(bt, seq_idx, pos_new, k_new, v_new, desc, k_pool, v_pool,
-                                slot_mapping_out=slots)
+                                ks, vs, src_dtype="bf16", slot_mapping_out=slots)
         decode()
 
     def timed(fn, n):
@@ -192,9 +206,7 @@ def main():
     parity = None
     try:
         import oracle
-        opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "bf16")
-        osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
-        oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+        opool = _oracle_pool(oracle, wl)
         sel = np.array([0, int(np.argmax(wl.context_lens))], np.int32)
         ref = oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
                                   seqs=sel)
@@ -214,7 +226,9 @@ def main():
     if os.path.exists(COUNTERS):
         c = json.load(open(COUNTERS))
         src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P:
+        if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
+                and c.get("kv_dtype", "bf16") == wl.kv_dtype
+                and c.get("scale_mode", "block") == wl.scale_mode):
             traffic = c.get("hbm_bytes_per_launch")
 
     res = {
@@ -238,7 +252,9 @@ def main():
             "num_seqs": wl.num_seqs, "context_lens": "U[128,4096], seed 2",
             "sum_context": int(wl.context_lens.sum()), "H_q": wl.num_q_heads,
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
-            "kv_dtype": "bf16", "num_blocks": wl.num_blocks, "partition_size": P,
+            "kv_dtype": wl.kv_dtype,
+            "scale_mode": wl.scale_mode if wl.kv_dtype in ("fp8", "int8") else None,
+            "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
             "step": "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) + paged_attention_decode",
         },
@@ -494,13 +510,21 @@ def cpu_baseline_prefill(wl, budget_s):
                       % (done, done * 37 // total, t_used)}
 
 
+def _oracle_pool(oracle, wl):
+    """The oracle's pool for the decode workload, filled by the oracle's own write path."""
+    opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                        scale_mode=wl.scale_mode)
+    opool.k_scale, opool.v_scale = wl.k_scale, wl.v_scale
+    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
+    oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, wl.src_dtype)
+    return opool
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle as it stands, on the same workload, on this host's cores: the write of
     the 64 new tokens plus decode attention for a bounded prefix of the sequences."""
     import oracle
-    opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, "bf16")
-    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
-    oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, "bf16")
+    opool = _oracle_pool(oracle, wl)
     rows = wl.decode_new_token_rows()
     order = np.arange(wl.num_seqs, dtype=np.int32)
     steps, t_used = 0, 0.0

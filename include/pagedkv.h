@@ -7,7 +7,8 @@
  *        §3 block table, slot formula; §3.1 page bytes; §4 paged kernel loop,
  *        online-softmax triple, split-KV decode, tiled prefill given the table;
  *        §4.1 write path through slot_mapping; §4.2 stable buffers, free only
- *        after consumers finish; §8.1 FP8 KV with FP32 scales.
+ *        after consumers finish; §8.1 quantised KV (FP8 / INT8 codes with FP32
+ *        scales per block and head, per tensor, or per token and head).
  *   [P2] "KV Cache: capacity, layout, lifecycle" (wineandchord)
  *        "Page-table addressing" (physical_slot and its errors), "Physical
  *        layout", "Correctness contract" (reject a mismatched descriptor),
@@ -38,7 +39,8 @@
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
  *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
  *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
- *   fp8 scales (K and V separately): float [num_blocks][num_kv_heads]
+ *   scales of a quantised pool (K and V separately): float arrays whose shape
+ *   the descriptor's scale_mode sets (pkv_scale_mode below)
  * One (block, kv head) page is contiguous in each pool.  The logical element
  * K[block][head][t][d] lives at K pool index
  *   (((block*num_kv_heads + head)*(head_dim/X) + d/X)*block_size + t)*X + d%X
@@ -59,13 +61,27 @@ extern "C" {
 
 #define PKV_VERSION 100
 
-/* element types; fp8 is OCP E4M3 (bias 7, max 448, no infinity) */
+/* element types; fp8 is OCP E4M3 (bias 7, max 448, no infinity); int8 is a
+ * symmetric code (value = code * scale).  fp8 and int8 pools are "quantised":
+ * each element has an fp32 scale, placed as the descriptor's scale_mode says. */
 typedef enum pkv_dtype {
   PKV_F32 = 0,
   PKV_F16 = 1,
   PKV_BF16 = 2,
-  PKV_FP8_E4M3 = 3
+  PKV_FP8_E4M3 = 3,
+  PKV_INT8 = 4
 } pkv_dtype;
+
+/* [P1 §8.1] where the scale of a quantised element (block, kv head, token offset)
+ * lives; k_scale and v_scale are separate device float arrays of this shape:
+ *   PKV_SCALE_BLOCK  [num_blocks][num_kv_heads]               (one per page)
+ *   PKV_SCALE_TENSOR [1]                                      (one per pool)
+ *   PKV_SCALE_TOKEN  [num_blocks][num_kv_heads][block_size]   (per token and head) */
+typedef enum pkv_scale_mode {
+  PKV_SCALE_BLOCK = 0,
+  PKV_SCALE_TENSOR = 1,
+  PKV_SCALE_TOKEN = 2
+} pkv_scale_mode;
 
 /* status codes */
 enum {
@@ -88,6 +104,7 @@ typedef struct pkv_pool_desc {
   int32_t num_kv_heads; /* H_kv */
   int32_t head_dim;     /* D */
   int32_t kv_dtype;     /* pkv_dtype */
+  int32_t scale_mode;   /* pkv_scale_mode: quantised pools; 0 for the others */
 } pkv_pool_desc;
 
 /* Human-readable text of a status code (static storage). */
@@ -99,8 +116,9 @@ int pkv_version(void);
 /* [P1 §3.1] Bytes of the K pool and the V pool:
  *   num_blocks * num_kv_heads * block_size * head_dim * E  each,
  * i.e. the per-layer page size 2*block_size*num_kv_heads*head_dim*E split
- * into K and V; for fp8 also the bytes of ONE scale array
- * (num_blocks*num_kv_heads*4), else 0.  Any output pointer may be NULL.
+ * into K and V; for quantised pools also the bytes of ONE scale array in the
+ * descriptor's scale mode ([P1 §8.1]: the scales count in the page size), else
+ * 0.  Any output pointer may be NULL.
  * Errors: PKV_EINVAL for a NULL/invalid descriptor, PKV_EUNSUPPORTED for a
  * valid one this library has no kernels for. */
 int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
@@ -139,12 +157,16 @@ int pkv_slot_mapping(const int32_t* block_table, int32_t num_seqs, int32_t max_b
  * any padded K/V), if 0 <= slot_mapping[i] < num_blocks*block_size, token i's
  * K/V rows k[i][h][:], v[i][h][:] are stored at block slot/B, offset slot%B.
  *   k, v: device [num_tokens][num_kv_heads][head_dim] of src_dtype.
- *   Non-fp8 pools: src_dtype must equal pool->kv_dtype; the copy is bitwise.
- *   fp8 pools: src_dtype in {F32, F16, BF16}; each element is stored as
- *     e4m3(x / scale[block][head]) with x / scale an IEEE fp32 division,
- *     rounded to nearest (ties to even), saturating finite overflow and
- *     infinities to +-448; NaN stays NaN.  k_scale, v_scale: device float
- *     [num_blocks][num_kv_heads], read only (the caller owns the scales).
+ *   Unquantised pools: src_dtype must equal pool->kv_dtype; the copy is bitwise.
+ *   Quantised pools: src_dtype in {F32, F16, BF16}.  With s the element's scale
+ *     (the one for its block and head, for the pool, or for its token and head,
+ *     as scale_mode says) and x / s an IEEE fp32 division, fp8 stores
+ *     e4m3(x / s) rounded to nearest (ties to even), saturating finite overflow
+ *     and infinities to +-448, NaN staying NaN; int8 stores x / s rounded to
+ *     the nearest integer (ties to even) and clamped to [-127, 127], infinities
+ *     giving +-127 and NaN 0.  k_scale, v_scale: device float arrays of the
+ *     scale mode's shape, read only: the caller owns and chooses the scales
+ *     (in token mode, those of the tokens being written).
  * Negative or out-of-pool slots are skipped.  Two tokens with the same slot
  * race (the caller's slot mapping should be injective).
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
@@ -195,13 +217,16 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
 /* [P1 §4] Paged decode attention, one query token per sequence.
  * For sequence s and query head h (kv head h / (num_q_heads / num_kv_heads)):
  *   z_t = scale * <q[s][h], K_t>,  t < ctx_s, K_t/V_t found through
- *   block_table[s][t / B] at offset t % B (fp8: times the page's scale),
+ *   block_table[s][t / B] at offset t % B (a quantised code times its scale),
  *   out[s][h] = sum_t exp(z_t - max z) V_t / sum_t exp(z_t - max z)
  * with fp32 accumulation; ctx_s = 0 gives zeros.  The newest token's K/V
  * must already have been written (context_lens counts it).
  *   q: device [num_seqs][num_q_heads][head_dim] of q_dtype;
- *      (pool f32, q f32), (f16, f16), (bf16, bf16), (fp8, bf16|f16) supported.
- *   k_pool, v_pool: device, layout above; k_scale, v_scale: fp8 only, else NULL.
+ *      (pool f32, q f32), (f16, f16), (bf16, bf16), (fp8 or int8, bf16|f16)
+ *      supported, each scale mode for the quantised pools.
+ *   k_pool, v_pool: device, layout above; k_scale, v_scale: quantised pools
+ *      only, else NULL.  Scales of slots past a sequence's context are never
+ *      used (in token mode they may hold anything, NaN included).
  *   block_table: device int32 [num_seqs][max_blocks_per_seq].
  *   context_lens: device int32 [num_seqs]; each is clamped to
  *      [0, min(max_context_len, max_blocks_per_seq * block_size)].
@@ -256,7 +281,8 @@ int pkv_split_kv_reduce(const float* part_out, const float* part_max, const floa
  *   q: device [total_q][num_q_heads][head_dim] of q_dtype; out likewise.
  *   cu_seqlens_q: device int32 [num_seqs + 1], non-decreasing, last = total_q.
  *   max_q_len: host-known upper bound on n_s (sizes the grid).
- *   Supported: q bf16 with a bf16 or fp8 pool; head_dim 64 or 128; block_size
+ *   Supported: q bf16 with a bf16 pool or an fp8 pool in PKV_SCALE_BLOCK mode
+ *   (other pools: PKV_EUNSUPPORTED); head_dim 64 or 128; block_size
  *   16..64 (a 16-token tile must lie in one block); group size G = H_q/H_kv
  *   in {1, 2, 4, 8, 16}.  fp8 keys widen exactly to bf16 for QK^T and K's
  *   scale multiplies the scores; fp8 values widen exactly to f16 and V's scale
@@ -335,12 +361,14 @@ int pkv_alloc_free_blocks(pkv_alloc* alloc, int32_t* free_order, int32_t capacit
 
 /* [P2] "Reference counting and tail-block COW": copy whole blocks.
  *   pairs: device int32 [num_pairs][2] of (src, dst) block ids.  For each pair,
- *   every byte of block src in both pools (all kv heads) and, for fp8 pools,
- *   its scales k_scale[src][:], v_scale[src][:] are copied to dst.  Pairs with
+ *   every byte of block src in both pools (all kv heads) and, for quantised
+ *   pools in block or token mode, its scales (k_scale[src] and v_scale[src]:
+ *   every head, and every offset in token mode) are copied to dst; a
+ *   PKV_SCALE_TENSOR scale belongs to no block and is left as it is.  Pairs with
  *   an id outside [0, num_blocks), or src == dst, are skipped; destinations
  *   must be distinct and must not be the source of another pair (else the
- *   copies race).  k_scale, v_scale: device float [num_blocks][num_kv_heads],
- *   fp8 pools only (else ignored).  Errors: PKV_EINVAL, PKV_EUNSUPPORTED,
+ *   copies race).  k_scale, v_scale: device float arrays of the scale mode's
+ *   shape, quantised pools only (else ignored).  Errors: PKV_EINVAL, PKV_EUNSUPPORTED,
  *   PKV_EHIP. */
 int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc* pool,
                     void* k_pool, void* v_pool, float* k_scale, float* v_scale, void* stream);

@@ -299,7 +299,9 @@ def copy_blocks(k_pool, v_pool, k_scale, v_scale, pairs):
     copy on write copies the old tail block's committed K/V and its quantisation scales.
     Here every byte of block src goes to block dst, in place, pair by pair; pairs with
     an id outside the pool, or src == dst, are skipped.  k_pool, v_pool: numpy arrays
-    whose first axis is the block; k_scale, v_scale: [num_blocks][H_kv] or None."""
+    whose first axis is the block; k_scale, v_scale: arrays whose first axis is the
+    block ([num_blocks][H_kv] or [num_blocks][H_kv][B]), or None where no scale
+    belongs to a block (unquantised pools, one scale for the whole pool)."""
     nb = k_pool.shape[0]
     for src, dst in np.asarray(pairs).reshape(-1, 2):
         if not (0 <= src < nb and 0 <= dst < nb) or src == dst:

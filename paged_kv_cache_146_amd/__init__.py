@@ -20,9 +20,15 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
-DTYPE_NAMES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
-ELEM_BYTES = {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3,
+               "int8": PKV_INT8}
+ELEM_BYTES = {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1, PKV_INT8: 1}
+QUANTISED = (PKV_FP8_E4M3, PKV_INT8)
+# where a quantised pool keeps its fp32 scales: one per (block, kv head), one for
+# the whole pool, or one per (block, kv head, token)
+PKV_SCALE_BLOCK, PKV_SCALE_TENSOR, PKV_SCALE_TOKEN = 0, 1, 2
+SCALE_MODES = {"block": PKV_SCALE_BLOCK, "tensor": PKV_SCALE_TENSOR, "token": PKV_SCALE_TOKEN}
 STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ERANGE", -3: "PKV_EUNSUPPORTED",
           -4: "PKV_EWORKSPACE", -5: "PKV_EHIP", -6: "PKV_ENOBLOCKS"}
 PKV_ENOBLOCKS = -6
@@ -46,11 +52,13 @@ class PagedKVError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32)]
 
     def __repr__(self):
-        return "PoolDesc(num_blocks=%d, block_size=%d, num_kv_heads=%d, head_dim=%d, kv_dtype=%d)" % (
-            self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim, self.kv_dtype)
+        return ("PoolDesc(num_blocks=%d, block_size=%d, num_kv_heads=%d, head_dim=%d, "
+                "kv_dtype=%d, scale_mode=%d)" % (self.num_blocks, self.block_size,
+                                                 self.num_kv_heads, self.head_dim,
+                                                 self.kv_dtype, self.scale_mode))
 
 
 _lock = threading.Lock()
@@ -141,7 +149,7 @@ def dtype_code(t) -> int:
 def torch_dtype(code: int):
     torch = _torch()
     return {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16,
-            PKV_FP8_E4M3: torch.uint8}[code]
+            PKV_FP8_E4M3: torch.uint8, PKV_INT8: torch.int8}[code]
 
 
 def _ptr(t, name, device=True, allow_none=False):
@@ -169,9 +177,12 @@ def pkv_version() -> int:
     return int(lib().pkv_version())
 
 
-def pool_desc(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype) -> PoolDesc:
+def pool_desc(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype,
+              scale_mode=PKV_SCALE_BLOCK) -> PoolDesc:
     code = dtype_code(kv_dtype) if not isinstance(kv_dtype, int) else kv_dtype
-    return PoolDesc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim), code)
+    mode = SCALE_MODES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
+    return PoolDesc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim), code,
+                    mode)
 
 
 def pkv_pool_bytes(desc: PoolDesc):

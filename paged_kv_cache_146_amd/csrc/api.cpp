@@ -23,7 +23,19 @@ int elem_bytes(int dt) {
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3: return 1;
+    case PKV_INT8: return 1;
     default: return 0;
+  }
+}
+
+bool quantised(int dt) { return dt == PKV_FP8_E4M3 || dt == PKV_INT8; }
+
+// floats in one scale array of a quantised pool
+size_t scale_count(const pkv_pool_desc* d) {
+  switch (d->scale_mode) {
+    case PKV_SCALE_TENSOR: return 1;
+    case PKV_SCALE_TOKEN: return (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
+    default: return (size_t)d->num_blocks * d->num_kv_heads;
   }
 }
 
@@ -36,6 +48,9 @@ int check_desc(const pkv_pool_desc* d) {
   if (d->num_blocks < 1 || d->block_size < 1 || d->num_kv_heads < 1 || d->head_dim < 1)
     return PKV_EINVAL;
   if (elem_bytes(d->kv_dtype) == 0) return PKV_EINVAL;
+  if (quantised(d->kv_dtype) ? (d->scale_mode < PKV_SCALE_BLOCK || d->scale_mode > PKV_SCALE_TOKEN)
+                             : d->scale_mode != 0)
+    return PKV_EINVAL;
   if ((d->head_dim * elem_bytes(d->kv_dtype)) % 16 != 0) return PKV_EINVAL;
   if (!pow2(d->block_size) || d->block_size > 64) return PKV_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
@@ -91,9 +106,7 @@ int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
   if (k_bytes) *k_bytes = e;
   if (v_bytes) *v_bytes = e;
   if (scale_bytes_each)
-    *scale_bytes_each = pool->kv_dtype == PKV_FP8_E4M3
-                            ? (size_t)pool->num_blocks * pool->num_kv_heads * sizeof(float)
-                            : 0;
+    *scale_bytes_each = quantised(pool->kv_dtype) ? scale_count(pool) * sizeof(float) : 0;
   return PKV_OK;
 }
 
@@ -160,8 +173,8 @@ int check_write(int32_t num_tokens, const void* k, const void* v, int32_t src_dt
   if (!k || !v || !k_pool || !v_pool) return PKV_EINVAL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_EINVAL;
-  if (elem_bytes(src_dtype) == 0 || src_dtype == PKV_FP8_E4M3) return PKV_EINVAL;
-  if (pool->kv_dtype == PKV_FP8_E4M3) {
+  if (elem_bytes(src_dtype) == 0 || quantised(src_dtype)) return PKV_EINVAL;
+  if (quantised(pool->kv_dtype)) {
     if (!k_scale || !v_scale) return PKV_EINVAL;
   } else if (src_dtype != pool->kv_dtype) {
     return PKV_EINVAL;  // descriptor/dtype mismatch: no silent conversion
@@ -186,6 +199,7 @@ pkv::WriteLaunch write_launch(int32_t num_tokens, const void* k, const void* v, 
   p.num_kv_heads = pool->num_kv_heads;
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
+  p.scale_mode = pool->scale_mode;
   return p;
 }
 
@@ -239,10 +253,11 @@ int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc
   if (num_pairs > 0x7fffffff / 2) return PKV_EINVAL;
   if (!pairs || !k_pool || !v_pool || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_EINVAL;
-  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (quantised(pool->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
   rc = pkv::launch_copy_blocks(pairs, num_pairs, k_pool, v_pool, k_scale, v_scale,
                                pool->num_blocks, pool->block_size, pool->num_kv_heads,
-                               pool->head_dim, pool->kv_dtype, as_stream(stream));
+                               pool->head_dim, pool->kv_dtype, pool->scale_mode,
+                               as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }
 
@@ -291,7 +306,7 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PKV_EINVAL;
-  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (quantised(pool->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
   if (num_seqs > 65535 || pool->num_kv_heads > 65535) return PKV_EUNSUPPORTED;
 
   int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
@@ -312,6 +327,7 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   p.num_kv_heads = pool->num_kv_heads;
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
+  p.scale_mode = pool->scale_mode;
   p.block_size = pool->block_size;
   p.num_blocks = pool->num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
@@ -432,7 +448,9 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
     return PKV_EINVAL;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
   if (q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
-  if (pool->kv_dtype != PKV_BF16 && pool->kv_dtype != PKV_FP8_E4M3) return PKV_EUNSUPPORTED;
+  if (pool->kv_dtype != PKV_BF16 &&
+      !(pool->kv_dtype == PKV_FP8_E4M3 && pool->scale_mode == PKV_SCALE_BLOCK))
+    return PKV_EUNSUPPORTED;
   if (pool->head_dim != 128 && pool->head_dim != 64) return PKV_EUNSUPPORTED;
   if (pool->block_size < 16) return PKV_EUNSUPPORTED;  // a 16-token tile sits in one block
   {
@@ -444,7 +462,7 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
     return PKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PKV_EINVAL;
-  if (pool->kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (quantised(pool->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;
   int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
   if (cap > max_context_len) cap = max_context_len;

@@ -3,8 +3,9 @@
 // Method: "03 | PagedAttention and the KV-cache memory system", §3 (slot =
 // physical_id * B + position mod B, physical_id = block_table[position / B])
 // and §4.1 (the model runner scatters each new token's K/V to its slot; the
-// number of tokens written is the length of slot_mapping); §8.1 (fp8 pages
-// carry fp32 scales).  "KV Cache: capacity, layout, lifecycle", "Page-table
+// number of tokens written is the length of slot_mapping); §8.1 (quantised
+// pages: fp8 or int8 codes with fp32 scales, one per block and head, per
+// tensor, or per token and head).  "KV Cache: capacity, layout, lifecycle", "Page-table
 // addressing": the cases where the reference raises become padding (-1) here.
 //
 // The fused append computes each token's slot in the scatter itself (one launch
@@ -12,9 +13,10 @@
 // one (token, kv head) row.  In the K pool ([block][head][D/X][B][X]) the piece
 // lands as one 16-byte store; in the V pool ([block][head][D][B], tokens
 // contiguous per dim) its elements go to D-strided slots, one store each.  Bit
-// copies for f32/f16/bf16 pools; for fp8 pools the thread divides 16 source
-// elements by the page's scale (IEEE fp32 division) and encodes them as OCP
-// E4M3 (nearest, ties to even, saturating).
+// copies for f32/f16/bf16 pools; for quantised pools the thread divides 16
+// source elements by their scale (IEEE fp32 division) and encodes them as OCP
+// E4M3 (nearest, ties to even, saturating) or as symmetric int8 (nearest, ties
+// to even, clamped to +-127).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -108,13 +110,26 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
   }
 }
 
-// fp8 pools: 16 source elements of SRC type -> one 16-byte piece of E4M3 codes.
-template <int SRC>
-__global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
+// symmetric int8 code of y (already divided by the scale): nearest integer, ties to
+// even, saturated to [-127, 127]; NaN -> 0
+__device__ __forceinline__ uint32_t f32_to_i8(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(y == y ? (int)r : 0);
+}
+
+// index of the scale of (block, head, token offset) in the pool's scale mode
+__device__ __forceinline__ size_t scale_index(int mode, size_t page, long long off, int B) {
+  return mode == SCALE_TENSOR ? 0 : (mode == SCALE_TOKEN ? page * B + off : page);
+}
+
+// quantised pools: 16 source elements of SRC type -> one 16-byte piece of KVT codes
+// (E4M3 or int8), each divided by its scale first.
+template <int SRC, int KVT>
+__global__ __launch_bounds__(kWriteThreads) void kv_write_quant_kernel(
     const SlotSource ss, int num_tokens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int num_blocks, int B,
-    int Hkv, int D) {
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int scale_mode,
+    int num_blocks, int B, int Hkv, int D) {
   constexpr int SES = Elem<SRC>::bytes;
   const int NC = D / 16;
   const long long total = (long long)num_tokens * Hkv * NC;
@@ -129,7 +144,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
   const bool isv = blockIdx.y != 0;
   const uint8_t* src = (isv ? v : k) + (((size_t)i * Hkv + h) * D + (size_t)c * 16) * SES;
   const size_t page = (size_t)blk * Hkv + h;
-  const float scale = (isv ? v_scale : k_scale)[page];
+  const float scale = (isv ? v_scale : k_scale)[scale_index(scale_mode, page, off, B)];
 
   float x[16];
   const u32x4* sp = reinterpret_cast<const u32x4*>(src);
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const float y = __fdiv_rn(x[e], scale);
-    w[e >> 2] |= f32_to_e4m3(y) << (8 * (e & 3));
+    w[e >> 2] |= (KVT == DT_FP8 ? f32_to_e4m3(y) : f32_to_i8(y)) << (8 * (e & 3));
   }
   if (!isv) {
     const u32x4 packed = {w[0], w[1], w[2], w[3]};
@@ -160,7 +175,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_fp8_kernel(
 // scales of the block.
 __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
     const int32_t* __restrict__ pairs, int num_pairs, uint8_t* k_pool, uint8_t* v_pool,
-    float* k_scale, float* v_scale, int num_blocks, int Hkv, long long block_pieces) {
+    float* k_scale, float* v_scale, int num_blocks, int scales_per_block,
+    long long block_pieces) {
   const int pr = blockIdx.x;
   const int src = pairs[2 * pr], dst = pairs[2 * pr + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
@@ -172,22 +188,27 @@ __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
        i += (long long)gridDim.z * kWriteThreads)
     to[i] = from[i];
   float* sc = isv ? v_scale : k_scale;
-  if (sc && blockIdx.z == 0)
-    for (int h = threadIdx.x; h < Hkv; h += kWriteThreads)
-      sc[(size_t)dst * Hkv + h] = sc[(size_t)src * Hkv + h];
+  if (sc && blockIdx.z == 0)  // the block's scales: one per kv head, or per (head, token)
+    for (int i = threadIdx.x; i < scales_per_block; i += kWriteThreads)
+      sc[(size_t)dst * scales_per_block + i] = sc[(size_t)src * scales_per_block + i];
 }
 
 int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* v_pool,
                        float* k_scale, float* v_scale, int num_blocks, int block_size, int Hkv,
-                       int head_dim, int kv_dtype, hipStream_t st) {
+                       int head_dim, int kv_dtype, int scale_mode, hipStream_t st) {
   if (num_pairs == 0) return 0;
-  const int ES = kv_dtype == DT_F32 ? 4 : (kv_dtype == DT_FP8 ? 1 : 2);
+  const bool quant = kv_dtype == DT_FP8 || kv_dtype == DT_I8;
+  const int ES = kv_dtype == DT_F32 ? 4 : (quant ? 1 : 2);
+  // a per-tensor scale belongs to no block; the others move with their block
+  const int spb = !quant || scale_mode == SCALE_TENSOR
+                      ? 0
+                      : (scale_mode == SCALE_TOKEN ? Hkv * block_size : Hkv);
   const long long pieces = (long long)Hkv * head_dim * block_size * ES / 16;  // per pool
   const long long parts = (pieces + 4 * kWriteThreads - 1) / (4 * kWriteThreads);
   dim3 grid((unsigned)num_pairs, 2, (unsigned)(parts < 1 ? 1 : (parts > 64 ? 64 : parts)));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kWriteThreads), 0, st, pairs, num_pairs,
-                     (uint8_t*)k_pool, (uint8_t*)v_pool, kv_dtype == DT_FP8 ? k_scale : nullptr,
-                     kv_dtype == DT_FP8 ? v_scale : nullptr, num_blocks, Hkv, pieces);
+                     (uint8_t*)k_pool, (uint8_t*)v_pool, spb ? k_scale : nullptr,
+                     spb ? v_scale : nullptr, num_blocks, spb, pieces);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
@@ -203,7 +224,8 @@ int launch_slot_mapping(const int32_t* block_table, int num_seqs, int W, const i
 
 int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
   if (p.num_tokens == 0) return 0;
-  const int ES = p.kv_dtype == DT_F32 ? 4 : (p.kv_dtype == DT_FP8 ? 1 : 2);
+  const bool quant = p.kv_dtype == DT_FP8 || p.kv_dtype == DT_I8;
+  const int ES = p.kv_dtype == DT_F32 ? 4 : (quant ? 1 : 2);
   const long long pieces = (long long)p.num_tokens * p.num_kv_heads * (p.head_dim * ES / 16);
   const long long blocks = (pieces + kWriteThreads - 1) / kWriteThreads;
   if (blocks > 0x7fffffffLL) return -3;
@@ -220,6 +242,11 @@ int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
   const uint8_t* v = (const uint8_t*)p.v;
   uint8_t* kp = (uint8_t*)p.k_pool;
   uint8_t* vp = (uint8_t*)p.v_pool;
+  auto quant_launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kWriteThreads), 0, st, ss, p.num_tokens, k, v, kp, vp,
+                       p.k_scale, p.v_scale, p.scale_mode, p.num_blocks, p.block_size,
+                       p.num_kv_heads, p.head_dim);
+  };
   if (p.kv_dtype == DT_F32)
     hipLaunchKernelGGL(kv_write_copy_kernel<4>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
@@ -228,18 +255,18 @@ int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
     hipLaunchKernelGGL(kv_write_copy_kernel<2>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
                        p.head_dim);
-  else if (p.src_dtype == DT_BF16)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_BF16>, grid, dim3(kWriteThreads), 0, st, ss,
-                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
-                       p.block_size, p.num_kv_heads, p.head_dim);
-  else if (p.src_dtype == DT_F16)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F16>, grid, dim3(kWriteThreads), 0, st, ss,
-                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
-                       p.block_size, p.num_kv_heads, p.head_dim);
-  else if (p.src_dtype == DT_F32)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<DT_F32>, grid, dim3(kWriteThreads), 0, st, ss,
-                       p.num_tokens, k, v, kp, vp, p.k_scale, p.v_scale, p.num_blocks,
-                       p.block_size, p.num_kv_heads, p.head_dim);
+  else if (p.kv_dtype == DT_FP8 && p.src_dtype == DT_BF16)
+    quant_launch(kv_write_quant_kernel<DT_BF16, DT_FP8>);
+  else if (p.kv_dtype == DT_FP8 && p.src_dtype == DT_F16)
+    quant_launch(kv_write_quant_kernel<DT_F16, DT_FP8>);
+  else if (p.kv_dtype == DT_FP8 && p.src_dtype == DT_F32)
+    quant_launch(kv_write_quant_kernel<DT_F32, DT_FP8>);
+  else if (p.kv_dtype == DT_I8 && p.src_dtype == DT_BF16)
+    quant_launch(kv_write_quant_kernel<DT_BF16, DT_I8>);
+  else if (p.kv_dtype == DT_I8 && p.src_dtype == DT_F16)
+    quant_launch(kv_write_quant_kernel<DT_F16, DT_I8>);
+  else if (p.kv_dtype == DT_I8 && p.src_dtype == DT_F32)
+    quant_launch(kv_write_quant_kernel<DT_F32, DT_I8>);
   else
     return -3;
   return hipGetLastError() == hipSuccess ? 0 : -5;

@@ -72,6 +72,7 @@ struct DecodeScalars {
   int out_dtype;
   int num_workers;  // balanced kernel: wavefront workers in the grid
   uint32_t epoch;   // balanced kernel: call tag of the shared-pair counters
+  int scale_mode;   // quantised pools: SCALE_BLOCK / SCALE_TENSOR / SCALE_TOKEN
   float scale_log2; // softmax scale * log2(e)
 };
 
@@ -215,16 +216,40 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
   }
 }
 
-// fp8 page scales of the chunk's tiles
-__device__ __forceinline__ void page_scales(float (&ks)[4], float (&vs)[4],
-                                            const float* __restrict__ k_scale,
-                                            const float* __restrict__ v_scale, const Pages& pg,
-                                            int kvh, const DecodeScalars& sc) {
+// index of the scale of (page, token offset) in the pool's scale mode
+__device__ __forceinline__ size_t scale_at(const DecodeScalars& sc, size_t page, int off) {
+  return sc.scale_mode == SCALE_TENSOR ? 0
+                                       : (sc.scale_mode == SCALE_TOKEN ? (page << sc.blog2) + off
+                                                                       : page);
+}
+
+// scales of the lane's 16 keys of a quantised chunk (key 16 T + 4 g + r at slot
+// 4 T + r): one per page, one for the pool, or one per token (four consecutive
+// tokens of a page for each tile)
+__device__ __forceinline__ void chunk_scales(float (&ks)[16], float (&vs)[16],
+                                             const float* __restrict__ k_scale,
+                                             const float* __restrict__ v_scale, const Pages& pg,
+                                             int kvh, const DecodeScalars& sc, int g) {
+  const int B = 1 << sc.blog2;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
-    ks[T] = k_scale[page];
-    vs[T] = v_scale[page];
+    if (sc.scale_mode == SCALE_TOKEN) {
+      const size_t i0 = page * B + ((16 * T) & (B - 1)) + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ks[4 * T + r] = k_scale[i0 + r];
+        vs[4 * T + r] = v_scale[i0 + r];
+      }
+    } else {
+      const size_t i = sc.scale_mode == SCALE_TENSOR ? 0 : page;
+      const float a = k_scale[i], b = v_scale[i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ks[4 * T + r] = a;
+        vs[4 * T + r] = b;
+      }
+    }
   }
 }
 
@@ -259,9 +284,10 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
       const int i = 4 * T + e;  // the lane's score index of this token
       const int t = min(base + 16 * T + 4 * g + e, end - 1);
       const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
-      if constexpr (C::EB == 1) {
-        ks[i] = k_scale[page];
-        vs[i] = v_scale[page];
+      if constexpr (C::EB == 1) {  // quantised
+        const size_t si = scale_at(sc, page, t & (B - 1));
+        ks[i] = k_scale[si];
+        vs[i] = v_scale[si];
       } else {
         ks[i] = vs[i] = 1.0f;
       }
@@ -305,8 +331,9 @@ __device__ __forceinline__ void chunk_qk(f32x4 (&S)[4], const u32x4 (&kr)[C::NK]
       for (int h = 0; h < C::SPP; ++h) {
         if constexpr (C::F32)
           acc = mma_f32(as_f32(piece[h]), qop[pq * C::SPP + h], acc);
-        else if constexpr (KVT == DT_FP8)
-          acc = mma16<CT>(fp8x8<CT>(piece[2 * h], piece[2 * h + 1]), qop[pq * C::SPP + h], acc);
+        else if constexpr (C::EB == 1)
+          acc = mma16<CT>(widen8<KVT, CT>(piece[2 * h], piece[2 * h + 1]), qop[pq * C::SPP + h],
+                          acc);
         else
           acc = mma16<CT>(piece, qop[pq], acc);
       }
@@ -345,27 +372,34 @@ __device__ __forceinline__ void mask_v(typename C::VPiece (&vr)[C::NV], int nval
     }
 }
 
-// Scores x[4 T + r] belong to token 16 T + 4 g + r.  NS = scale values per lane:
-// 4 (one page per tile, block_size >= 16) or 16 (one per token).
-template <class C, int KVT, int CT, int NS>
+// Scores x[4 T + r] belong to token 16 T + 4 g + r, and so do the scales ks[4 T + r]
+// and vs[4 T + r] of a quantised pool.
+template <class C, int KVT, int CT>
 __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[4],
                                                  typename C::VPiece (&vr)[C::NV], float zscale,
-                                                 const float (&ks)[NS], const float (&vs)[NS],
+                                                 const float (&ks)[16], float (&vs)[16],
                                                  int nvalid, int g) {
-  constexpr bool kFp8 = (KVT == DT_FP8);
+  constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);  // quantised: scaled 8-bit codes
   float x[16];
 #pragma unroll
   for (int T = 0; T < 4; ++T)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * T + r;
-      x[i] = S[T][r] * (kFp8 ? zscale * ks[NS == 4 ? T : i] : zscale);
+      x[i] = S[T][r] * (kFp8 ? zscale * ks[i] : zscale);
     }
   if (nvalid < 64) {
+    // a key past the context gets weight 0; its V codes and its scale (read from a
+    // slot nothing wrote, or from a page past the table's live entries) may hold
+    // anything, NaN included, so both are cleared rather than multiplied by 0
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[4 * T + r] = 16 * T + 4 * g + r < nvalid ? x[4 * T + r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const bool live = 16 * T + 4 * g + r < nvalid;
+        x[4 * T + r] = live ? x[4 * T + r] : -INFINITY;
+        if constexpr (kFp8) vs[4 * T + r] = live ? vs[4 * T + r] : 0.0f;
+      }
     mask_v<C>(vr, nvalid, g);
   }
   float cm = x[0];
@@ -408,8 +442,8 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
         const int i0 = 8 * s2 + 2 * wd;
         float a = p[i0], b = p[i0 + 1];
         if constexpr (kFp8) {
-          a *= vs[NS == 4 ? (i0 >> 2) : i0];
-          b *= vs[NS == 4 ? (i0 >> 2) : i0 + 1];
+          a *= vs[i0];
+          b *= vs[i0 + 1];
         }
         wh[wd] = pack2<CT>(a, b);
         const f32x2 h = unpack2<CT>(wh[wd]);
@@ -425,7 +459,7 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
         // slots 0-3: tokens 32 s2 + 4 g + (0..3) (tile 2 s2); 4-7: tile 2 s2 + 1
         u32x4 a;
         if constexpr (kFp8) {
-          a = fp8x8<CT>(vr[dt * 4 + 2 * s2], vr[dt * 4 + 2 * s2 + 1]);
+          a = widen8<KVT, CT>(vr[dt * 4 + 2 * s2], vr[dt * 4 + 2 * s2 + 1]);
         } else {
           const u32x2 lo = vr[dt * 4 + 2 * s2], hi = vr[dt * 4 + 2 * s2 + 1];
           a = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -449,7 +483,7 @@ paged_decode_kernel(
     float* __restrict__ part_out, float* __restrict__ part_max, float* __restrict__ part_sum,
     const DecodeScalars sc) {
   using C = Cfg<KVT, CT, D>;
-  constexpr bool kFp8 = (KVT == DT_FP8);
+  constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);  // quantised: scaled 8-bit codes
 
   __shared__ float c_acc[kWaves][16][D];
   __shared__ float c_m[kWaves][16];
@@ -491,7 +525,7 @@ paged_decode_kernel(
       load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
-      chunk_softmax_pv<C, KVT, CT, 16>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g);
+      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g);
     }
   } else if (cnt > 0) {
     // Single-buffered pipeline: chunk i+1's K pieces are requested as soon as
@@ -500,11 +534,13 @@ paged_decode_kernel(
     // every wait on the in-order memory counter narrow (K(i) never waits for
     // V(i), and so on).
     Chunk<C> R;
-    float ks0[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vs0[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    float ks0[16], vs0[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ks0[i] = vs0[i] = 1.0f;
     {
       const Pages p0 = pages_of(trow, base_of(0), t_end, sc);
       issue_k<C>(R.k, k_pool, p0, kvh, sc, n, g);
-      if constexpr (kFp8) page_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc);
+      if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
       issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
     }
     Pages p1 = pages_of(trow, base_of(1), t_end, sc);
@@ -514,23 +550,26 @@ paged_decode_kernel(
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, R.k, qop);
       issue_point();
-      float ks1[4] = {1.0f, 1.0f, 1.0f, 1.0f}, vs1[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      float ks1[16], vs1[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ks1[k] = vs1[k] = 1.0f;
       Pages p2 = p1;
       if (more) {
         issue_k<C>(R.k, k_pool, p1, kvh, sc, n, g);
-        if constexpr (kFp8) page_scales(ks1, vs1, k_scale, v_scale, p1, kvh, sc);
+        if constexpr (kFp8) chunk_scales(ks1, vs1, k_scale, v_scale, p1, kvh, sc, g);
         p2 = pages_of(trow, base_of(i + 2), t_end, sc);
       }
       issue_point();
-      chunk_softmax_pv<C, KVT, CT, 4>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0), g);
+      chunk_softmax_pv<C, KVT, CT>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0),
+                                       g);
       issue_point();
       if (more) issue_v<C>(R.v, v_pool, p1, kvh, sc, n, g);
       issue_point();
       p1 = p2;
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        ks0[T] = ks1[T];
-        vs0[T] = vs1[T];
+      for (int k = 0; k < 16; ++k) {
+        ks0[k] = ks1[k];
+        vs0[k] = vs1[k];
       }
     }
   }
@@ -715,7 +754,7 @@ paged_decode_balanced_kernel(
     const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out, float* slot_out,
     float* slot_ml, unsigned long long* counters, const DecodeScalars sc) {
   using C = Cfg<KVT, CT, D>;
-  constexpr bool kFp8 = (KVT == DT_FP8);
+  constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);  // quantised: scaled 8-bit codes
 
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
@@ -877,7 +916,7 @@ paged_decode_balanced_kernel(
                     pc.kvh, sc, n, g);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
-      chunk_softmax_pv<C, KVT, CT, 16>(st, S, ch.v, sc.scale_log2, ks, vs,
+      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs,
                                        min(64, pc.ctx - 64 * pc.j), g);
       const bool done = pc.k + 1 >= n_units;
       if (done || piece_ends(pc)) {
@@ -902,16 +941,17 @@ paged_decode_balanced_kernel(
     constexpr int NB = C::NBUF;
     Chunk<C> R[NB];
     Pos pp[NB];          // pp[k]: position of the chunk k stages ahead of pc
-    float ksr[NB][4], vsr[NB][4];
+    float ksr[NB][16], vsr[NB][16];
 #pragma unroll
     for (int k = 0; k < NB; ++k)
 #pragma unroll
-      for (int T = 0; T < 4; ++T) ksr[k][T] = vsr[k][T] = 1.0f;
+      for (int i = 0; i < 16; ++i) ksr[k][i] = vsr[k][i] = 1.0f;
     pp[0] = pc;
-    auto issue = [&](Chunk<C>& dst, const Pos& p, const Pages& pg, float (&ks)[4], float (&vs)[4]) {
+    auto issue = [&](Chunk<C>& dst, const Pos& p, const Pages& pg, float (&ks)[16],
+                     float (&vs)[16]) {
       issue_k<C>(dst.k, k_pool, pg, p.kvh, sc, n, g);
       issue_v<C>(dst.v, v_pool, pg, p.kvh, sc, n, g);
-      if constexpr (kFp8) page_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc);
+      if constexpr (kFp8) chunk_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc, g);
     };
     auto pages_at = [&](const Pos& p) { return pages_of(trow_of(p), 64 * p.j, p.ctx, sc); };
 #pragma unroll
@@ -946,8 +986,8 @@ paged_decode_balanced_kernel(
       const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
       if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
       issue_point();
-      chunk_softmax_pv<C, KVT, CT, 4>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
-                                      min(64, p0.ctx - 64 * p0.j), g);
+      chunk_softmax_pv<C, KVT, CT>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
+                                       min(64, p0.ctx - 64 * p0.j), g);
       issue_point();
       if (last || piece_ends(p0)) {
         finish_piece(p0);
@@ -1104,6 +1144,7 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
   sc.out_dtype = p.q_dtype;
   sc.num_workers = p.num_workers;
   sc.epoch = p.epoch;
+  sc.scale_mode = p.scale_mode;
   sc.scale_log2 = p.scale * kLog2e;
   if (sc.blog2 < 0 || p.block_size > 64 || sc.G > 16) return -3;
   const int kv = p.kv_dtype, qd = p.q_dtype;
@@ -1112,6 +1153,8 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
   if (kv == DT_BF16 && qd == DT_BF16) return pick_d<DT_BF16, DT_BF16>(p, sc, st);
   if (kv == DT_FP8 && qd == DT_BF16) return pick_d<DT_FP8, DT_BF16>(p, sc, st);
   if (kv == DT_FP8 && qd == DT_F16) return pick_d<DT_FP8, DT_F16>(p, sc, st);
+  if (kv == DT_I8 && qd == DT_BF16) return pick_d<DT_I8, DT_BF16>(p, sc, st);
+  if (kv == DT_I8 && qd == DT_F16) return pick_d<DT_I8, DT_F16>(p, sc, st);
   return -3;
 }
 
@@ -1160,6 +1203,8 @@ int balanced_worker_capacity(int kv, int qd, int D, int block_size) {
   if (kv == DT_F32) n = bpc<DT_F32, DT_F32>(D, block_size);
   else if (kv == DT_F16) n = bpc<DT_F16, DT_F16>(D, block_size);
   else if (kv == DT_BF16) n = bpc<DT_BF16, DT_BF16>(D, block_size);
+  else if (kv == DT_I8) n = qd == DT_F16 ? bpc<DT_I8, DT_F16>(D, block_size)
+                                         : bpc<DT_I8, DT_BF16>(D, block_size);
   else if (qd == DT_F16) n = bpc<DT_FP8, DT_F16>(D, block_size);
   else n = bpc<DT_FP8, DT_BF16>(D, block_size);
   return device_cus() * n * kWaves;

@@ -10,7 +10,9 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3, DT_I8 = 4 };
+// where a quantised element's scale lives (the C ABI's pkv_scale_mode)
+enum : int { SCALE_BLOCK = 0, SCALE_TENSOR = 1, SCALE_TOKEN = 2 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -25,6 +27,7 @@ template <> struct Elem<DT_F32> { static constexpr int bytes = 4, per16 = 4; };
 template <> struct Elem<DT_F16> { static constexpr int bytes = 2, per16 = 8; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2, per16 = 8; };
 template <> struct Elem<DT_FP8> { static constexpr int bytes = 1, per16 = 16; };
+template <> struct Elem<DT_I8> { static constexpr int bytes = 1, per16 = 16; };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

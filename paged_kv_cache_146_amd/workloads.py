@@ -22,8 +22,12 @@ from typing import Optional
 
 import numpy as np
 
-STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+           "int8": np.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
+QUANTISED = ("fp8", "int8")
+# the largest magnitude of each quantised type (E4M3: 448; symmetric int8: 127)
+QMAX = {"fp8": 448.0, "int8": 127.0}
 NAN_BITS = {"f32": np.array(0x7FC00000, np.uint32).view(np.float32), "f16": 0x7E00,
             "bf16": 0x7FC0, "fp8": 0x7F}
 
@@ -73,8 +77,9 @@ class Workload:
     src_dtype: str
     scale: float                      # softmax scale (fp32 value of 1/sqrt(D))
     pad_block: int                    # block id used for table entries past the live length
-    k_scale: Optional[np.ndarray] = None   # fp8 only: float32 [num_blocks][Hkv]
+    k_scale: Optional[np.ndarray] = None   # quantised pools: float32, shape per scale_mode
     v_scale: Optional[np.ndarray] = None
+    scale_mode: str = "block"             # "block" [nb][Hkv], "tensor" [1], "token" [nb][Hkv][B]
     cu_seqlens_q: Optional[np.ndarray] = None  # prefill only: int32 [S+1]
     partition_size: int = 0
     shared_blocks: int = 0
@@ -104,12 +109,20 @@ class Workload:
         return idx
 
     def kv_bytes(self) -> int:
-        """Bytes of K and V that decode reads: sum(ctx) * 2 * Hkv * D * elem (+ fp8 scales)."""
+        """Bytes of K and V that decode reads: sum(ctx) * 2 * Hkv * D * elem, plus the scales
+        of a quantised pool (one per live block and head, one per token and head, or 2 x 4
+        bytes for the whole pool)."""
         e = ELEM_BYTES[self.kv_dtype]
-        tot = int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * e
-        if self.kv_dtype == "fp8":
-            nblk = sum(math.ceil(int(c) / self.block_size) for c in self.context_lens)
-            tot += nblk * 2 * self.num_kv_heads * 4
+        ntok = int(self.context_lens.astype(np.int64).sum())
+        tot = ntok * 2 * self.num_kv_heads * self.head_dim * e
+        if self.kv_dtype in QUANTISED:
+            if self.scale_mode == "block":
+                nblk = sum(math.ceil(int(c) / self.block_size) for c in self.context_lens)
+                tot += nblk * 2 * self.num_kv_heads * 4
+            elif self.scale_mode == "token":
+                tot += ntok * 2 * self.num_kv_heads * 4
+            else:
+                tot += 2 * 4
         return tot
 
 
@@ -151,7 +164,7 @@ def _draw_kv(rng, T, Hkv, D, dtype, chunk=1 << 24):
 
 def make_decode(name, seed, ctx_lens=None, ctx_range=None, num_seqs=None, Hq=4, Hkv=2, D=64,
                 B=4, kv_dtype="f32", q_dtype=None, spare_frac=0.0, shared_prefix=0,
-                tail_range=None, partition_size=0, fp8_src_dtype="bf16"):
+                tail_range=None, partition_size=0, fp8_src_dtype="bf16", scale_mode="block"):
     """Generic decode workload.  ctx from an explicit list, from U[lo, hi] (inclusive), or
     as shared_prefix + U[tail_range] tails."""
     rng = np.random.default_rng(seed)
@@ -180,14 +193,14 @@ def make_decode(name, seed, ctx_lens=None, ctx_range=None, num_seqs=None, Hq=4, 
         fp.append(np.arange(start, int(ctx[s]), dtype=np.int32))
     fill_seq = np.concatenate(fs) if fs else np.zeros(0, np.int32)
     fill_pos = np.concatenate(fp) if fp else np.zeros(0, np.int32)
-    src_dtype = fp8_src_dtype if kv_dtype == "fp8" else kv_dtype
+    src_dtype = fp8_src_dtype if kv_dtype in QUANTISED else kv_dtype
     k_src, v_src = _draw_kv(rng, len(fill_seq), Hkv, D, src_dtype)
     wl = Workload(name, S, Hq, Hkv, D, B, kv_dtype, q_dtype, num_blocks, ctx, table, q,
                   fill_seq, fill_pos, k_src, v_src, src_dtype,
-                  float(np.float32(1.0 / math.sqrt(D))), pad,
+                  float(np.float32(1.0 / math.sqrt(D))), pad, scale_mode=scale_mode,
                   partition_size=partition_size, shared_blocks=shared_blocks)
-    if kv_dtype == "fp8":
-        wl.k_scale, wl.v_scale = block_scales(wl)
+    if kv_dtype in QUANTISED:
+        wl.k_scale, wl.v_scale = amax_scales(wl)
     return wl
 
 
@@ -204,32 +217,46 @@ def make_prefill(name, seed, num_seqs, cached, new, Hq, Hkv, D, B, kv_dtype="fp8
     q = to_storage(rng.standard_normal((total_q, Hq, D), dtype=np.float32), q_dtype)
     fill_seq = np.concatenate([np.full(int(c), s, np.int32) for s, c in enumerate(ctx)])
     fill_pos = np.concatenate([np.arange(int(c), dtype=np.int32) for c in ctx])
-    src_dtype = fp8_src_dtype if kv_dtype == "fp8" else kv_dtype
+    src_dtype = fp8_src_dtype if kv_dtype in QUANTISED else kv_dtype
     k_src, v_src = _draw_kv(rng, len(fill_seq), Hkv, D, src_dtype)
     cu = np.zeros(num_seqs + 1, np.int32)
     cu[1:] = np.cumsum(new)
     wl = Workload(name, num_seqs, Hq, Hkv, D, B, kv_dtype, q_dtype, num_blocks, ctx, table, q,
                   fill_seq, fill_pos, k_src, v_src, src_dtype,
                   float(np.float32(1.0 / math.sqrt(D))), pad, cu_seqlens_q=cu)
-    if kv_dtype == "fp8":
-        wl.k_scale, wl.v_scale = block_scales(wl)
+    if kv_dtype in QUANTISED:
+        wl.k_scale, wl.v_scale = amax_scales(wl)
     return wl
 
 
-def block_scales(wl: Workload):
-    """Per (block, kv head) fp32 scales for an fp8 pool: max(amax of the values stored in
-    that block for that head, 2^-20) / 448, separately for K and V (1.0 for unused blocks).
-    This is a property of the input, not of the method: any positive scale is valid."""
+def amax_scales(wl: Workload):
+    """fp32 scales of a quantised pool, K and V separately: max(amax, 2^-20) / QMAX over the
+    values that share the scale in the workload's scale_mode (a block and head, the whole
+    pool, or one token and head).  Unused blocks get 1.0; in token mode a slot no token
+    is written to gets NaN, so that a kernel that reads the scale of a key past the
+    context shows it.  This is a property of the input, not of the method: any positive
+    scale is valid."""
+    qmax = np.float32(QMAX[wl.kv_dtype])
+    floor = np.float32(2.0 ** -20)
+    B, H = wl.block_size, wl.num_kv_heads
+    phys = wl.block_table[wl.fill_seq, wl.fill_pos // B]
+    off = wl.fill_pos % B
     scales = []
-    phys = wl.block_table[wl.fill_seq, wl.fill_pos // wl.block_size]
     for src in (wl.k_src, wl.v_src):
         vals = np.abs(storage_to_f32(src, wl.src_dtype)).max(axis=2)  # [T][Hkv]
-        amax = np.zeros((wl.num_blocks, wl.num_kv_heads), np.float32)
-        np.maximum.at(amax, phys, vals)
-        sc = (np.maximum(amax, np.float32(2.0 ** -20)) / np.float32(448.0)).astype(np.float32)
-        used = np.zeros(wl.num_blocks, bool)
-        used[phys] = True
-        sc[~used] = 1.0
+        if wl.scale_mode == "tensor":
+            amax = np.float32(vals.max()) if vals.size else np.float32(0)
+            sc = np.array([np.maximum(amax, floor) / qmax], np.float32)
+        elif wl.scale_mode == "token":
+            sc = np.full((wl.num_blocks, H, B), np.nan, np.float32)
+            sc[phys, :, off] = (np.maximum(vals, floor) / qmax).astype(np.float32)
+        else:
+            amax = np.zeros((wl.num_blocks, H), np.float32)
+            np.maximum.at(amax, phys, vals)
+            sc = (np.maximum(amax, floor) / qmax).astype(np.float32)
+            used = np.zeros(wl.num_blocks, bool)
+            used[phys] = True
+            sc[~used] = 1.0
         scales.append(sc)
     return scales[0], scales[1]
 
@@ -255,16 +282,22 @@ def tiny_decode(seed=1):
                     fill_pos, k_src, v_src, "f32", float(np.float32(1.0 / 8.0)), int(perm[5]))
 
 
-def llama3_8b_decode(seed=2, small=False, partition_size=512):
+def llama3_8b_decode(seed=2, small=False, partition_size=512, kv_dtype="bf16",
+                     scale_mode="block"):
     """64 sequences, ctx U[128, 4096], H_q 32, H_kv 8, D 128, B 16, bf16, pool = needed
-    blocks + 20% spare, shuffled tables."""
+    blocks + 20% spare, shuffled tables.  A quantised kv_dtype ("fp8", "int8") stores the
+    same bf16 draws as codes with scales in `scale_mode`; q stays bf16."""
+    kv = kv_dtype if kv_dtype == "bf16" else "%s, %s scales" % (kv_dtype, scale_mode)
     if small:
-        return make_decode("llama3-8b-shaped decode (small: S=6, ctx U[1,1200])", seed,
+        return make_decode("llama3-8b-shaped decode (small: S=6, ctx U[1,1200], %s)" % kv, seed,
                            ctx_range=(1, 1200), num_seqs=6, Hq=32, Hkv=8, D=128, B=16,
-                           kv_dtype="bf16", spare_frac=0.2, partition_size=partition_size)
-    return make_decode("llama3-8b-shaped decode (S=64, ctx U[128,4096], Hq32 Hkv8 D128 B16 bf16)",
+                           kv_dtype=kv_dtype, q_dtype="bf16", spare_frac=0.2,
+                           partition_size=partition_size, scale_mode=scale_mode)
+    return make_decode("llama3-8b-shaped decode (S=64, ctx U[128,4096], Hq32 Hkv8 D128 B16 %s)"
+                       % kv,
                        seed, ctx_range=(128, 4096), num_seqs=64, Hq=32, Hkv=8, D=128, B=16,
-                       kv_dtype="bf16", spare_frac=0.2, partition_size=partition_size)
+                       kv_dtype=kv_dtype, q_dtype="bf16", spare_frac=0.2,
+                       partition_size=partition_size, scale_mode=scale_mode)
 
 
 def long_context_decode(seed=3, small=False):

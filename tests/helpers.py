@@ -11,7 +11,7 @@ import oracle
 from paged_kv_cache_146_amd.workloads import STORAGE, Workload
 
 ATOL, RTOL = 2e-3, 1e-2  # |gpu - oracle| <= ATOL + RTOL * |oracle|, element-wise
-ES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+ES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 def torch_bits(a: np.ndarray, dtype: str, device="cuda"):
@@ -66,7 +66,7 @@ class GpuCase:
         import paged_kv_cache_146_amd as pkv
         self.wl = wl
         self.desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
-                                  wl.kv_dtype)
+                                  wl.kv_dtype, wl.scale_mode)
         self.k_pool, self.v_pool = pkv.alloc_pool(self.desc, fill_byte=fill_byte)
         self.k_scale = torch.from_numpy(wl.k_scale).cuda() if wl.k_scale is not None else None
         self.v_scale = torch.from_numpy(wl.v_scale).cuda() if wl.v_scale is not None else None
@@ -129,7 +129,8 @@ class GpuCase:
 
 def oracle_pool(wl: Workload) -> oracle.Pool:
     """The oracle's own pool for the workload, filled by the oracle's write path."""
-    pool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    pool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                       scale_mode=wl.scale_mode)
     pool.k.view(np.uint8)[...] = 0xFF
     pool.v.view(np.uint8)[...] = 0xFF
     pool.k_scale, pool.v_scale = wl.k_scale, wl.v_scale

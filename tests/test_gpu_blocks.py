@@ -22,24 +22,30 @@ def _pkv():
     return pkv
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_copy_blocks_bit_exact(kv):
+@pytest.mark.parametrize("kv,mode", [("bf16", "block"), ("fp8", "block"), ("int8", "token"),
+                                     ("fp8", "tensor")])
+def test_copy_blocks_bit_exact(kv, mode):
     import torch
     pkv = _pkv()
     NB, B, H, D = 24, 16, 4, 128
-    desc = pkv.pool_desc(NB, B, H, D, kv)
+    desc = pkv.pool_desc(NB, B, H, D, kv, mode)
     kp, vp = pkv.alloc_pool(desc)
     g = torch.Generator(device="cuda").manual_seed(5)
     kp.copy_(torch.randint(0, 256, kp.shape, dtype=torch.uint8, device="cuda", generator=g))
     vp.copy_(torch.randint(0, 256, vp.shape, dtype=torch.uint8, device="cuda", generator=g))
-    ks = torch.rand((NB, H), device="cuda", generator=g) if kv == "fp8" else None
-    vs = torch.rand((NB, H), device="cuda", generator=g) if kv == "fp8" else None
+    shape = {"block": (NB, H), "tensor": (1,), "token": (NB, H, B)}[mode]
+    quant = kv in ("fp8", "int8")
+    ks = torch.rand(shape, device="cuda", generator=g) if quant else None
+    vs = torch.rand(shape, device="cuda", generator=g) if quant else None
     pairs = [(3, 10), (5, 11), (7, 7), (-1, 2), (4, NB), (20, 0)]
     want_k = kp.cpu().numpy().reshape(NB, -1).copy()
     want_v = vp.cpu().numpy().reshape(NB, -1).copy()
     want_ks = ks.cpu().numpy().copy() if ks is not None else None
     want_vs = vs.cpu().numpy().copy() if vs is not None else None
-    oracle.copy_blocks(want_k, want_v, want_ks, want_vs, pairs)
+    # one scale for the whole pool belongs to no block: it is left as it is
+    per_block = quant and mode != "tensor"
+    oracle.copy_blocks(want_k, want_v, want_ks if per_block else None,
+                       want_vs if per_block else None, pairs)
     pkv.pkv_copy_blocks(torch.tensor(pairs, dtype=torch.int32, device="cuda"), desc, kp, vp,
                         ks, vs)
     assert np.array_equal(kp.cpu().numpy().reshape(NB, -1), want_k)

@@ -84,6 +84,25 @@ def test_fp8_q_f16():
     print(_run(wl, [0, 128, -1]))
 
 
+@pytest.mark.parametrize("kv,mode,B,Hq,Hkv,D,q_dtype", [
+    ("int8", "block", 16, 8, 2, 128, "bf16"), ("int8", "token", 16, 8, 2, 128, "bf16"),
+    ("int8", "tensor", 32, 16, 2, 64, "f16"), ("int8", "token", 4, 8, 2, 128, "bf16"),
+    ("int8", "block", 1, 6, 2, 64, "bf16"), ("fp8", "token", 16, 8, 2, 128, "bf16"),
+    ("fp8", "tensor", 16, 12, 4, 128, "bf16"), ("fp8", "token", 8, 3, 3, 64, "f16"),
+    ("int8", "token", 64, 32, 8, 128, "f16")])
+def test_quantised_scale_modes(kv, mode, B, Hq, Hkv, D, q_dtype):
+    """fp8 and int8 pools with one scale per (block, head), per pool, or per (token, head).
+    In token mode every scale slot that no token was written to holds NaN, so a kernel
+    that lets the scale of a key past the context reach the output fails."""
+    ctx = sorted({0, 1, max(B - 1, 1), B, B + 1, 63, 64, 65, 200, 517})
+    wl = W.make_decode("quant %s/%s B%d" % (kv, mode, B), 13 * B + Hq + len(mode), ctx_lens=ctx,
+                       Hq=Hq, Hkv=Hkv, D=D, B=B, kv_dtype=kv, q_dtype=q_dtype,
+                       fp8_src_dtype=q_dtype, spare_frac=0.2, scale_mode=mode)
+    if mode == "token":
+        assert np.isnan(wl.v_scale).any()
+    print(_run(wl, [0, 128, -1]))
+
+
 def test_permutation_invariance_bitwise():
     """Relabelling physical ids (pool'[pi(b)] = pool[b], table' = pi(table)) leaves the GPU
     output bitwise unchanged (same partitioning)."""

@@ -47,36 +47,61 @@ def test_slot_mapping_random_vs_oracle():
     assert (want >= 0).sum() > T // 2 and (want < 0).sum() > 100
 
 
-@pytest.mark.parametrize("kv,src,D,B,H", [
-    ("f32", "f32", 64, 4, 2), ("f16", "f16", 128, 32, 4), ("bf16", "bf16", 128, 16, 8),
-    ("bf16", "bf16", 64, 1, 3), ("fp8", "bf16", 128, 16, 8), ("fp8", "f16", 64, 8, 2),
-    ("fp8", "f32", 128, 64, 1)])
-def test_kv_cache_write_bit_exact(kv, src, D, B, H):
+def _scale_per_slot(scale, mode, slots, H, B):
+    """[T][H] scale that each (slot, head) is quantised with (slots >= 0)."""
+    if mode == "tensor":
+        return np.broadcast_to(scale[0], (len(slots), H))
+    if mode == "token":
+        return scale[slots // B, :, slots % B]
+    return scale[slots // B]
+
+
+@pytest.mark.parametrize("kv,src,D,B,H,mode", [
+    ("f32", "f32", 64, 4, 2, "block"), ("f16", "f16", 128, 32, 4, "block"),
+    ("bf16", "bf16", 128, 16, 8, "block"), ("bf16", "bf16", 64, 1, 3, "block"),
+    ("fp8", "bf16", 128, 16, 8, "block"), ("fp8", "f16", 64, 8, 2, "block"),
+    ("fp8", "f32", 128, 64, 1, "block"), ("fp8", "bf16", 128, 16, 8, "token"),
+    ("fp8", "f16", 64, 32, 2, "tensor"), ("int8", "bf16", 128, 16, 8, "token"),
+    ("int8", "f16", 64, 8, 2, "block"), ("int8", "f32", 128, 64, 1, "tensor"),
+    ("int8", "bf16", 64, 1, 3, "token")])
+def test_kv_cache_write_bit_exact(kv, src, D, B, H, mode):
     import torch
     pkv = _pkv()
-    rng = np.random.default_rng([D, B, H, ord(kv[-1]), ord(src[-1]), len(kv) + len(src)])
+    rng = np.random.default_rng([D, B, H, ord(kv[-1]), ord(src[-1]), len(kv) + len(src),
+                                 len(mode)])
     NB = 41
     T = 300
     slots = rng.permutation(NB * B)[:T].astype(np.int64)
     slots[::17] = -1                      # padding
     slots[5] = NB * B + 3                 # outside the pool: skipped
     x = rng.standard_normal((2, T, H, D)).astype(np.float32)
-    if kv == "fp8":
+    quant = kv in ("fp8", "int8")
+    if quant:
         # a wide dynamic range reaches saturation, subnormals and ties
         x *= np.exp2(rng.integers(-14, 10, size=(2, T, H, 1))).astype(np.float32)
-    k = to_storage(x[0], src)
-    v = to_storage(x[1], src)
-    pool = oracle.Pool(NB, B, H, D, kv)
+    pool = oracle.Pool(NB, B, H, D, kv, scale_mode=mode)
     pool.k.view(np.uint8)[...] = 0xFF
     pool.v.view(np.uint8)[...] = 0xFF
     ks = vs = None
-    if kv == "fp8":
-        pool.k_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
-        pool.v_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
+    if quant:
+        if kv == "int8":
+            # powers of two, and a third of the tokens on odd multiples of half the
+            # smallest one: many quotients are exact ties of the rounding
+            pool.k_scale = np.exp2(rng.integers(-6, -1, size=pool.scale_shape())).astype(np.float32)
+            pool.v_scale = np.exp2(rng.integers(-6, -1, size=pool.scale_shape())).astype(np.float32)
+            pool.k_scale.reshape(-1)[::2] = 2.0 ** -6
+            pool.v_scale.reshape(-1)[::2] = 2.0 ** -6
+            x[:, ::3] = ((rng.integers(-120, 120, size=x[:, ::3].shape) + 0.5)
+                         * 2.0 ** -6).astype(np.float32)
+        else:
+            pool.k_scale = rng.uniform(0.001, 0.1, size=pool.scale_shape()).astype(np.float32)
+            pool.v_scale = rng.uniform(0.001, 0.1, size=pool.scale_shape()).astype(np.float32)
         ks = torch.from_numpy(pool.k_scale).cuda()
         vs = torch.from_numpy(pool.v_scale).cuda()
+    k = to_storage(x[0], src)
+    v = to_storage(x[1], src)
     oracle.kv_cache_write(pool, slots, k, v, src)
-    desc = pkv.pool_desc(NB, B, H, D, kv)
+    desc = pkv.pool_desc(NB, B, H, D, kv, mode)
     kp, vp = pkv.alloc_pool(desc, fill_byte=0xFF)
     pkv.pkv_kv_cache_write(torch.from_numpy(slots).cuda(), torch_bits(k, src), torch_bits(v, src),
                            desc, kp, vp, ks, vs, src_dtype=src)
@@ -88,6 +113,13 @@ def test_kv_cache_write_bit_exact(kv, src, D, B, H):
         codes = pool.k.reshape(-1)
         assert (codes & 0x7F == 0x7E).any(), "saturation not exercised"
         assert ((codes & 0x78) == 0).sum() > 10, "subnormals not exercised"
+    if kv == "int8":
+        codes = pool.k.view(np.int8).reshape(-1)
+        assert (np.abs(codes.astype(np.int32)) == 127).sum() > 10, "saturation not exercised"
+        live = (slots >= 0) & (slots < NB * B)
+        sc = _scale_per_slot(pool.k_scale, mode, slots[live], H, B)[:, :, None]
+        quot = np.abs(x[0][:len(slots)][live] / sc)
+        assert ((quot - np.floor(quot) == 0.5) & (quot < 127)).sum() > 100, "ties not exercised"
 
 
 def test_write_zero_tokens_is_a_no_op():
@@ -102,9 +134,11 @@ def test_write_zero_tokens_is_a_no_op():
     assert (kp == 0x5A).all() and (vp == 0x5A).all()
 
 
-@pytest.mark.parametrize("kv,src,D,B,H", [("bf16", "bf16", 128, 16, 8), ("fp8", "bf16", 128, 16, 8),
-                                          ("f16", "f16", 64, 32, 2), ("fp8", "f32", 64, 64, 3)])
-def test_kv_cache_append_bit_exact(kv, src, D, B, H):
+@pytest.mark.parametrize("kv,src,D,B,H,mode", [
+    ("bf16", "bf16", 128, 16, 8, "block"), ("fp8", "bf16", 128, 16, 8, "block"),
+    ("f16", "f16", 64, 32, 2, "block"), ("fp8", "f32", 64, 64, 3, "block"),
+    ("int8", "bf16", 128, 16, 8, "token"), ("fp8", "f16", 64, 8, 2, "tensor")])
+def test_kv_cache_append_bit_exact(kv, src, D, B, H, mode):
     # the fused append against the oracle's slot mapping followed by its scatter; the
     # table is a permutation of the pool with holes, the tokens distinct (sequence,
     # position) pairs plus padding cases (bad sequence, negative position, position past
@@ -127,17 +161,17 @@ def test_kv_cache_append_bit_exact(kv, src, D, B, H):
     x = rng.standard_normal((2, T, H, D)).astype(np.float32)
     k = to_storage(x[0], src)
     v = to_storage(x[1], src)
-    pool = oracle.Pool(NB, B, H, D, kv)
+    pool = oracle.Pool(NB, B, H, D, kv, scale_mode=mode)
     pool.k.view(np.uint8)[...] = 0xFF
     pool.v.view(np.uint8)[...] = 0xFF
     ks = vs = None
-    if kv == "fp8":
-        pool.k_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
-        pool.v_scale = rng.uniform(0.001, 0.1, size=(NB, H)).astype(np.float32)
+    if kv in ("fp8", "int8"):
+        pool.k_scale = rng.uniform(0.001, 0.1, size=pool.scale_shape()).astype(np.float32)
+        pool.v_scale = rng.uniform(0.001, 0.1, size=pool.scale_shape()).astype(np.float32)
         ks = torch.from_numpy(pool.k_scale).cuda()
         vs = torch.from_numpy(pool.v_scale).cuda()
     oracle.kv_cache_write(pool, want_slots, k, v, src)
-    desc = pkv.pool_desc(NB, B, H, D, kv)
+    desc = pkv.pool_desc(NB, B, H, D, kv, mode)
     kp, vp = pkv.alloc_pool(desc, fill_byte=0xFF)
     slots_out = torch.full((T,), -7, dtype=torch.int64, device="cuda")
     pkv.pkv_kv_cache_append(torch.from_numpy(bt).cuda(), torch.from_numpy(seq).cuda(),

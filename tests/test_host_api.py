@@ -86,12 +86,21 @@ def test_pool_bytes_is_page_size_rule():
         k, v, s = pkv.pkv_pool_bytes(pkv.pool_desc(nb, B, H, D, dt))
         assert k == v == nb * B * H * D * e
         assert s == (nb * H * 4 if dt == "fp8" else 0)
+    # a quantised pool's scale array, per placement: [nb][H], [1], [nb][H][B] fp32
+    for dt in ("fp8", "int8"):
+        for mode, n in (("block", 10 * 8), ("tensor", 1), ("token", 10 * 8 * 16)):
+            k, v, s = pkv.pkv_pool_bytes(pkv.pool_desc(10, 16, 8, 128, dt, mode))
+            assert k == v == 10 * 16 * 8 * 128
+            assert s == 4 * n
 
 
 @pytest.mark.parametrize("desc,status", [
     ((0, 16, 8, 128, 2), -1), ((10, 0, 8, 128, 2), -1), ((10, 16, 0, 128, 2), -1),
     ((10, 16, 8, 128, 9), -1), ((10, 24, 8, 128, 2), -3), ((10, 128, 8, 128, 2), -3),
-    ((10, 16, 8, 96, 2), -3), ((10, 16, 8, 2, 0), -1)])
+    ((10, 16, 8, 96, 2), -3), ((10, 16, 8, 2, 0), -1),
+    # a scale placement only for quantised pools, and only the three defined ones
+    ((10, 16, 8, 128, 2, 1), -1), ((10, 16, 8, 128, 3, 3), -1), ((10, 16, 8, 128, 4, -1), -1),
+    ((10, 16, 8, 128, 5, 0), -1)])
 def test_pool_descriptor_validation(desc, status):
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.pkv_pool_bytes(pkv.PoolDesc(*desc))
@@ -188,6 +197,11 @@ def test_write_and_prefill_argument_errors_caught_on_host():
                                None, None, 8, None, 64, 0.1, 1, None, None) == -3  # G = 3
     assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 256, ctypes.byref(desc), None, None, None,
                                None, None, 8, None, 64, 0.1, 1, None, None) == -3  # G = 32
+    # the prefill kernel reads bf16 pools and fp8 pools with one scale per (block, head)
+    for dt, mode in (("int8", "block"), ("fp8", "token"), ("fp8", "tensor")):
+        qd = pkv.pool_desc(10, 16, 8, 128, dt, mode)
+        assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 32, ctypes.byref(qd), None, None,
+                                   None, None, None, 8, None, 64, 0.1, 1, None, None) == -3
     d64 = pkv.pool_desc(10, 16, 8, 64, "fp8")
     assert L.pkv_paged_prefill(None, 2, None, 1, 0, 1, 32, ctypes.byref(d64), None, None, None,
                                None, None, 8, None, 64, 0.1, 1, None, None) == 0  # nothing to do
