@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
-    ap.add_argument("--workload", choices=["decode", "prefill", "copy"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "copy", "shared-prefix"],
+                    default="decode")
     ap.add_argument("--kv", choices=["bf16", "fp8", "int8"], default="bf16",
                     help="decode workload: pool element type (quantised pools store the "
                          "same bf16 draws as codes with fp32 scales)")
@@ -118,6 +119,9 @@ def main():
         return
     if a.gpus == 1 and a.workload == "copy":
         copy_main(a)
+        return
+    if a.gpus == 1 and a.workload == "shared-prefix":
+        shared_main(a)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -457,6 +461,164 @@ def copy_main(a):
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_copy(pairs_np, block_bytes)
     print(json.dumps(res), flush=True)
+
+
+def shared_bytes(wl, shared_len) -> int:
+    """Algorithmic bytes of one shared-prefix decode: the prefix's K/V once, every
+    sequence's own K/V once, q and out, the used table entries and the lengths."""
+    e = W_ELEM[wl.kv_dtype]
+    row = 2 * wl.num_kv_heads * wl.head_dim * e
+    ctx = wl.context_lens.astype(np.int64)
+    own = int(np.maximum(ctx - shared_len, 0).sum())
+    nblk = shared_len // wl.block_size + sum(
+        max(0, math.ceil(int(c) / wl.block_size) - shared_len // wl.block_size) for c in ctx)
+    return ((shared_len + own) * row + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * 2
+            + 4 * nblk + 4 * wl.num_seqs)
+
+
+def shared_main(a):
+    """The shared-prefix decode step: 256 sequences whose first 2048 tokens sit in the
+    same 64 blocks, private tails U[0, 512], H_q = H_kv = 32, D 128, B 32, fp16.  Step =
+    append of the 256 new tokens + pkv_paged_attention_decode_shared; the per-sequence
+    balanced decode of the same batch is timed beside it."""
+    import torch
+    import paged_kv_cache_146_amd as pkv
+    from paged_kv_cache_146_amd import workloads as W
+
+    wl = W.shared_prefix_decode(seed=4)
+    shared_len = wl.shared_blocks * wl.block_size
+    dev = "cuda"
+    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype)
+    k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.float16).to(dev)
+
+    T = len(wl.fill_seq)
+    for o in range(0, T, 1 << 17):
+        e = min(T, o + (1 << 17))
+        sl = pkv.pkv_slot_mapping(bt, torch.from_numpy(wl.fill_seq[o:e]).to(dev),
+                                  torch.from_numpy(wl.fill_pos[o:e]).to(dev), wl.block_size)
+        pkv.pkv_kv_cache_write(sl, bits(wl.k_src[o:e]), bits(wl.v_src[o:e]), desc, k_pool, v_pool)
+    q = bits(wl.q)
+    rows = wl.decode_new_token_rows()
+    k_new, v_new = bits(wl.k_src[rows]), bits(wl.v_src[rows])
+    seq_idx = torch.arange(wl.num_seqs, dtype=torch.int32, device=dev)
+    pos_new = (cl - 1).to(torch.int32)
+    out = torch.empty_like(q)
+    out_plain = torch.empty_like(q)
+    ws = torch.empty(pkv.pkv_decode_shared_workspace_bytes(
+        wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, shared_len),
+        dtype=torch.uint8, device=dev)
+    ws_plain = torch.empty(pkv.pkv_decode_workspace_bytes(
+        wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.max_context_len, -1),
+        dtype=torch.uint8, device=dev)
+    flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
+    def decode():
+        pkv.pkv_paged_attention_decode_shared(q, desc, k_pool, v_pool, bt, cl,
+                                              wl.max_context_len, wl.scale, shared_len,
+                                              workspace=ws, out=out)
+
+    def plain():
+        pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
+                                       wl.scale, partition_size=-1, workspace=ws_plain,
+                                       out=out_plain)
+
+    def step():
+        pkv.pkv_kv_cache_append(bt, seq_idx, pos_new, k_new, v_new, desc, k_pool, v_pool)
+        decode()
+
+    def timed(fn, n):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            if not a.no_flush:
+                flush.sum()
+            starts[i].record()
+            fn()
+            ends[i].record()
+        torch.cuda.synchronize()
+        return np.array([x.elapsed_time(y) for x, y in zip(starts, ends)])
+
+    for _ in range(a.warmup):
+        if not a.no_flush:
+            flush.sum()
+        step()
+    step_us = float(timed(step, a.steps).mean() * 1e3)
+    dec_us = float(timed(decode, a.steps).mean() * 1e3)
+    plain_us = float(timed(plain, a.steps).mean() * 1e3)
+
+    parity = None
+    try:
+        import oracle
+        opool = _oracle_pool(oracle, wl)
+        sel = np.array([0, int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))],
+                       np.int32)
+        ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens,
+                                  wl.scale, seqs=sel)
+        got = out.float().cpu().numpy().astype(np.float64)[sel]
+        err = np.abs(got - ref)
+        parity = {"seqs": sel.tolist(), "max_abs": float(err.max()),
+                  "within_tol": bool((err <= 2e-3 + 1e-2 * np.abs(ref)).all())}
+    except Exception as ex:  # the bench still reports; the tests are the parity gate
+        parity = {"error": repr(ex)}
+
+    dbytes = shared_bytes(wl, shared_len)
+    wbytes = write_bytes(wl)
+    achieved = dbytes / (dec_us * 1e-6) / 1e9
+    res = {
+        "metric": "shared-prefix paged decode: algorithmic GB/s (prefix counted once)",
+        "value": round((dbytes + wbytes) / (step_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(step_us / 1e3, 5), "us_per_step": round(step_us, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "MHA shared-prefix decode: 256 sequences, 2048-token shared "
+                               "prefix + tails U[0,512] (seed 4), H 32/32, D 128, B 32, fp16",
+                   "shared_len": shared_len, "sum_context": int(wl.context_lens.sum()),
+                   "caches": "warm" if a.no_flush else "flushed before every step",
+                   "step": "kv_cache_append (256 new tokens) + paged_attention_decode_shared"},
+        "algorithmic_bytes_per_step": dbytes + wbytes,
+        "decode_us": round(dec_us, 2),
+        "per_sequence_balanced_decode_us": round(plain_us, 2),
+        "roofline": {"bound": "hbm",
+                     "kernel": "shared_prefix_kernel + paged_decode_balanced_kernel (tails) + "
+                               "split_reduce_kernel, one call",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(dec_us, 2)},
+        "parity_spot_check": parity,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_shared(wl, shared_len, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_shared(wl, shared_len, budget_s):
+    """The oracle's paged decode (which reads the prefix once per sequence) on rounds of
+    16 sequences of the same batch until the budget is spent, scaled to all 256."""
+    import oracle
+    opool = _oracle_pool(oracle, wl)
+    done, t_used, k = 0, 0.0, 0
+    while t_used < budget_s and done < wl.num_seqs:
+        sel = np.arange(k, min(k + 16, wl.num_seqs), dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale,
+                            seqs=sel)
+        t_used += time.perf_counter() - t0
+        done += len(sel)
+        k += len(sel)
+    step_s = t_used * wl.num_seqs / done
+    return {"value": round((shared_bytes(wl, shared_len) + write_bytes(wl)) / step_s / 1e9, 3),
+            "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "decode of %d of the 256 sequences (%.1f s), scaled to the whole batch"
+                      % (done, t_used),
+            "us_per_step": round(step_s * 1e6, 1)}
 
 
 def cpu_baseline_copy(pairs_np, block_bytes):

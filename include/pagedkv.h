@@ -256,6 +256,43 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
                                int32_t max_context_len, float scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* Decode for a batch whose sequences share a prefix of blocks ([P1] §5: two
+ * requests that hit the same prefix pages point their block tables at the same
+ * physical blocks, with reference counts; [P3] section 4, block-level sharing:
+ * sequences with the same prompt share read-only physical blocks).  Computes
+ * exactly what pkv_paged_attention_decode computes (up to rounding order), but
+ * reads each shared block once per kv head for the whole batch instead of once
+ * per sequence:
+ *   1. the prefix tokens [0, shared_len): one pass per (kv head, slice of the
+ *      prefix) over row 0's blocks, the queries of 16/G sequences x G heads in
+ *      the 16 columns of each matrix-core tile;
+ *   2. every sequence's own tokens [shared_len, ctx_s): the balanced decode,
+ *      started shared_len / block_size entries into each table row;
+ *   3. the log-sum-exp merge of the prefix slices and the tail (as
+ *      pkv_split_kv_reduce).
+ *   shared_len: a multiple of block_size, at most max_blocks_per_seq *
+ *      block_size.  The caller guarantees block_table[s][j] == block_table[0][j]
+ *      for every s and every j < shared_len / block_size (the kernel reads row
+ *      0 there; a row that differs is not detected and gets row 0's keys).  A
+ *      sequence with ctx_s < shared_len sees only its first ctx_s keys.
+ *   workspace: device, at least pkv_decode_shared_workspace_bytes bytes,
+ *      16-byte aligned, no initialisation needed; calls that share it must
+ *      not overlap in time.
+ *   Everything else as pkv_paged_attention_decode (same dtypes, scale modes,
+ *   block sizes and head-group limits); shared_len = 0 is the balanced decode.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP. */
+int pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t shared_len,
+                                      size_t* bytes);
+int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                      int32_t num_q_heads, const pkv_pool_desc* pool,
+                                      const void* k_pool, const void* v_pool,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t shared_len, float scale, void* workspace,
+                                      size_t workspace_bytes, void* out, void* stream);
+
 /* [P1 §4] Log-sum-exp merge of split-KV partitions.  For sequence s, head h,
  * partitions i < min(ceil(ctx_s / partition_size), max_partitions) with state
  * (m_i = part_max, l_i = part_sum, o_i = part_out normalised by l_i):

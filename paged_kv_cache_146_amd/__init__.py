@@ -39,7 +39,8 @@ EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_split_kv_reduce", "pkv_paged_prefill", "pkv_alloc_create", "pkv_alloc_destroy",
            "pkv_alloc_add_seq", "pkv_alloc_fork", "pkv_alloc_append", "pkv_alloc_free_seq",
            "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
-           "pkv_copy_blocks"]
+           "pkv_copy_blocks", "pkv_decode_shared_workspace_bytes",
+           "pkv_paged_attention_decode_shared"]
 
 
 class PagedKVError(RuntimeError):
@@ -94,6 +95,11 @@ def lib():
                                                                   P, P]),
                     "pkv_split_kv_reduce": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I32, I32, P,
                                                            I32, P]),
+                    "pkv_decode_shared_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32,
+                                                                         P]),
+                    "pkv_paged_attention_decode_shared": (ctypes.c_int, [P, I32, I32, I32, P, P, P,
+                                                                         P, P, P, I32, P, I32,
+                                                                         I32, F, P, SZ, P, P]),
                     "pkv_paged_prefill": (ctypes.c_int, [P, I32, P, I32, I32, I32, I32, P, P, P,
                                                          P, P, P, I32, P, I32, F, I32, P, P]),
                     "pkv_alloc_create": (ctypes.c_int, [I32, I32, P, I32, P]),
@@ -389,6 +395,42 @@ def pkv_paged_attention_decode(q, desc: PoolDesc, k_pool, v_pool, block_table, c
         int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
         float(scale), int(partition_size), _ptr(workspace, "workspace", allow_none=True),
         ws_bytes, _ptr(out, "out"), _stream(stream)), "pkv_paged_attention_decode")
+    return out
+
+
+def pkv_decode_shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                      shared_len) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().pkv_decode_shared_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                   int(num_kv_heads), int(head_dim),
+                                                   int(shared_len), ctypes.byref(out)),
+           "pkv_decode_shared_workspace_bytes")
+    return out.value
+
+
+def pkv_paged_attention_decode_shared(q, desc: PoolDesc, k_pool, v_pool, block_table,
+                                      context_lens, max_context_len: int, scale: float,
+                                      shared_len: int, k_scale=None, v_scale=None,
+                                      workspace=None, out=None, q_dtype=None, stream=None):
+    """Decode of a batch whose table rows share their first shared_len / block_size
+    entries (the shared prefix is read once per kv head)."""
+    torch = _torch()
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if workspace is None:
+        need = pkv_decode_shared_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim,
+                                                 shared_len)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = int(workspace.numel() * workspace.element_size())
+    _check(lib().pkv_paged_attention_decode_shared(
+        _ptr(q, "q"), qd, S, Hq, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
+        _ptr(v_pool, "v_pool"), _ptr(k_scale, "k_scale", allow_none=True),
+        _ptr(v_scale, "v_scale", allow_none=True), _ptr(block_table, "block_table"),
+        int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
+        int(shared_len), float(scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out"),
+        _stream(stream)), "pkv_paged_attention_decode_shared")
     return out
 
 

@@ -261,6 +261,72 @@ int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc
   return rc == 0 ? PKV_OK : rc;
 }
 
+namespace {
+
+// The balanced decode on a prepared launch (p.ctx_cap = the per-sequence token
+// cap of the stream): one stream of 64-token chunks over every (sequence, kv
+// head) pair, cut evenly across the resident wavefronts.
+int launch_balanced(pkv::DecodeLaunch& p, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const int64_t units = (int64_t)p.num_seqs * ((p.ctx_cap + 63) / 64) * p.num_kv_heads;
+  if (p.num_seqs > kMaxBalancedSeqs || units >= ((int64_t)1 << 31)) return PKV_EUNSUPPORTED;
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const size_t slot_bytes = (size_t)group * ((size_t)p.head_dim + 2) * sizeof(float);
+  const size_t cnt_bytes = balanced_counter_bytes(p.num_seqs, p.num_kv_heads);
+  if (!workspace || workspace_bytes < cnt_bytes + 2 * slot_bytes) return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
+  int nw = pkv::balanced_worker_capacity(p.kv_dtype, p.q_dtype, p.head_dim, p.block_size);
+  if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
+  const size_t fit = (workspace_bytes - cnt_bytes) / (2 * slot_bytes);
+  if ((size_t)nw > fit) nw = (int)fit;
+  char* base = static_cast<char*>(workspace);
+  float* ws = reinterpret_cast<float*>(base + cnt_bytes);
+  p.balanced = 1;
+  p.split = 1;
+  p.num_workers = nw;
+  p.counters = reinterpret_cast<unsigned long long*>(base);         // [S][H_kv]
+  p.epoch = next_epoch();
+  p.part_out = ws;                                                  // [2*nw][G][D]
+  p.part_max = ws + (size_t)2 * nw * group * p.head_dim;            // [2*nw][G][2]
+  const int rc = pkv::launch_decode(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+size_t balanced_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim) {
+  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  return balanced_counter_bytes(num_seqs, num_kv_heads) +
+         2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+// How a shared-prefix decode cuts the prefix: slices of whole 64-token chunks,
+// enough of them that (kv heads x column tiles x slices) reaches about 2048
+// wavefronts; the partial slots are the slices plus one for the tails.
+struct SharedPlan {
+  int n_slices, slice_chunks, max_parts;
+  size_t part_bytes;  // partial arrays, rounded up to 256 bytes
+};
+
+SharedPlan shared_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int shared_len) {
+  SharedPlan sp = {};
+  const int nch = (shared_len + 63) / 64;
+  if (nch > 0) {
+    const int G = num_q_heads / num_kv_heads;
+    const int64_t tiles = (num_seqs + 16 / G - 1) / (16 / G);
+    const int64_t per_slice = (int64_t)num_kv_heads * (tiles > 0 ? tiles : 1);
+    int64_t want = (2048 + per_slice - 1) / per_slice;
+    if (want > nch) want = nch;
+    sp.slice_chunks = (int)((nch + want - 1) / want);
+    sp.n_slices = (nch + sp.slice_chunks - 1) / sp.slice_chunks;
+  }
+  sp.max_parts = sp.n_slices + 1;
+  const size_t n = (size_t)num_seqs * num_q_heads * sp.max_parts;
+  sp.part_bytes = (n * ((size_t)head_dim + 2) * sizeof(float) + 255) / 256 * 256;
+  return sp;
+}
+
+}  // namespace
+
 int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                                size_t* bytes) {
@@ -273,9 +339,7 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
     return PKV_OK;
   }
   if (partition_size == PKV_PARTITION_BALANCED) {
-    const size_t group = (size_t)(num_q_heads / num_kv_heads);
-    *bytes = balanced_counter_bytes(num_seqs, num_kv_heads) +
-             2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
+    *bytes = balanced_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
     return PKV_OK;
   }
   if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
@@ -334,32 +398,7 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   p.ctx_cap = (int)cap;
   p.scale = scale;
 
-  if (balanced) {
-    // one stream of 64-token chunks over every (sequence, kv head) pair, cut evenly
-    const int64_t units = (int64_t)num_seqs * ((cap + 63) / 64) * pool->num_kv_heads;
-    if (num_seqs > kMaxBalancedSeqs || units >= ((int64_t)1 << 31)) return PKV_EUNSUPPORTED;
-    const int group = num_q_heads / pool->num_kv_heads;
-    const size_t slot_bytes = (size_t)group * ((size_t)pool->head_dim + 2) * sizeof(float);
-    const size_t cnt_bytes = balanced_counter_bytes(num_seqs, pool->num_kv_heads);
-    if (!workspace || workspace_bytes < cnt_bytes + 2 * slot_bytes) return PKV_EWORKSPACE;
-    if (!aligned16(workspace)) return PKV_EINVAL;
-    int nw = pkv::balanced_worker_capacity(pool->kv_dtype, q_dtype, pool->head_dim,
-                                           pool->block_size);
-    if (nw > PKV_MAX_WORKERS) nw = PKV_MAX_WORKERS;
-    const size_t fit = (workspace_bytes - cnt_bytes) / (2 * slot_bytes);
-    if ((size_t)nw > fit) nw = (int)fit;
-    char* base = static_cast<char*>(workspace);
-    float* ws = reinterpret_cast<float*>(base + cnt_bytes);
-    p.balanced = 1;
-    p.split = 1;
-    p.num_workers = nw;
-    p.counters = reinterpret_cast<unsigned long long*>(base);         // [S][H_kv]
-    p.epoch = next_epoch();
-    p.part_out = ws;                                                  // [2*nw][G][D]
-    p.part_max = ws + (size_t)2 * nw * group * pool->head_dim;        // [2*nw][G][2]
-    rc = pkv::launch_decode(p, as_stream(stream));
-    return rc == 0 ? PKV_OK : rc;
-  }
+  if (balanced) return launch_balanced(p, workspace, workspace_bytes, stream);
 
   if (partition_size == 0) {
     p.split = 0;
@@ -402,6 +441,133 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   r.head_dim = pool->head_dim;
   r.part_size = partition_size;
   r.max_parts = max_parts;
+  rc = pkv::launch_split_reduce(r, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
+int pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t shared_len,
+                                      size_t* bytes) {
+  if (!bytes || num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 0 ||
+      shared_len < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return PKV_EINVAL;
+  if (num_q_heads / num_kv_heads > kMaxHeadsGroup) return PKV_EUNSUPPORTED;
+  const SharedPlan sp = shared_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, shared_len);
+  *bytes = sp.part_bytes + balanced_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim);
+  return PKV_OK;
+}
+
+int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                      int32_t num_q_heads, const pkv_pool_desc* pool,
+                                      const void* k_pool, const void* v_pool,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t shared_len, float scale, void* workspace,
+                                      size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
+  if (num_q_heads / pool->num_kv_heads > kMaxHeadsGroup) return PKV_EUNSUPPORTED;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EINVAL;
+  if (shared_len < 0 || shared_len % pool->block_size != 0 ||
+      (int64_t)shared_len > (int64_t)max_blocks_per_seq * pool->block_size)
+    return PKV_EINVAL;
+  if (max_context_len > (1 << 30)) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PKV_EINVAL;
+  if (quantised(pool->kv_dtype) && (!k_scale || !v_scale)) return PKV_EINVAL;
+  if (num_seqs > 65535 || pool->num_kv_heads > 65535) return PKV_EUNSUPPORTED;
+  size_t need = 0;
+  rc = pkv_decode_shared_workspace_bytes(num_seqs, num_q_heads, pool->num_kv_heads,
+                                         pool->head_dim, shared_len, &need);
+  if (rc != PKV_OK) return rc;
+  if (!workspace || workspace_bytes < need) return PKV_EWORKSPACE;
+  if (!aligned16(workspace)) return PKV_EINVAL;
+  if (shared_len == 0)  // nothing shared: the plain balanced decode
+    return pkv_paged_attention_decode(q, q_dtype, num_seqs, num_q_heads, pool, k_pool, v_pool,
+                                      k_scale, v_scale, block_table, max_blocks_per_seq,
+                                      context_lens, max_context_len, scale,
+                                      PKV_PARTITION_BALANCED, workspace, workspace_bytes, out,
+                                      stream);
+
+  int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+  if (cap > max_context_len) cap = max_context_len;
+  const SharedPlan sp =
+      shared_plan(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim, shared_len);
+  const size_t n_part = (size_t)num_seqs * num_q_heads * sp.max_parts;
+  float* part_out = static_cast<float*>(workspace);
+  float* part_max = part_out + n_part * pool->head_dim;
+  float* part_sum = part_max + n_part;
+  char* bal = static_cast<char*>(workspace) + sp.part_bytes;
+
+  pkv::DecodeLaunch p = {};
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.kv_dtype = pool->kv_dtype;
+  p.scale_mode = pool->scale_mode;
+  p.block_size = pool->block_size;
+  p.num_blocks = pool->num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.scale = scale;
+  p.max_parts = sp.max_parts;
+
+  // 1. the prefix, read once per kv head: partial slots 0 .. n_slices-1
+  pkv::DecodeLaunch pre = p;
+  pre.prefix = 1;
+  pre.ctx_cap = (int)cap;
+  pre.shared_len = shared_len;
+  pre.n_slices = sp.n_slices;
+  pre.slice_chunks = sp.slice_chunks;
+  pre.part_out = part_out;
+  pre.part_max = part_max;
+  pre.part_sum = part_sum;
+  rc = pkv::launch_decode(pre, as_stream(stream));
+  if (rc != 0) return rc;
+
+  // 2. the private tails, balanced: partial slot n_slices
+  pkv::DecodeLaunch tail = p;
+  const int64_t tail_cap = cap - shared_len;
+  const int64_t tail_rows = ((int64_t)max_blocks_per_seq * pool->block_size - shared_len);
+  tail.ctx_off = shared_len;
+  tail.tbl_off = shared_len / pool->block_size;
+  tail.ctx_cap = (int)(tail_cap < 0 ? 0 : (tail_cap < tail_rows ? tail_cap : tail_rows));
+  tail.tail_part = sp.n_slices;
+  tail.tail_out = part_out;
+  tail.tail_max = part_max;
+  tail.tail_sum = part_sum;
+  rc = launch_balanced(tail, bal, workspace_bytes - sp.part_bytes, stream);
+  if (rc != PKV_OK) return rc;
+
+  // 3. the log-sum-exp merge of every slot
+  pkv::ReduceLaunch r;
+  r.part_out = part_out;
+  r.part_max = part_max;
+  r.part_sum = part_sum;
+  r.context_lens = nullptr;  // all max_parts slots
+  r.out = out;
+  r.out_dtype = q_dtype;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = pool->head_dim;
+  r.part_size = 1;
+  r.max_parts = sp.max_parts;
   rc = pkv::launch_split_reduce(r, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }

@@ -74,6 +74,14 @@ struct DecodeScalars {
   uint32_t epoch;   // balanced kernel: call tag of the shared-pair counters
   int scale_mode;   // quantised pools: SCALE_BLOCK / SCALE_TENSOR / SCALE_TOKEN
   float scale_log2; // softmax scale * log2(e)
+  // balanced kernel over the private tails of a batch with a shared prefix:
+  // every sequence starts ctx_off tokens (tbl_off table entries) in, and its
+  // result goes to partial slot tail_part of the part arrays (stride max_parts)
+  // instead of `out`; tail_part < 0: plain decode
+  int ctx_off, tbl_off, tail_part;
+  float* tail_out;
+  float* tail_max;
+  float* tail_sum;
 };
 
 constexpr int kWaves = 4;
@@ -133,12 +141,8 @@ __device__ __forceinline__ void state_init(State<C>& st) {
 // apart so that a prefetch of the next pair's q does not wait on its own load).
 // Operand (pq, h) of lane group g covers the dims of K piece c = 4 pq + g, step h.
 template <class C>
-__device__ __forceinline__ void load_q(typename C::QOp (&qop)[C::NQ],
-                                       const uint8_t* __restrict__ q, int s, int kvh,
-                                       const DecodeScalars& sc, int n, int g) {
-  const bool live = n < sc.G;
-  const uint8_t* row =
-      q + ((size_t)s * sc.Hq + (size_t)kvh * sc.G + (live ? n : 0)) * C::Dim * C::QEB;
+__device__ __forceinline__ void load_q_row(typename C::QOp (&qop)[C::NQ],
+                                           const uint8_t* __restrict__ row, int g) {
 #pragma unroll
   for (int pq = 0; pq < C::NPL; ++pq) {
     const int c = 4 * pq + g;
@@ -152,6 +156,15 @@ __device__ __forceinline__ void load_q(typename C::QOp (&qop)[C::NQ],
         qop[pq * C::SPP + h] = *reinterpret_cast<const u32x4*>(row + ((size_t)c * C::E + 8 * h) * 2);
     }
   }
+}
+
+template <class C>
+__device__ __forceinline__ void load_q(typename C::QOp (&qop)[C::NQ],
+                                       const uint8_t* __restrict__ q, int s, int kvh,
+                                       const DecodeScalars& sc, int n, int g) {
+  const bool live = n < sc.G;
+  load_q_row<C>(qop, q + ((size_t)s * sc.Hq + (size_t)kvh * sc.G + (live ? n : 0)) * C::Dim * C::QEB,
+                g);
 }
 
 template <class C>
@@ -373,12 +386,14 @@ __device__ __forceinline__ void mask_v(typename C::VPiece (&vr)[C::NV], int nval
 }
 
 // Scores x[4 T + r] belong to token 16 T + 4 g + r, and so do the scales ks[4 T + r]
-// and vs[4 T + r] of a quantised pool.
-template <class C, int KVT, int CT>
+// and vs[4 T + r] of a quantised pool.  Keys from nvalid on (wave-uniform) are
+// past the context of every column.  COLMASK: the lane's column also hides the
+// keys from xvalid on, and may see no key of the chunk at all.
+template <class C, int KVT, int CT, bool COLMASK = false>
 __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[4],
                                                  typename C::VPiece (&vr)[C::NV], float zscale,
                                                  const float (&ks)[16], float (&vs)[16],
-                                                 int nvalid, int g) {
+                                                 int nvalid, int g, int xvalid = 64) {
   constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);  // quantised: scaled 8-bit codes
   float x[16];
 #pragma unroll
@@ -402,17 +417,26 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
       }
     mask_v<C>(vr, nvalid, g);
   }
+  if constexpr (COLMASK) {
+    if (xvalid < 64) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        x[i] = 16 * (i >> 2) + 4 * g + (i & 3) < xvalid ? x[i] : -INFINITY;
+    }
+  }
   float cm = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) cm = fmaxf(cm, x[i]);
-  cm = max_groups(cm);  // finite: token 0 of every chunk is visible
+  cm = max_groups(cm);  // finite unless COLMASK: token 0 of every chunk is visible
   const float mn = fmaxf(st.m, cm);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+  // a column that has seen no key yet keeps m = -inf and adds nothing
+  const float mref = COLMASK && mn == -INFINITY ? 0.0f : mn;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
   st.m = mn;
   float p[16], ps = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(x[i] - mn);
+    p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
     ps += p[i];
   }
   st.l = st.l * alpha + ps;
@@ -621,8 +645,8 @@ paged_decode_kernel(
 
 // exclusive prefix of per-sequence unit counts into lds[0..S], by one workgroup:
 // tiles of 256 sequences, each scanned by wave shuffles plus the wave totals
-__device__ void unit_prefix(const int32_t* __restrict__ context_lens, int S, int ctx_cap, int Hkv,
-                            int* lds, int* tmp) {
+__device__ void unit_prefix(const int32_t* __restrict__ context_lens, int S, int ctx_off,
+                            int ctx_cap, int Hkv, int* lds, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int carry = 0;
   for (int base = 0; base < S; base += kThreads) {
@@ -630,7 +654,8 @@ __device__ void unit_prefix(const int32_t* __restrict__ context_lens, int S, int
     int v = 0;
     if (s < S) {
       int c = context_lens[s];
-      c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+      c = c < ctx_off ? 0 : c - ctx_off;
+      c = c > ctx_cap ? ctx_cap : c;
       v = ((c + 63) >> 6) * Hkv;
     }
     int x = v;  // inclusive scan inside the wave
@@ -696,6 +721,23 @@ __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch,
   }
 }
 
+// The result of query head hq of sequence s as partial slot sc.tail_part: the
+// normalised output, its log-sum-exp (natural-log units of z) and weight 1.
+// acc * inv is the output; m is the log2-domain max and l the exp-sum.
+template <int NDT>
+__device__ __forceinline__ void tail_emit(const DecodeScalars& sc, int s, int hq,
+                                          const f32x4 (&acc)[NDT], float inv, float m, float l,
+                                          int g) {
+  const size_t pi = ((size_t)s * sc.Hq + hq) * sc.max_parts + sc.tail_part;
+  float* o = sc.tail_out + pi * (16 * NDT) + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = acc[dt] * inv;
+  if (g == 0) {
+    sc.tail_max[pi] = m * kLn2 + logf(l);
+    sc.tail_sum[pi] = 1.0f;
+  }
+}
+
 // One wavefront merges the partial states of a shared pair (pieces of workers wa..wb,
 // log2-domain maxima) in a single online pass over the pieces.  Lane (n, g) takes
 // head n and dims 16 dt + 4 g + r, the layout the pieces were written in.  Reads
@@ -733,9 +775,13 @@ __device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict_
   }
   if (n < sc.G) {
     const float inv = 1.0f / L;
-    const size_t orow = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + n) * D + 4 * g;
+    if (sc.tail_part >= 0) {
+      tail_emit<NDT>(sc, s, kvh * sc.G + n, O, inv, M, L, g);
+    } else {
+      const size_t orow = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + n) * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) store4(out, QDT, orow + 16 * dt, O[dt] * inv);
+      for (int dt = 0; dt < NDT; ++dt) store4(out, QDT, orow + 16 * dt, O[dt] * inv);
+    }
   }
 }
 
@@ -759,13 +805,25 @@ paged_decode_balanced_kernel(
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
 
-  unit_prefix(context_lens, sc.S, sc.ctx_cap, sc.Hkv, prefix, tmp);
+  unit_prefix(context_lens, sc.S, sc.ctx_off, sc.ctx_cap, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
   if (blockIdx.x == 0) {  // sequences with an empty context own no unit: their output is zero
     for (int s0 = 0; s0 < sc.S; ++s0) {
       if (prefix[s0 + 1] != prefix[s0]) continue;
-      for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads)
-        store_any(out, CT, (size_t)s0 * sc.Hq * D + i, 0.0f);
+      if (sc.tail_part >= 0) {  // an empty partial: weight 0
+        for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads) {
+          const int hq = i / D, d = i - hq * D;
+          const size_t pi = ((size_t)s0 * sc.Hq + hq) * sc.max_parts + sc.tail_part;
+          sc.tail_out[pi * D + d] = 0.0f;
+          if (d == 0) {
+            sc.tail_max[pi] = -INFINITY;
+            sc.tail_sum[pi] = 0.0f;
+          }
+        }
+      } else {
+        for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads)
+          store_any(out, CT, (size_t)s0 * sc.Hq * D + i, 0.0f);
+      }
     }
   }
   const int NWe = min(sc.num_workers, U);
@@ -779,8 +837,9 @@ paged_decode_balanced_kernel(
   const int u_end = worker_start(w + 1, U, NWe);
 
   auto clamp_ctx = [&](int s) {
-    const int c = context_lens[s];
-    return uniform(c < 0 ? 0 : (c > sc.ctx_cap ? sc.ctx_cap : c));
+    int c = context_lens[s];
+    c = c < sc.ctx_off ? 0 : c - sc.ctx_off;
+    return uniform(c > sc.ctx_cap ? sc.ctx_cap : c);
   };
   auto locate = [&](int u) {
     Pos p;
@@ -822,7 +881,7 @@ paged_decode_balanced_kernel(
   };
   // a piece ends at the last chunk of its pair or of the worker's share
   auto piece_ends = [&](const Pos& p) { return p.j == p.nch - 1 || p.k + 1 >= n_units; };
-  auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W; };
+  auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W + sc.tbl_off; };
 
   State<C> st;
   state_init(st);
@@ -867,9 +926,13 @@ paged_decode_balanced_kernel(
     if (whole) {
       if (n < sc.G) {
         const float inv = 1.0f / lw;
-        const size_t orow = ((size_t)p.s * sc.Hq + (size_t)p.kvh * sc.G + n) * D + 4 * g;
+        if (sc.tail_part >= 0) {
+          tail_emit<C::NDT>(sc, p.s, p.kvh * sc.G + n, st.acc, inv, st.m, lw, g);
+        } else {
+          const size_t orow = ((size_t)p.s * sc.Hq + (size_t)p.kvh * sc.G + n) * D + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) store4(out, CT, orow + 16 * dt, st.acc[dt] * inv);
+          for (int dt = 0; dt < C::NDT; ++dt) store4(out, CT, orow + 16 * dt, st.acc[dt] * inv);
+        }
       }
     } else {
       // Publish the partial state with device-scope stores (coherent across the
@@ -1022,6 +1085,8 @@ paged_decode_balanced_kernel(
 
 // =================================================================================
 // Split-KV reduce for fixed partitions: one workgroup per (query head, sequence).
+// Without context_lens every one of the max_parts slots is merged (empty ones,
+// with exp-sum 0, weigh nothing).
 // =================================================================================
 template <int D>
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
@@ -1033,10 +1098,13 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
   __shared__ float o_lds[kWaves][D];
   const int h = blockIdx.x, s = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  long long cap = (long long)max_parts * part_size;
-  long long ctx = context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int np = (int)((ctx + part_size - 1) / part_size);
+  int np = max_parts;
+  if (context_lens) {
+    const long long cap = (long long)max_parts * part_size;
+    long long ctx = context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    np = (int)((ctx + part_size - 1) / part_size);
+  }
   const size_t orow = ((size_t)s * Hq + h) * D;
   if (np == 0) {
     for (int d = threadIdx.x; d < D; d += kThreads) store_any(out, out_dtype, orow + d, 0.0f);
@@ -1079,7 +1147,148 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += kThreads) {
     const float o = (o_lds[0][d] + o_lds[1][d]) + (o_lds[2][d] + o_lds[3][d]);
-    store_any(out, out_dtype, orow + d, o / L);
+    store_any(out, out_dtype, orow + d, L > 0.0f ? o / L : 0.0f);
+  }
+}
+
+// =================================================================================
+// Kernel C: the shared prefix of a batch, read once per kv head
+// =================================================================================
+// Every sequence of the batch holds its first shared_len tokens in the same
+// physical blocks (the caller's table rows agree there; row 0 is read).  A
+// wavefront takes one kv head, one slice of the prefix and a tile of 16 query
+// columns, here 16/G sequences x the G heads of that kv head, so one K/V chunk
+// feeds the scores of 16/G sequences instead of one: the product S^T = K . Q^T
+// has distinct queries in every column even for G = 1.  Column (sequence s,
+// head h) sees the keys below min(ctx_s, shared_len).  The slice's state goes to
+// partial slot `slice` of (s, query head); the tails and the merge follow.
+struct PrefixGrid {
+  int shared_len;
+  int n_slices;    // slices of the prefix (partial slots 0 .. n_slices-1)
+  int slice_chunks;  // 64-token chunks per slice
+  int spt;         // sequences per column tile: 16 / G
+  int n_tiles;     // column tiles: ceil(S / spt)
+  int wg_per_group;  // workgroups per (kv head, slice): ceil(n_tiles / 4)
+  int n_groups;    // Hkv * n_slices
+};
+
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return uniform(x);
+}
+
+template <int KVT, int CT, int D, bool SMALLB>
+__global__ __launch_bounds__(kThreads) void shared_prefix_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ context_lens, float* __restrict__ part_out,
+    float* __restrict__ part_max, float* __restrict__ part_sum, const DecodeScalars sc,
+    const PrefixGrid pg) {
+  using C = Cfg<KVT, CT, D>;
+  constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);
+  // The workgroups of one (kv head, slice) share a residue of blockIdx mod 8, so
+  // they run on one XCD and read the slice's pages through one L2.
+  const int x = blockIdx.x;
+  const int grp = (x >> 3) / pg.wg_per_group * 8 + (x & 7);
+  if (grp >= pg.n_groups) return;  // no barrier in this kernel
+  const int kvh = grp / pg.n_slices, slice = grp - kvh * pg.n_slices;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int tile = ((x >> 3) % pg.wg_per_group) * kWaves + wave;
+  if (tile >= pg.n_tiles) return;
+
+  const int sl = n / sc.G, h = n - sl * sc.G;
+  const int s = tile * pg.spt + sl;
+  const bool live = sl < pg.spt && s < sc.S;
+  int lim = 0;  // keys of the prefix this column sees
+  if (live) {
+    int c = context_lens[s];
+    c = c < 0 ? 0 : (c > sc.ctx_cap ? sc.ctx_cap : c);
+    lim = min(c, pg.shared_len);
+  }
+  const int lim_tile = wave_max_int(lim);
+  const int t_begin = slice * pg.slice_chunks * 64;
+  const int t_end = min(t_begin + pg.slice_chunks * 64, lim_tile);
+
+  typename C::QOp qop[C::NQ];
+  load_q_row<C>(qop, q + ((size_t)(live ? s : 0) * sc.Hq + (size_t)kvh * sc.G + h) * D * C::QEB,
+                g);
+  q_live<C>(qop, qop, live);
+  State<C> st;
+  state_init(st);
+  const int32_t* trow = block_table;  // row 0: the shared blocks
+  const int cnt = t_end > t_begin ? (t_end - t_begin + 63) >> 6 : 0;
+  auto base_of = [&](int i) { return t_begin + 64 * min(i, cnt - 1); };
+
+  if constexpr (SMALLB) {
+    for (int i = 0; i < cnt; ++i) {
+      const int base = base_of(i);
+      Chunk<C> ch;
+      float ks[16], vs[16];
+      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g);
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, ch.k, qop);
+      chunk_softmax_pv<C, KVT, CT, true>(st, S, ch.v, sc.scale_log2, ks, vs,
+                                         min(64, t_end - base), g, lim - base);
+    }
+  } else if (cnt > 0) {
+    // the single-buffered pipeline of paged_decode_kernel
+    Chunk<C> R;
+    float ks0[16], vs0[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ks0[i] = vs0[i] = 1.0f;
+    {
+      const Pages p0 = pages_of(trow, base_of(0), t_end, sc);
+      issue_k<C>(R.k, k_pool, p0, kvh, sc, n, g);
+      if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
+      issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
+    }
+    Pages p1 = pages_of(trow, base_of(1), t_end, sc);
+    for (int i = 0; i < cnt; ++i) {
+      const int b0 = base_of(i);
+      const bool more = i + 1 < cnt;
+      f32x4 S[4];
+      chunk_qk<C, KVT, CT>(S, R.k, qop);
+      issue_point();
+      float ks1[16], vs1[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ks1[k] = vs1[k] = 1.0f;
+      Pages p2 = p1;
+      if (more) {
+        issue_k<C>(R.k, k_pool, p1, kvh, sc, n, g);
+        if constexpr (kFp8) chunk_scales(ks1, vs1, k_scale, v_scale, p1, kvh, sc, g);
+        p2 = pages_of(trow, base_of(i + 2), t_end, sc);
+      }
+      issue_point();
+      chunk_softmax_pv<C, KVT, CT, true>(st, S, R.v, sc.scale_log2, ks0, vs0,
+                                         min(64, t_end - b0), g, lim - b0);
+      issue_point();
+      if (more) issue_v<C>(R.v, v_pool, p1, kvh, sc, n, g);
+      issue_point();
+      p1 = p2;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        ks0[k] = ks1[k];
+        vs0[k] = vs1[k];
+      }
+    }
+  }
+
+  // the slice's state of column (s, h): normalised output, max (natural-log units
+  // of z) and exp-sum; a column that saw no key leaves an empty state (weight 0)
+  const float lw = sum_groups(st.l);
+  if (live) {
+    const size_t pi = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + h) * sc.max_parts + slice;
+    const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
+    float* o = part_out + pi * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = st.acc[dt] * inv;
+    if (g == 0) {
+      part_max[pi] = lw > 0.0f ? st.m * kLn2 : -INFINITY;
+      part_sum[pi] = lw;
+    }
   }
 }
 
@@ -1090,6 +1299,23 @@ namespace {
 
 template <int KVT, int CT, int D, bool SMALLB>
 int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
+  if (p.prefix) {
+    PrefixGrid pg;
+    pg.shared_len = p.shared_len;
+    pg.n_slices = p.n_slices;
+    pg.slice_chunks = p.slice_chunks;
+    pg.spt = 16 / sc.G;
+    pg.n_tiles = (p.num_seqs + pg.spt - 1) / pg.spt;
+    pg.wg_per_group = (pg.n_tiles + kWaves - 1) / kWaves;
+    pg.n_groups = p.num_kv_heads * p.n_slices;
+    const long long wgs = (long long)(pg.n_groups + 7) / 8 * 8 * pg.wg_per_group;
+    if (pg.n_groups < 1 || wgs >= (1LL << 31)) return -3;
+    hipLaunchKernelGGL((shared_prefix_kernel<KVT, CT, D, SMALLB>), dim3((unsigned)wgs),
+                       dim3(kThreads), 0, st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
+                       (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
+                       p.context_lens, p.part_out, p.part_max, p.part_sum, sc, pg);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   if (p.balanced) {
     const size_t lds = ((size_t)p.num_seqs + 1) * sizeof(int);
     dim3 grid((sc.num_workers + kWaves - 1) / kWaves);
@@ -1128,7 +1354,9 @@ int log2_exact(int x) {
 
 }  // namespace
 
-int launch_decode(const DecodeLaunch& p, hipStream_t st) {
+namespace {
+
+DecodeScalars scalars_of(const DecodeLaunch& p) {
   DecodeScalars sc;
   sc.W = p.max_blocks_per_seq;
   sc.ctx_cap = p.ctx_cap;
@@ -1146,6 +1374,19 @@ int launch_decode(const DecodeLaunch& p, hipStream_t st) {
   sc.epoch = p.epoch;
   sc.scale_mode = p.scale_mode;
   sc.scale_log2 = p.scale * kLog2e;
+  sc.ctx_off = p.ctx_off;
+  sc.tbl_off = p.tbl_off;
+  sc.tail_part = p.tail_part;
+  sc.tail_out = p.tail_out;
+  sc.tail_max = p.tail_max;
+  sc.tail_sum = p.tail_sum;
+  return sc;
+}
+
+}  // namespace
+
+int launch_decode(const DecodeLaunch& p, hipStream_t st) {
+  const DecodeScalars sc = scalars_of(p);
   if (sc.blog2 < 0 || p.block_size > 64 || sc.G > 16) return -3;
   const int kv = p.kv_dtype, qd = p.q_dtype;
   if (kv == DT_F32 && qd == DT_F32) return pick_d<DT_F32, DT_F32>(p, sc, st);

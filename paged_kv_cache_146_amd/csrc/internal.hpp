@@ -33,6 +33,16 @@ struct DecodeLaunch {
   unsigned long long* counters;  // balanced: one per (sequence, kv head)
   uint32_t epoch;     // balanced: tag of this call for the counters
   float scale;
+  // balanced over the private tails of a shared-prefix batch: start ctx_off
+  // tokens / tbl_off table entries in, result to partial slot tail_part (< 0: off)
+  int ctx_off = 0, tbl_off = 0, tail_part = -1;
+  float* tail_out = nullptr;
+  float* tail_max = nullptr;
+  float* tail_sum = nullptr;
+  // the shared-prefix kernel (part_out/part_max/part_sum: partial slots 0 ..
+  // n_slices-1 of stride max_parts)
+  int prefix = 0;
+  int shared_len = 0, n_slices = 0, slice_chunks = 0;
 };
 
 // Wavefront workers the balanced decode can keep resident on the current device
