@@ -78,7 +78,8 @@ def _load():
                 "orc_int8_encode_n": (None, [P, I64, P]),
                 "orc_kv_cache_write": (I32, [P, I64, P, P, I32, I64, I64, I64, I64, I32, P, P, P, P,
                                               I32]),
-                "orc_paged_decode": (I32, [P, I32, I64, I64, P, P, I64, P, D, P, I64, P, P]),
+                "orc_paged_decode": (I32, [P, I32, I64, I64, P, P, I64, P, D, I64, P, I64, P,
+                                           P]),
                 "orc_decode_partials": (I32, [P, I32, I64, I64, P, P, I64, P, D, I64, I64, P, P, P]),
                 "orc_state_merge": (None, [D, D, P, D, D, P, I64, P, P, P]),
                 "orc_split_reduce": (None, [P, P, P, P, I64, I64, I64, I64, I64, P]),
@@ -216,7 +217,8 @@ def kv_cache_write(pool: Pool, slots, k, v, src_dtype: str):
 # Attention  [P1 §4], [P3 §5]
 # --------------------------------------------------------------------------------------
 def paged_decode(q, q_dtype: str, pool: Pool, block_table, context_lens, scale: float,
-                 seqs=None, return_lse: bool = False):
+                 seqs=None, return_lse: bool = False, window: int = 0):
+    """window > 0: sliding-window decode ([P1 §1.1, §7]), keys [ctx - window, ctx) only."""
     q = _c(q, _NP_STORAGE[q_dtype])
     S, Hq, D = q.shape
     bt = _c(block_table, np.int32)
@@ -227,8 +229,8 @@ def paged_decode(q, q_dtype: str, pool: Pool, block_table, context_lens, scale: 
     lse = np.empty((n, Hq), np.float64) if return_lse else None
     st = pool._struct()
     rc = _load().orc_paged_decode(_ptr(q), DTYPES[q_dtype], S, Hq, ctypes.byref(st), _ptr(bt),
-                                  bt.shape[1], _ptr(cl), float(scale), _ptr(sel), n, _ptr(out),
-                                  _ptr(lse))
+                                  bt.shape[1], _ptr(cl), float(scale), int(window), _ptr(sel),
+                                  n, _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("invalid decode arguments")
     return (out, lse) if return_lse else out

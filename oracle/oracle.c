@@ -279,11 +279,15 @@ static int check_pool(const orc_pool* pool, int64_t num_q_heads) {
   return 0;
 }
 
-/* ---- [P1 §4], [P3 §5] decode: one-shot softmax over the gathered context --- */
+/* ---- [P1 §4], [P3 §5] decode: one-shot softmax over the gathered context ---
+ * [P1 §1.1, §7] with a window w > 0 the query at position p = ctx - 1 sees only
+ * the keys of [p - w + 1, p], i.e. t in [max(0, ctx - w), ctx). */
 int orc_paged_decode(const void* q, int q_dtype, int64_t num_seqs, int64_t num_q_heads,
                      const orc_pool* pool, const int32_t* block_table,
                      int64_t max_blocks_per_seq, const int32_t* context_lens, double scale,
-                     const int32_t* seqs, int64_t n_sel, double* out, double* lse) {
+                     int64_t window, const int32_t* seqs, int64_t n_sel, double* out,
+                     double* lse) {
+  if (window < 0) return -1;
   if (check_pool(pool, num_q_heads) || elem_size(q_dtype) == 0 || quantised(q_dtype))
     return -1;
   if (!seqs) n_sel = num_seqs;
@@ -307,8 +311,10 @@ int orc_paged_decode(const void* q, int q_dtype, int64_t num_seqs, int64_t num_q
       int64_t s = seqs ? seqs[i] : i;
       for (int64_t d = 0; d < D; ++d) qv[d] = load_value(q, q_dtype, (s * num_q_heads + h) * D + d);
       double m, l;
-      attend_range(qv, pool, block_table + s * max_blocks_per_seq, h / G, 0, context_lens[s],
-                   scale, &m, &l, acc, z, krow, vrow);
+      int64_t first = 0;  /* the oldest visible key */
+      if (window > 0 && context_lens[s] > window) first = context_lens[s] - window;
+      attend_range(qv, pool, block_table + s * max_blocks_per_seq, h / G, first,
+                   context_lens[s], scale, &m, &l, acc, z, krow, vrow);
       double* o = out + (i * num_q_heads + h) * D;
       for (int64_t d = 0; d < D; ++d) o[d] = l > 0 ? acc[d] / l : 0.0;
       if (lse) lse[i * num_q_heads + h] = l > 0 ? m + log(l) : -INFINITY;

@@ -128,11 +128,16 @@ typedef struct orc_pool {
  * to compute (NULL: all, n_sel ignored).  out: [n_sel][num_q_heads][head_dim];
  * lse (optional): [n_sel][num_q_heads] natural-log sum-exp of z.
  * Pinned by dense contiguous attention (brute force and a library routine), by the
- * closed forms ctx=1 and q=0, and by block-id permutation invariance. */
+ * closed forms ctx=1 and q=0, and by block-id permutation invariance.
+ * window > 0: [P1 §1.1 table, §7] sliding/local attention, only the keys
+ * t in [max(0, ctx_s - window), ctx_s) are gathered; 0 = the whole context.
+ * Pinned by masked dense attention, window = 1 (out = the newest V row) and by
+ * NaN written into every key before the window. */
 int orc_paged_decode(const void* q, int q_dtype, int64_t num_seqs, int64_t num_q_heads,
                      const orc_pool* pool, const int32_t* block_table,
                      int64_t max_blocks_per_seq, const int32_t* context_lens, double scale,
-                     const int32_t* seqs, int64_t n_sel, double* out, double* lse);
+                     int64_t window, const int32_t* seqs, int64_t n_sel, double* out,
+                     double* lse);
 
 /* [P1 §4] split-KV: partition i of sequence s covers tokens
  * [i*P, min((i+1)*P, ctx_s)).  For each non-empty partition:

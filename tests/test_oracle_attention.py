@@ -311,3 +311,67 @@ def test_prefill_with_cache_is_bottom_right_causal():
     dec_q = np.stack([qs[0][-1], qs[1][-1]])
     dec = oracle.paged_decode(dec_q, "f16", case["pool"], case["table"], case["ctx"], 0.125)
     assert np.array_equal(nc[[cu[1] - 1, cu[2] - 1]], dec)
+
+
+# --------------------------------------------------------------------------------------
+# Sliding window ("03 | PagedAttention and the KV-cache memory system" §1.1 table:
+# sliding/local attention keeps and uses only the tokens inside the window; §7: at
+# position p the window is [p - w + 1, p], and blocks before it may be released)
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("kv_dtype,Hq,Hkv,D,B,w", [
+    ("bf16", 8, 2, 128, 16, 37), ("f32", 4, 2, 64, 4, 5), ("fp8", 8, 1, 128, 16, 100),
+    ("f16", 4, 4, 64, 32, 64)])
+def test_window_decode_equals_masked_sdpa(kv_dtype, Hq, Hkv, D, B, w):
+    """Against the library routine on the keys of [ctx - w, ctx) only."""
+    rng = np.random.default_rng(500 + w + B)
+    ctxs = [1, w - 1, w, w + 1, 2 * w + 3, 5 * B + 7, 300]
+    case = _paged_case(rng, ctxs, Hq, Hkv, D, B, kv_dtype)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.paged_decode(case["q"], case["q_dtype"], case["pool"], case["table"],
+                              case["ctx"], scale, window=w)
+    for s, c in enumerate(ctxs):
+        q = _values(case["q"][s], case["q_dtype"])
+        lo = max(0, c - w)
+        K = _contiguous_values(case, s, "k")[lo:].permute(1, 0, 2)[None]
+        V = _contiguous_values(case, s, "v")[lo:].permute(1, 0, 2)[None]
+        ref = F.scaled_dot_product_attention(q[None, :, None, :], K, V, scale=scale,
+                                             enable_gqa=True)[0, :, 0, :].numpy()
+        np.testing.assert_allclose(got[s], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_window_of_one_is_the_newest_value_row():
+    rng = np.random.default_rng(77)
+    case = _paged_case(rng, [1, 9, 40], 4, 2, 64, 8, "bf16")
+    got = oracle.paged_decode(case["q"], case["q_dtype"], case["pool"], case["table"],
+                              case["ctx"], 0.125, window=1)
+    for s, c in enumerate([1, 9, 40]):
+        v_last = _contiguous_values(case, s, "v")[c - 1].numpy()  # [Hkv][D]
+        np.testing.assert_array_equal(got[s], np.repeat(v_last, 2, axis=0))
+
+
+def test_window_never_reads_keys_before_it():
+    """NaN written into every K/V slot older than each sequence's window leaves the
+    windowed output finite and unchanged, while the whole-context decode sees it."""
+    rng = np.random.default_rng(78)
+    ctxs = [70, 129, 16, 300]
+    w = 48
+    case = _paged_case(rng, ctxs, 8, 2, 64, 16, "bf16")
+    pool, B = case["pool"], 16
+    scale = 0.125
+    before = oracle.paged_decode(case["q"], "bf16", pool, case["table"], case["ctx"], scale,
+                                 window=w)
+    full_before = oracle.paged_decode(case["q"], "bf16", pool, case["table"], case["ctx"], scale)
+    for s, c in enumerate(ctxs):
+        for t in range(max(0, c - w)):
+            blk, off = case["table"][s, t // B], t % B
+            pool.k[blk, :, off, :] = NAN_BITS["bf16"]
+            pool.v[blk, :, off, :] = NAN_BITS["bf16"]
+    after = oracle.paged_decode(case["q"], "bf16", pool, case["table"], case["ctx"], scale,
+                                window=w)
+    assert np.isfinite(after).all()
+    np.testing.assert_array_equal(after, before)
+    # the whole-context decode does read those slots (sequence 2 has none before its window)
+    full = oracle.paged_decode(case["q"], "bf16", pool, case["table"], case["ctx"], scale)
+    for s in (0, 1, 3):
+        assert not np.array_equal(full[s], full_before[s])
+    np.testing.assert_array_equal(full[2], full_before[2])
