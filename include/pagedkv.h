@@ -256,6 +256,27 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
                                int32_t max_context_len, float scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* out, void* stream);
 
+/* [P1 §1.1 table, §7] Sliding-window (local) decode: as pkv_paged_attention_decode,
+ * but the query of sequence s (at position p = ctx_s - 1) sees only the keys of
+ * its window [p - window + 1, p], i.e. t in [max(0, ctx_s - window), ctx_s).
+ * Blocks entirely older than the window are never read and their table entries
+ * may hold anything (the allocator may have released them): with block_size >=
+ * 16 the kernels start at the window's first 16-token tile, which lies in that
+ * key's own block; with smaller blocks every token below the window is replaced
+ * by the window's first key before its block is looked up.  window = 0 is the
+ * whole context (pkv_paged_attention_decode is this call with window 0).  Same
+ * arguments, partition modes, workspace sizes and errors otherwise; window < 0
+ * is PKV_EINVAL. */
+int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                      int32_t num_q_heads, const pkv_pool_desc* pool,
+                                      const void* k_pool, const void* v_pool,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      float scale, int32_t window, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* out,
+                                      void* stream);
+
 /* Decode for a batch whose sequences share a prefix of blocks ([P1] §5: two
  * requests that hit the same prefix pages point their block tables at the same
  * physical blocks, with reference counts; [P3] section 4, block-level sharing:

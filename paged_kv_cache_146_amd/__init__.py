@@ -40,7 +40,7 @@ EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_alloc_add_seq", "pkv_alloc_fork", "pkv_alloc_append", "pkv_alloc_free_seq",
            "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
            "pkv_copy_blocks", "pkv_decode_shared_workspace_bytes",
-           "pkv_paged_attention_decode_shared"]
+           "pkv_paged_attention_decode_shared", "pkv_paged_attention_decode_window"]
 
 
 class PagedKVError(RuntimeError):
@@ -96,6 +96,10 @@ def lib():
                     "pkv_split_kv_reduce": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I32, I32, P,
                                                            I32, P]),
                     "pkv_decode_shared_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32,
+                                                                         P]),
+                    "pkv_paged_attention_decode_window": (ctypes.c_int, [P, I32, I32, I32, P, P, P,
+                                                                         P, P, P, I32, P, I32,
+                                                                         F, I32, I32, P, SZ, P,
                                                                          P]),
                     "pkv_paged_attention_decode_shared": (ctypes.c_int, [P, I32, I32, I32, P, P, P,
                                                                          P, P, P, I32, P, I32,
@@ -431,6 +435,33 @@ def pkv_paged_attention_decode_shared(q, desc: PoolDesc, k_pool, v_pool, block_t
         int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
         int(shared_len), float(scale), _ptr(workspace, "workspace"), ws_bytes, _ptr(out, "out"),
         _stream(stream)), "pkv_paged_attention_decode_shared")
+    return out
+
+
+def pkv_paged_attention_decode_window(q, desc: PoolDesc, k_pool, v_pool, block_table,
+                                      context_lens, max_context_len: int, scale: float,
+                                      window: int, partition_size: int = 0, k_scale=None,
+                                      v_scale=None, workspace=None, out=None, q_dtype=None,
+                                      stream=None):
+    """Sliding-window decode: sequence s sees the keys [max(0, ctx_s - window), ctx_s)."""
+    torch = _torch()
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    need = pkv_decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim, max_context_len,
+                                      partition_size)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    _check(lib().pkv_paged_attention_decode_window(
+        _ptr(q, "q"), qd, S, Hq, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
+        _ptr(v_pool, "v_pool"), _ptr(k_scale, "k_scale", allow_none=True),
+        _ptr(v_scale, "v_scale", allow_none=True), _ptr(block_table, "block_table"),
+        int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
+        float(scale), int(window), int(partition_size),
+        _ptr(workspace, "workspace", allow_none=True), ws_bytes, _ptr(out, "out"),
+        _stream(stream)), "pkv_paged_attention_decode_window")
     return out
 
 

@@ -356,8 +356,25 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
                                int32_t max_context_len, float scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* out,
                                void* stream) {
+  return pkv_paged_attention_decode_window(q, q_dtype, num_seqs, num_q_heads, pool, k_pool,
+                                           v_pool, k_scale, v_scale, block_table,
+                                           max_blocks_per_seq, context_lens, max_context_len,
+                                           scale, 0, partition_size, workspace, workspace_bytes,
+                                           out, stream);
+}
+
+int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                      int32_t num_q_heads, const pkv_pool_desc* pool,
+                                      const void* k_pool, const void* v_pool,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      float scale, int32_t window, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* out,
+                                      void* stream) {
   int rc = check_desc(pool);
   if (rc != PKV_OK) return rc;
+  if (window < 0) return PKV_EINVAL;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
     return PKV_EINVAL;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
@@ -397,6 +414,7 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.ctx_cap = (int)cap;
   p.scale = scale;
+  p.window = window;
 
   if (balanced) return launch_balanced(p, workspace, workspace_bytes, stream);
 

@@ -82,7 +82,17 @@ struct DecodeScalars {
   float* tail_out;
   float* tail_max;
   float* tail_sum;
+  int window;       // > 0: a sequence of context c sees only the keys [c - window, c)
 };
+
+// The oldest key a sequence of (clamped) context ctx sees, and where its chunk grid
+// starts: that key rounded down to a 16-token tile.  With block_size >= 16 the tile
+// lies in the key's own block, so no table entry of an older block is ever read
+// (those blocks may have been released); the keys of the tile older than the
+// window are masked.
+__device__ __forceinline__ int window_lo(int ctx, int window) {
+  return window > 0 && ctx > window ? ctx - window : 0;
+}
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -185,11 +195,13 @@ __device__ __forceinline__ void q_live(typename C::QOp (&dst)[C::NQ],
 // visible block (their values are masked).
 struct Pages {
   int b[4];
+  int off;  // base mod block_size: tile T starts at offset (off + 16 T) mod block_size
 };
 
 __device__ __forceinline__ Pages pages_of(const int32_t* __restrict__ trow, int base, int end,
                                           const DecodeScalars& sc) {
   Pages pg;
+  pg.off = uniform(base & ((1 << sc.blog2) - 1));
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const int t = uniform(min(base + 16 * T, end - 1));
@@ -207,7 +219,7 @@ __device__ __forceinline__ void issue_k(u32x4 (&kr)[C::NK], const uint8_t* __res
   for (int T = 0; T < 4; ++T) {
     const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
     const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B +
-                      ((16 * T) & (B - 1)) + n + (size_t)g * B;
+                      ((pg.off + 16 * T) & (B - 1)) + n + (size_t)g * B;
 #pragma unroll
     for (int pq = 0; pq < C::NPL; ++pq) kr[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
   }
@@ -222,7 +234,8 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
-    const uint8_t* vp = v_pool + ((page * C::Dim + n) * B + ((16 * T) & (B - 1)) + 4 * g) * C::EB;
+    const uint8_t* vp =
+        v_pool + ((page * C::Dim + n) * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g) * C::EB;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
       vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * B * C::EB);
@@ -248,7 +261,7 @@ __device__ __forceinline__ void chunk_scales(float (&ks)[16], float (&vs)[16],
   for (int T = 0; T < 4; ++T) {
     const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
     if (sc.scale_mode == SCALE_TOKEN) {
-      const size_t i0 = page * B + ((16 * T) & (B - 1)) + 4 * g;
+      const size_t i0 = page * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ks[4 * T + r] = k_scale[i0 + r];
@@ -274,11 +287,14 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
                                            const float* __restrict__ k_scale,
                                            const float* __restrict__ v_scale,
                                            const int32_t* __restrict__ trow, int base, int end,
-                                           int kvh, const DecodeScalars& sc, int n, int g) {
+                                           int kvh, const DecodeScalars& sc, int n, int g,
+                                           int lo = 0) {
+  // tokens outside [lo, end) load the nearest visible one instead (masked later):
+  // the blocks outside may have been released
   const int B = 1 << sc.blog2;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    const int t = min(base + 16 * T + n, end - 1);
+    const int t = max(min(base + 16 * T + n, end - 1), lo);
     const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
     const u32x4* kp =
         reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B + (t & (B - 1)) + (size_t)g * B;
@@ -295,7 +311,7 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * T + e;  // the lane's score index of this token
-      const int t = min(base + 16 * T + 4 * g + e, end - 1);
+      const int t = max(min(base + 16 * T + 4 * g + e, end - 1), lo);
       const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
       if constexpr (C::EB == 1) {  // quantised
         const size_t si = scale_at(sc, page, t & (B - 1));
@@ -388,12 +404,16 @@ __device__ __forceinline__ void mask_v(typename C::VPiece (&vr)[C::NV], int nval
 // Scores x[4 T + r] belong to token 16 T + 4 g + r, and so do the scales ks[4 T + r]
 // and vs[4 T + r] of a quantised pool.  Keys from nvalid on (wave-uniform) are
 // past the context of every column.  COLMASK: the lane's column also hides the
-// keys from xvalid on, and may see no key of the chunk at all.
+// keys from xvalid on, and may see no key of the chunk at all.  Keys below nlow
+// (wave-uniform; the first chunk of a sliding window) are older than the window:
+// their values are finite (the window's own first tile, or a clamped load) and
+// only their scores are masked.
 template <class C, int KVT, int CT, bool COLMASK = false>
 __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[4],
                                                  typename C::VPiece (&vr)[C::NV], float zscale,
                                                  const float (&ks)[16], float (&vs)[16],
-                                                 int nvalid, int g, int xvalid = 64) {
+                                                 int nvalid, int g, int xvalid = 64,
+                                                 int nlow = 0) {
   constexpr bool kFp8 = (KVT == DT_FP8 || KVT == DT_I8);  // quantised: scaled 8-bit codes
   float x[16];
 #pragma unroll
@@ -416,6 +436,11 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
         if constexpr (kFp8) vs[4 * T + r] = live ? vs[4 * T + r] : 0.0f;
       }
     mask_v<C>(vr, nvalid, g);
+  }
+  if (nlow > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      x[i] = 16 * (i >> 2) + 4 * g + (i & 3) >= nlow ? x[i] : -INFINITY;
   }
   if constexpr (COLMASK) {
     if (xvalid < 64) {
@@ -519,13 +544,25 @@ paged_decode_kernel(
 
   int ctx = context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > sc.ctx_cap ? sc.ctx_cap : ctx);
-  const int t_begin = part * sc.part_size;
-  const int t_end = min(t_begin + sc.part_size, ctx);
+  const int lo = window_lo(ctx, sc.window);
+  const int t_begin = max(part * sc.part_size, lo & ~15);
+  const int t_end = min(part * sc.part_size + sc.part_size, ctx);
   if (t_begin >= t_end) {
     if (!sc.split && part == 0) {  // empty context: zeros
       for (int i = threadIdx.x; i < sc.G * D; i += kThreads) {
         size_t o = ((size_t)s * sc.Hq + (size_t)kvh * sc.G) * D + i;
         store_any(out, sc.out_dtype, o, 0.0f);
+      }
+    } else if (sc.split && part * sc.part_size < ctx) {
+      // a partition older than the window: an empty state for the merge
+      for (int i = threadIdx.x; i < sc.G * D; i += kThreads) {
+        const int h = i / D, d = i - h * D;
+        const size_t pi = ((size_t)s * sc.Hq + (size_t)kvh * sc.G + h) * sc.max_parts + part;
+        part_out[pi * D + d] = 0.0f;
+        if (d == 0) {
+          part_max[pi] = -INFINITY;
+          part_sum[pi] = 0.0f;
+        }
       }
     }
     return;
@@ -546,10 +583,12 @@ paged_decode_kernel(
       const int base = base_of(i);
       Chunk<C> ch;
       float ks[16], vs[16];
-      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g);
+      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g,
+                    lo);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
-      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g);
+      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g,
+                                   64, lo - base);
     }
   } else if (cnt > 0) {
     // Single-buffered pipeline: chunk i+1's K pieces are requested as soon as
@@ -585,7 +624,7 @@ paged_decode_kernel(
       }
       issue_point();
       chunk_softmax_pv<C, KVT, CT>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0),
-                                       g);
+                                   g, 64, lo - b0);
       issue_point();
       if (more) issue_v<C>(R.v, v_pool, p1, kvh, sc, n, g);
       issue_point();
@@ -646,7 +685,7 @@ paged_decode_kernel(
 // exclusive prefix of per-sequence unit counts into lds[0..S], by one workgroup:
 // tiles of 256 sequences, each scanned by wave shuffles plus the wave totals
 __device__ void unit_prefix(const int32_t* __restrict__ context_lens, int S, int ctx_off,
-                            int ctx_cap, int Hkv, int* lds, int* tmp) {
+                            int ctx_cap, int window, int Hkv, int* lds, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int carry = 0;
   for (int base = 0; base < S; base += kThreads) {
@@ -656,6 +695,7 @@ __device__ void unit_prefix(const int32_t* __restrict__ context_lens, int S, int
       int c = context_lens[s];
       c = c < ctx_off ? 0 : c - ctx_off;
       c = c > ctx_cap ? ctx_cap : c;
+      c -= window_lo(c, window) & ~15;  // keys from the window's first tile on
       v = ((c + 63) >> 6) * Hkv;
     }
     int x = v;  // inclusive scan inside the wave
@@ -786,9 +826,10 @@ __device__ void merge_pair(float* slot_out, float* slot_ml, uint8_t* __restrict_
 }
 
 // where a worker is in the unit stream: unit u = chunk j of pair (s, kvh), the
-// k-th unit of the worker's share
+// k-th unit of the worker's share; the chunk covers keys [st + 64 j, st + 64 j + 64)
+// of which those below lo (a sliding window's) and from ctx on are masked
 struct Pos {
-  int u, s, kvh, j, nch, ctx, k;
+  int u, s, kvh, j, nch, ctx, k, lo, st;
 };
 
 template <int KVT, int CT, int D, bool SMALLB>
@@ -805,7 +846,7 @@ paged_decode_balanced_kernel(
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
 
-  unit_prefix(context_lens, sc.S, sc.ctx_off, sc.ctx_cap, sc.Hkv, prefix, tmp);
+  unit_prefix(context_lens, sc.S, sc.ctx_off, sc.ctx_cap, sc.window, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
   if (blockIdx.x == 0) {  // sequences with an empty context own no unit: their output is zero
     for (int s0 = 0; s0 < sc.S; ++s0) {
@@ -851,6 +892,8 @@ paged_decode_balanced_kernel(
     p.kvh = rel / p.nch;
     p.j = rel - p.kvh * p.nch;
     p.ctx = clamp_ctx(p.s);
+    p.lo = uniform(window_lo(p.ctx, sc.window));
+    p.st = p.lo & ~15;
     return p;
   };
   // the unit after p, or p itself at the end of the share (its loads are then
@@ -877,6 +920,8 @@ paged_decode_balanced_kernel(
     p.s = uniform(p.s);
     p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
     p.ctx = clamp_ctx(p.s);
+    p.lo = uniform(window_lo(p.ctx, sc.window));
+    p.st = p.lo & ~15;
     return p;
   };
   // a piece ends at the last chunk of its pair or of the worker's share
@@ -975,12 +1020,13 @@ paged_decode_balanced_kernel(
       const Pos pn = advance(pc);
       Chunk<C> ch;
       float ks[16], vs[16];
-      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow_of(pc), 64 * pc.j, pc.ctx,
-                    pc.kvh, sc, n, g);
+      const int base = pc.st + 64 * pc.j;
+      load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow_of(pc), base, pc.ctx,
+                    pc.kvh, sc, n, g, pc.lo);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
-      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs,
-                                       min(64, pc.ctx - 64 * pc.j), g);
+      chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, pc.ctx - base),
+                                   g, 64, pc.lo - base);
       const bool done = pc.k + 1 >= n_units;
       if (done || piece_ends(pc)) {
         finish_piece(pc);
@@ -1016,7 +1062,9 @@ paged_decode_balanced_kernel(
       issue_v<C>(dst.v, v_pool, pg, p.kvh, sc, n, g);
       if constexpr (kFp8) chunk_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc, g);
     };
-    auto pages_at = [&](const Pos& p) { return pages_of(trow_of(p), 64 * p.j, p.ctx, sc); };
+    auto pages_at = [&](const Pos& p) {
+      return pages_of(trow_of(p), p.st + 64 * p.j, p.ctx, sc);
+    };
 #pragma unroll
     for (int k = 0; k + 1 < NB; ++k) {
       if (k > 0) pp[k] = advance(pp[k - 1]);
@@ -1049,8 +1097,9 @@ paged_decode_balanced_kernel(
       const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
       if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
       issue_point();
+      const int base0 = p0.st + 64 * p0.j;
       chunk_softmax_pv<C, KVT, CT>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
-                                       min(64, p0.ctx - 64 * p0.j), g);
+                                   min(64, p0.ctx - base0), g, 64, p0.lo - base0);
       issue_point();
       if (last || piece_ends(p0)) {
         finish_piece(p0);
@@ -1380,6 +1429,7 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.tail_out = p.tail_out;
   sc.tail_max = p.tail_max;
   sc.tail_sum = p.tail_sum;
+  sc.window = p.window;
   return sc;
 }
 

@@ -43,6 +43,7 @@ struct DecodeLaunch {
   // n_slices-1 of stride max_parts)
   int prefix = 0;
   int shared_len = 0, n_slices = 0, slice_chunks = 0;
+  int window = 0;  // > 0: sliding-window decode (keys [ctx - window, ctx))
 };
 
 // Wavefront workers the balanced decode can keep resident on the current device

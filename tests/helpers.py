@@ -99,11 +99,17 @@ class GpuCase:
         out.view(torch.uint8).fill_(0xFF)
         return out
 
-    def decode(self, partition_size=None, out=None, workspace=None):
+    def decode(self, partition_size=None, out=None, workspace=None, window=None):
         import paged_kv_cache_146_amd as pkv
         P = self.wl.partition_size if partition_size is None else partition_size
         if out is None:
             out = self.nan_out()
+        if window is not None:
+            return pkv.pkv_paged_attention_decode_window(
+                self.q, self.desc, self.k_pool, self.v_pool, self.block_table,
+                self.context_lens, self.wl.max_context_len, self.wl.scale, window,
+                partition_size=P, k_scale=self.k_scale, v_scale=self.v_scale, out=out,
+                q_dtype=self.wl.q_dtype, workspace=workspace)
         return pkv.pkv_paged_attention_decode(
             self.q, self.desc, self.k_pool, self.v_pool, self.block_table, self.context_lens,
             self.wl.max_context_len, self.wl.scale, partition_size=P, k_scale=self.k_scale,
