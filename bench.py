@@ -64,6 +64,8 @@ def parse():
                          "same bf16 draws as codes with fp32 scales)")
     ap.add_argument("--scale-mode", choices=["block", "tensor", "token"], default="block",
                     help="decode workload with a quantised pool: where the scales live")
+    ap.add_argument("--window", type=int, default=0,
+                    help="decode workload: sliding window (keys [ctx - window, ctx)); 0 = all")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a 512 MiB device copy five times (a kernel of known HBM "
                          "traffic) so that rocprofv3's FETCH_SIZE/WRITE_SIZE can be scaled")
@@ -90,12 +92,24 @@ DEFAULT_PARTITION = -1  # balanced split-KV
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}  # pool bytes per element
 
 
-def decode_bytes(wl) -> int:
+def decode_bytes(wl, window=0) -> int:
     """Algorithmic bytes of one decode launch: every K/V element of every sequence's
-    context once, q and out once, the used block-table entries and the lengths."""
+    visible keys once (the whole context, or its sliding window), q and out once, the
+    used block-table entries and the lengths."""
     e = 2  # bf16
-    nblk = sum(math.ceil(int(c) / wl.block_size) for c in wl.context_lens)
-    return (wl.kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * e
+    if window <= 0:
+        nblk = sum(math.ceil(int(c) / wl.block_size) for c in wl.context_lens)
+        return (wl.kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * e
+                + 4 * nblk + 4 * wl.num_seqs)
+    row = 2 * wl.num_kv_heads * wl.head_dim * W_ELEM[wl.kv_dtype]
+    vis = sum(min(int(c), window) for c in wl.context_lens)
+    nblk = sum(math.ceil(int(c) / wl.block_size) - max(0, int(c) - window) // wl.block_size
+               for c in wl.context_lens)
+    scales = 0
+    if wl.kv_dtype in ("fp8", "int8"):
+        scales = {"block": nblk * 2 * wl.num_kv_heads * 4,
+                  "token": vis * 2 * wl.num_kv_heads * 4}.get(wl.scale_mode, 8)
+    return (vis * row + scales + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * e
             + 4 * nblk + 4 * wl.num_seqs)
 
 
@@ -170,9 +184,14 @@ def main():
     torch.cuda.synchronize()
 
     def decode():
-        pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
-                                       wl.scale, partition_size=P, k_scale=ks, v_scale=vs,
-                                       workspace=ws, out=out, q_dtype="bf16")
+        if a.window > 0:
+            pkv.pkv_paged_attention_decode_window(
+                q, desc, k_pool, v_pool, bt, cl, wl.max_context_len, wl.scale, a.window,
+                partition_size=P, k_scale=ks, v_scale=vs, workspace=ws, out=out, q_dtype="bf16")
+        else:
+            pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
+                                           wl.scale, partition_size=P, k_scale=ks, v_scale=vs,
+                                           workspace=ws, out=out, q_dtype="bf16")
 
     def step():
         # slot mapping and scatter of the new tokens in one launch (the slots are
@@ -213,7 +232,7 @@ def main():
         opool = _oracle_pool(oracle, wl)
         sel = np.array([0, int(np.argmax(wl.context_lens))], np.int32)
         ref = oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
-                                  seqs=sel)
+                                  seqs=sel, window=a.window)
         got = out.float().cpu().numpy().astype(np.float64)[sel]
         err = np.abs(got - ref)
         parity = {"seqs": sel.tolist(), "max_abs": float(err.max()),
@@ -223,7 +242,7 @@ def main():
 
     step_us = float(np.mean(step_ms) * 1e3)
     dec_us = float(np.mean(dec_ms) * 1e3)
-    dbytes = decode_bytes(wl)
+    dbytes = decode_bytes(wl, a.window)
     sbytes = dbytes + write_bytes(wl)
     achieved = dbytes / (dec_us * 1e-6) / 1e9
     traffic = None
@@ -231,7 +250,7 @@ def main():
         c = json.load(open(COUNTERS))
         src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
         if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
-                and c.get("kv_dtype", "bf16") == wl.kv_dtype
+                and a.window == 0 and c.get("kv_dtype", "bf16") == wl.kv_dtype
                 and c.get("scale_mode", "block") == wl.scale_mode):
             traffic = c.get("hbm_bytes_per_launch")
 
@@ -258,6 +277,7 @@ def main():
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
             "kv_dtype": wl.kv_dtype,
             "scale_mode": wl.scale_mode if wl.kv_dtype in ("fp8", "int8") else None,
+            "window": a.window if a.window > 0 else None,
             "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
             "step": "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) + paged_attention_decode",
@@ -277,7 +297,7 @@ def main():
         "parity_spot_check": parity,
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds, a.window)
     print(json.dumps(res), flush=True)
 
 
@@ -682,7 +702,7 @@ def _oracle_pool(oracle, wl):
     return opool
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_baseline(wl, budget_s, window=0):
     """The oracle as it stands, on the same workload, on this host's cores: the write of
     the 64 new tokens plus decode attention for a bounded prefix of the sequences."""
     import oracle
@@ -694,11 +714,12 @@ def cpu_baseline(wl, budget_s):
         t0 = time.perf_counter()
         s_new = oracle.slot_mapping(wl.block_table, order, wl.context_lens - 1, wl.block_size)
         oracle.kv_cache_write(opool, s_new, wl.k_src[rows], wl.v_src[rows], "bf16")
-        oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale)
+        oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
+                            window=window)
         t_used += time.perf_counter() - t0
         steps += 1
     step_s = t_used / steps
-    step_bytes = decode_bytes(wl) + write_bytes(wl)
+    step_bytes = decode_bytes(wl, window) + write_bytes(wl)
     return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d whole steps of the same workload (write of the 64 new tokens + decode "

@@ -41,6 +41,7 @@
  *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
  *   scales of a quantised pool (K and V separately): float arrays whose shape
  *   the descriptor's scale_mode sets (pkv_scale_mode below)
+ * (block strides other than the dense one: see pkv_pool_desc.block_stride).
  * One (block, kv head) page is contiguous in each pool.  The logical element
  * K[block][head][t][d] lives at K pool index
  *   (((block*num_kv_heads + head)*(head_dim/X) + d/X)*block_size + t)*X + d%X
@@ -105,6 +106,13 @@ typedef struct pkv_pool_desc {
   int32_t head_dim;     /* D */
   int32_t kv_dtype;     /* pkv_dtype */
   int32_t scale_mode;   /* pkv_scale_mode: quantised pools; 0 for the others */
+  /* [P1 §3.1] bytes from block b to block b + 1 in each pool; 0 = dense
+   * (num_kv_heads pages of block_size * head_dim elements).  A larger stride,
+   * a multiple of 16, lets one allocation hold every layer's K and V of a block
+   * together ("cross-layer" blocks, [block][layer][K|V][kv head][page]): layer
+   * l's k_pool / v_pool point at its K / V pages of block 0 and the stride is
+   * the whole block.  All layers share the block ids (and a block table). */
+  int64_t block_stride;
 } pkv_pool_desc;
 
 /* Human-readable text of a status code (static storage). */
@@ -116,7 +124,9 @@ int pkv_version(void);
 /* [P1 §3.1] Bytes of the K pool and the V pool:
  *   num_blocks * num_kv_heads * block_size * head_dim * E  each,
  * i.e. the per-layer page size 2*block_size*num_kv_heads*head_dim*E split
- * into K and V; for quantised pools also the bytes of ONE scale array in the
+ * into K and V; with a block_stride, the span one pool pointer addresses,
+ * (num_blocks - 1) * block_stride + num_kv_heads * block_size * head_dim * E;
+ * for quantised pools also the bytes of ONE scale array in the
  * descriptor's scale mode ([P1 §8.1]: the scales count in the page size), else
  * 0.  Any output pointer may be NULL.
  * Errors: PKV_EINVAL for a NULL/invalid descriptor, PKV_EUNSUPPORTED for a

@@ -53,13 +53,14 @@ class PagedKVError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("block_stride", ctypes.c_int64)]
 
     def __repr__(self):
         return ("PoolDesc(num_blocks=%d, block_size=%d, num_kv_heads=%d, head_dim=%d, "
-                "kv_dtype=%d, scale_mode=%d)" % (self.num_blocks, self.block_size,
-                                                 self.num_kv_heads, self.head_dim,
-                                                 self.kv_dtype, self.scale_mode))
+                "kv_dtype=%d, scale_mode=%d, block_stride=%d)"
+                % (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
+                   self.kv_dtype, self.scale_mode, self.block_stride))
 
 
 _lock = threading.Lock()
@@ -188,11 +189,12 @@ def pkv_version() -> int:
 
 
 def pool_desc(num_blocks, block_size, num_kv_heads, head_dim, kv_dtype,
-              scale_mode=PKV_SCALE_BLOCK) -> PoolDesc:
+              scale_mode=PKV_SCALE_BLOCK, block_stride=0) -> PoolDesc:
+    """block_stride: bytes from one block to the next in each pool (0 = dense)."""
     code = dtype_code(kv_dtype) if not isinstance(kv_dtype, int) else kv_dtype
     mode = SCALE_MODES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
     return PoolDesc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim), code,
-                    mode)
+                    mode, int(block_stride))
 
 
 def pkv_pool_bytes(desc: PoolDesc):

@@ -41,6 +41,14 @@ size_t scale_count(const pkv_pool_desc* d) {
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// 16-byte units from one block to the next in each pool (of a validated descriptor)
+long long block_units(const pkv_pool_desc* d) {
+  const int64_t bytes = d->block_stride ? d->block_stride
+                                        : (int64_t)d->num_kv_heads * d->block_size *
+                                              d->head_dim * elem_bytes(d->kv_dtype);
+  return (long long)(bytes / 16);
+}
+
 // Descriptor validation ("KV Cache: capacity, layout, lifecycle", correctness
 // contract: a mismatched descriptor is rejected, never reinterpreted).
 int check_desc(const pkv_pool_desc* d) {
@@ -54,6 +62,11 @@ int check_desc(const pkv_pool_desc* d) {
   if ((d->head_dim * elem_bytes(d->kv_dtype)) % 16 != 0) return PKV_EINVAL;
   if (!pow2(d->block_size) || d->block_size > 64) return PKV_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
+  // a block stride leaves room for at least the block's own pages, in 16-byte steps
+  const int64_t dense = (int64_t)d->num_kv_heads * d->block_size * d->head_dim *
+                        elem_bytes(d->kv_dtype);
+  if (d->block_stride != 0 && (d->block_stride < dense || d->block_stride % 16 != 0))
+    return PKV_EINVAL;
   // page-aligned pools: total element count must fit the kernels' index math
   const double rows = (double)d->num_blocks * d->num_kv_heads * d->block_size;
   if (rows >= 4294967296.0) return PKV_EUNSUPPORTED;
@@ -101,8 +114,11 @@ int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
                    size_t* scale_bytes_each) {
   int rc = check_desc(pool);
   if (rc != PKV_OK) return rc;
-  const size_t e = (size_t)pool->num_blocks * pool->num_kv_heads * pool->block_size *
-                   pool->head_dim * elem_bytes(pool->kv_dtype);
+  const size_t block = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
+                       elem_bytes(pool->kv_dtype);
+  const size_t e = pool->block_stride
+                       ? (size_t)(pool->num_blocks - 1) * pool->block_stride + block
+                       : (size_t)pool->num_blocks * block;
   if (k_bytes) *k_bytes = e;
   if (v_bytes) *v_bytes = e;
   if (scale_bytes_each)
@@ -200,6 +216,7 @@ pkv::WriteLaunch write_launch(int32_t num_tokens, const void* k, const void* v, 
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
   p.scale_mode = pool->scale_mode;
+  p.bstride = block_units(pool);
   return p;
 }
 
@@ -257,7 +274,7 @@ int pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_pool_desc
   rc = pkv::launch_copy_blocks(pairs, num_pairs, k_pool, v_pool, k_scale, v_scale,
                                pool->num_blocks, pool->block_size, pool->num_kv_heads,
                                pool->head_dim, pool->kv_dtype, pool->scale_mode,
-                               as_stream(stream));
+                               block_units(pool), as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }
 
@@ -409,6 +426,7 @@ int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t nu
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
   p.scale_mode = pool->scale_mode;
+  p.bstride = block_units(pool);
   p.block_size = pool->block_size;
   p.num_blocks = pool->num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
@@ -540,6 +558,7 @@ int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t nu
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
   p.scale_mode = pool->scale_mode;
+  p.bstride = block_units(pool);
   p.block_size = pool->block_size;
   p.num_blocks = pool->num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
@@ -668,6 +687,7 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
   p.num_kv_heads = pool->num_kv_heads;
   p.head_dim = pool->head_dim;
   p.kv_dtype = pool->kv_dtype;
+  p.bstride = block_units(pool);
   p.block_table = block_table;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.context_lens = context_lens;

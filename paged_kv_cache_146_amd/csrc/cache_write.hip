@@ -76,7 +76,7 @@ template <int ES>
 __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
     const SlotSource ss, int num_tokens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-    int num_blocks, int B, int Hkv, int D) {
+    int num_blocks, int B, int Hkv, int D, long long bstride) {
   const int NC = D * ES / 16;  // pieces per row
   const long long total = (long long)num_tokens * Hkv * NC;
   const long long idx = (long long)blockIdx.x * kWriteThreads + threadIdx.x;
@@ -90,14 +90,15 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
   if (slot < 0 || slot >= (long long)num_blocks * B) return;
   const long long blk = slot / B, off = slot % B;
   const size_t src = ((size_t)i * Hkv + h) * NC + c;  // in 16-byte pieces
-  const size_t page = (size_t)blk * Hkv + h;
+  constexpr int E = 16 / ES;
+  const size_t blk16 = (size_t)blk * (size_t)bstride;  // where the block starts, 16-byte units
   if (blockIdx.y == 0) {
-    reinterpret_cast<u32x4*>(k_pool)[(page * NC + c) * B + off] =
+    reinterpret_cast<u32x4*>(k_pool)[blk16 + ((size_t)h * NC + c) * B + off] =
         reinterpret_cast<const u32x4*>(k)[src];
   } else {
-    constexpr int E = 16 / ES;
     const u32x4 x = reinterpret_cast<const u32x4*>(v)[src];
-    const size_t d0 = (page * D + (size_t)c * E) * B + off;  // element (dim c E, token off)
+    // element (dim c E, token off)
+    const size_t d0 = blk16 * E + ((size_t)h * D + (size_t)c * E) * B + off;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t w = x[e * ES / 4];
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_quant_kernel(
     const SlotSource ss, int num_tokens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ v, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale, int scale_mode,
-    int num_blocks, int B, int Hkv, int D) {
+    int num_blocks, int B, int Hkv, int D, long long bstride) {
   constexpr int SES = Elem<SRC>::bytes;
   const int NC = D / 16;
   const long long total = (long long)num_tokens * Hkv * NC;
@@ -156,11 +157,13 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_quant_kernel(
     const float y = __fdiv_rn(x[e], scale);
     w[e >> 2] |= (KVT == DT_FP8 ? f32_to_e4m3(y) : f32_to_i8(y)) << (8 * (e & 3));
   }
+  const size_t blk16 = (size_t)blk * (size_t)bstride;  // where the block starts, 16-byte units
   if (!isv) {
     const u32x4 packed = {w[0], w[1], w[2], w[3]};
-    reinterpret_cast<u32x4*>(k_pool)[(page * NC + c) * B + off] = packed;
+    reinterpret_cast<u32x4*>(k_pool)[blk16 + ((size_t)h * NC + c) * B + off] = packed;
   } else {
-    const size_t d0 = (page * D + (size_t)c * 16) * B + off;  // element (dim 16 c, token off)
+    // element (dim 16 c, token off); one-byte codes: 16 elements per 16-byte unit
+    const size_t d0 = blk16 * 16 + ((size_t)h * D + (size_t)c * 16) * B + off;
 #pragma unroll
     for (int e = 0; e < 16; ++e) v_pool[d0 + (size_t)e * B] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
   }
@@ -176,14 +179,14 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_quant_kernel(
 __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
     const int32_t* __restrict__ pairs, int num_pairs, uint8_t* k_pool, uint8_t* v_pool,
     float* k_scale, float* v_scale, int num_blocks, int scales_per_block,
-    long long block_pieces) {
+    long long block_pieces, long long bstride) {
   const int pr = blockIdx.x;
   const int src = pairs[2 * pr], dst = pairs[2 * pr + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
   const bool isv = blockIdx.y != 0;
   u32x4* pool = reinterpret_cast<u32x4*>(isv ? v_pool : k_pool);
-  const u32x4* from = pool + (size_t)src * block_pieces;
-  u32x4* to = pool + (size_t)dst * block_pieces;
+  const u32x4* from = pool + (size_t)src * (size_t)bstride;
+  u32x4* to = pool + (size_t)dst * (size_t)bstride;
   for (long long i = (long long)blockIdx.z * kWriteThreads + threadIdx.x; i < block_pieces;
        i += (long long)gridDim.z * kWriteThreads)
     to[i] = from[i];
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(kWriteThreads) void copy_blocks_kernel(
 
 int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* v_pool,
                        float* k_scale, float* v_scale, int num_blocks, int block_size, int Hkv,
-                       int head_dim, int kv_dtype, int scale_mode, hipStream_t st) {
+                       int head_dim, int kv_dtype, int scale_mode, long long bstride,
+                       hipStream_t st) {
   if (num_pairs == 0) return 0;
   const bool quant = kv_dtype == DT_FP8 || kv_dtype == DT_I8;
   const int ES = kv_dtype == DT_F32 ? 4 : (quant ? 1 : 2);
@@ -208,7 +212,7 @@ int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* 
   dim3 grid((unsigned)num_pairs, 2, (unsigned)(parts < 1 ? 1 : (parts > 64 ? 64 : parts)));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kWriteThreads), 0, st, pairs, num_pairs,
                      (uint8_t*)k_pool, (uint8_t*)v_pool, spb ? k_scale : nullptr,
-                     spb ? v_scale : nullptr, num_blocks, spb, pieces);
+                     spb ? v_scale : nullptr, num_blocks, spb, pieces, bstride);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
@@ -245,16 +249,16 @@ int launch_kv_cache_write(const WriteLaunch& p, hipStream_t st) {
   auto quant_launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWriteThreads), 0, st, ss, p.num_tokens, k, v, kp, vp,
                        p.k_scale, p.v_scale, p.scale_mode, p.num_blocks, p.block_size,
-                       p.num_kv_heads, p.head_dim);
+                       p.num_kv_heads, p.head_dim, p.bstride);
   };
   if (p.kv_dtype == DT_F32)
     hipLaunchKernelGGL(kv_write_copy_kernel<4>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
-                       p.head_dim);
+                       p.head_dim, p.bstride);
   else if (p.kv_dtype == DT_F16 || p.kv_dtype == DT_BF16)
     hipLaunchKernelGGL(kv_write_copy_kernel<2>, grid, dim3(kWriteThreads), 0, st, ss,
                        p.num_tokens, k, v, kp, vp, p.num_blocks, p.block_size, p.num_kv_heads,
-                       p.head_dim);
+                       p.head_dim, p.bstride);
   else if (p.kv_dtype == DT_FP8 && p.src_dtype == DT_BF16)
     quant_launch(kv_write_quant_kernel<DT_BF16, DT_FP8>);
   else if (p.kv_dtype == DT_FP8 && p.src_dtype == DT_F16)

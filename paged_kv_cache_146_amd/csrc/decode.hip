@@ -83,7 +83,13 @@ struct DecodeScalars {
   float* tail_max;
   float* tail_sum;
   int window;       // > 0: a sequence of context c sees only the keys [c - window, c)
+  long long bstride;  // 16-byte units from one block to the next in each pool
 };
+
+// 16-byte unit where block b's K pages start, and element where its V pages start
+__device__ __forceinline__ size_t block_k16(const DecodeScalars& sc, int b) {
+  return (size_t)b * (size_t)sc.bstride;
+}
 
 // The oldest key a sequence of (clamped) context ctx sees, and where its chunk grid
 // starts: that key rounded down to a 16-token tile.  With block_size >= 16 the tile
@@ -217,8 +223,8 @@ __device__ __forceinline__ void issue_k(u32x4 (&kr)[C::NK], const uint8_t* __res
   const int B = 1 << sc.blog2;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B +
+    const size_t page = block_k16(sc, pg.b[T]) + (size_t)kvh * C::NC * B;  // 16-byte units
+    const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + page +
                       ((pg.off + 16 * T) & (B - 1)) + n + (size_t)g * B;
 #pragma unroll
     for (int pq = 0; pq < C::NPL; ++pq) kr[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
@@ -233,9 +239,9 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
   const int B = 1 << sc.blog2;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
-    const uint8_t* vp =
-        v_pool + ((page * C::Dim + n) * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g) * C::EB;
+    const uint8_t* vp = v_pool + block_k16(sc, pg.b[T]) * 16 +
+                        (((size_t)kvh * C::Dim + n) * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g) *
+                            C::EB;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
       vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * B * C::EB);
@@ -295,9 +301,9 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const int t = max(min(base + 16 * T + n, end - 1), lo);
-    const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
-    const u32x4* kp =
-        reinterpret_cast<const u32x4*>(k_pool) + page * C::NC * B + (t & (B - 1)) + (size_t)g * B;
+    const int blk = clamp_block(trow[t >> sc.blog2], sc.num_blocks);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + block_k16(sc, blk) +
+                      (size_t)kvh * C::NC * B + (t & (B - 1)) + (size_t)g * B;
 #pragma unroll
     for (int pq = 0; pq < C::NPL; ++pq) ch.k[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
   }
@@ -312,7 +318,8 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * T + e;  // the lane's score index of this token
       const int t = max(min(base + 16 * T + 4 * g + e, end - 1), lo);
-      const size_t page = (size_t)clamp_block(trow[t >> sc.blog2], sc.num_blocks) * sc.Hkv + kvh;
+      const int blk = clamp_block(trow[t >> sc.blog2], sc.num_blocks);
+      const size_t page = (size_t)blk * sc.Hkv + kvh;  // scale index base
       if constexpr (C::EB == 1) {  // quantised
         const size_t si = scale_at(sc, page, t & (B - 1));
         ks[i] = k_scale[si];
@@ -320,7 +327,8 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
       } else {
         ks[i] = vs[i] = 1.0f;
       }
-      const size_t e0 = (page * C::Dim + n) * B + (t & (B - 1));  // element of dim n
+      // element of dim n
+      const size_t e0 = block_k16(sc, blk) * C::E + ((size_t)kvh * C::Dim + n) * B + (t & (B - 1));
       const int word = e * C::EB / 4, sh = (e * C::EB % 4) * 8;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
@@ -1430,6 +1438,7 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.tail_max = p.tail_max;
   sc.tail_sum = p.tail_sum;
   sc.window = p.window;
+  sc.bstride = p.bstride;
   return sc;
 }
 

@@ -23,6 +23,7 @@ struct DecodeLaunch {
   float* part_sum;
   int num_seqs, num_q_heads, num_kv_heads, head_dim, kv_dtype;
   int scale_mode;     // quantised pools: where an element's scale lives
+  long long bstride;  // 16-byte units from one block to the next in each pool
   int block_size, num_blocks, max_blocks_per_seq;
   int ctx_cap;        // min(max_context_len, max_blocks_per_seq * block_size)
   int part_size;      // > 0: tokens per partition (multiple of 64)
@@ -85,12 +86,14 @@ struct WriteLaunch {
   const float* v_scale;
   int num_blocks, block_size, num_kv_heads, head_dim, kv_dtype;
   int scale_mode;
+  long long bstride;            // 16-byte units from one block to the next
 };
 int launch_kv_cache_write(const WriteLaunch& p, hipStream_t stream);
 
 int launch_copy_blocks(const int32_t* pairs, int num_pairs, void* k_pool, void* v_pool,
                        float* k_scale, float* v_scale, int num_blocks, int block_size, int Hkv,
-                       int head_dim, int kv_dtype, int scale_mode, hipStream_t stream);
+                       int head_dim, int kv_dtype, int scale_mode, long long bstride,
+                       hipStream_t stream);
 
 struct PrefillLaunch {
   const void* q;
@@ -102,6 +105,7 @@ struct PrefillLaunch {
   const float* k_scale;
   const float* v_scale;
   int num_blocks, block_size, num_kv_heads, head_dim, kv_dtype;
+  long long bstride;  // 16-byte units from one block to the next
   const int32_t* block_table;
   int max_blocks_per_seq;
   const int32_t* context_lens;

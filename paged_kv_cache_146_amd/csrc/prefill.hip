@@ -43,6 +43,7 @@ struct PrefillScalars {
   int causal;
   int nqb;         // query blocks per sequence (grid)
   float scale_log2;
+  long long bstride;  // 16-byte units from one block to the next in each pool
 };
 
 // Workgroups are dealt to the XCDs round robin by id (id mod 8), and each XCD has
@@ -133,8 +134,8 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
   const int B = 1 << ps.blog2;
   const bool full = base + 64 <= end;  // uniform
   {
-    const size_t page = (size_t)pick4(pg, wave) * ps.Hkv + kvh;
-    const uint8_t* pb = k_pool + page * (C::NC * B * 16);
+    const uint8_t* pb = k_pool + ((size_t)pick4(pg, wave) * (size_t)ps.bstride +
+                                  (size_t)kvh * C::NC * B) * 16;
 #pragma unroll
     for (int i = 0; i < C::KP; ++i) {
       uint32_t off = pm.k_off[i];
@@ -148,8 +149,8 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
 #pragma unroll
   for (int i = 0; i < C::VP; ++i) {
     const int t0 = uniform(pm.v_p[i]) * C::TP;  // first token of the piece within the chunk
-    const size_t page = (size_t)pick4(pg, t0 >> 4) * ps.Hkv + kvh;
-    const uint8_t* pb = v_pool + page * (D * B * C::EB);
+    const uint8_t* pb = v_pool + (size_t)pick4(pg, t0 >> 4) * (size_t)ps.bstride * 16 +
+                        (size_t)kvh * (D * B * C::EB);
     uint32_t off = pm.v_off[i];
     if (!full) {
       const int t = (min(base + t0, end - 1) & (B - 1)) & ~(C::TP - 1);
@@ -604,6 +605,7 @@ int launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   ps.ctx_cap = p.ctx_cap;
   ps.causal = p.causal;
   ps.scale_log2 = p.scale * kLog2e;
+  ps.bstride = p.bstride;
   if (ps.blog2 < 4 || p.block_size > 64) return -3;  // a 16-token tile must sit in one block
   if (ps.G < 1 || ps.G > 16 || (16 % ps.G) != 0) return -3;
   if (p.q_dtype != DT_BF16) return -3;

@@ -86,6 +86,9 @@ def test_pool_bytes_is_page_size_rule():
         k, v, s = pkv.pkv_pool_bytes(pkv.pool_desc(nb, B, H, D, dt))
         assert k == v == nb * B * H * D * e
         assert s == (nb * H * 4 if dt == "fp8" else 0)
+    # a block stride (cross-layer blocks): the span one pool pointer addresses
+    k, v, s = pkv.pkv_pool_bytes(pkv.pool_desc(10, 16, 8, 128, "bf16", block_stride=6 * 32768))
+    assert k == v == 9 * 6 * 32768 + 32768
     # a quantised pool's scale array, per placement: [nb][H], [1], [nb][H][B] fp32
     for dt in ("fp8", "int8"):
         for mode, n in (("block", 10 * 8), ("tensor", 1), ("token", 10 * 8 * 16)):
@@ -100,7 +103,9 @@ def test_pool_bytes_is_page_size_rule():
     ((10, 16, 8, 96, 2), -3), ((10, 16, 8, 2, 0), -1),
     # a scale placement only for quantised pools, and only the three defined ones
     ((10, 16, 8, 128, 2, 1), -1), ((10, 16, 8, 128, 3, 3), -1), ((10, 16, 8, 128, 4, -1), -1),
-    ((10, 16, 8, 128, 5, 0), -1)])
+    ((10, 16, 8, 128, 5, 0), -1),
+    # a block stride shorter than the block's own pages, or not in 16-byte steps
+    ((10, 16, 8, 128, 2, 0, 32768 - 16), -1), ((10, 16, 8, 128, 2, 0, 65536 + 8), -1)])
 def test_pool_descriptor_validation(desc, status):
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.pkv_pool_bytes(pkv.PoolDesc(*desc))
