@@ -3,16 +3,21 @@
 Workload: 64 sequences, context lengths U[128, 4096] (seed 2), H_q 32, H_kv 8,
 D 128, bf16 KV, block size 16, pool = needed blocks + 20% spare with shuffled
 block tables.  A step is the whole hot path for one new token per sequence:
-slot mapping -> scatter of the new K/V -> paged decode attention (split-KV +
-log-sum-exp reduce when a partition size is set).  Inputs are resident in HBM;
+slot mapping -> store of the new K/V -> paged decode attention, by default in one
+launch (pkv_decode_append, balanced split-KV); `--separate` runs the append and
+the decode as two launches, `--partition P` fixed partitions + the log-sum-exp
+reduce (two launches as well).  Inputs are resident in HBM;
 the L2 and Infinity Cache are flushed before every step (outside the timed
 events), so K/V stream from HBM as they would behind the other layers.
 
 Prints ONE JSON line.  `value` is the achieved algorithmic HBM bandwidth of the
-step (GB/s); `roofline` is the decode kernel's achieved bandwidth against the
-8 TB/s peak; `cpu_baseline` is the plain CPU oracle on the same workload.
+step (GB/s); `roofline` is the dominant kernel's (the fused step's one kernel, or
+the decode) achieved bandwidth against the 8 TB/s peak; `cpu_baseline` is the
+plain CPU oracle on the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--partition P] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--partition P] [--separate] [--no-cpu-baseline]
+    python bench.py --kv fp8|int8 --scale-mode block|tensor|token   (two launches)
+    python bench.py --window W                                    (two launches)
 
 `--workload prefill` measures the fp8 chunked-prefill configuration instead (16
 sequences, 4096 cached + 512 new tokens, H_q 32, H_kv 8, D 128, B 16, E4M3 KV with
@@ -44,6 +49,7 @@ METRIC = "paged decode attention µs/step + achieved HBM GB/s (% of MI355X peak)
 HBM_PEAK_GBS = 8000.0
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_146_amd", "csrc", "decode.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "decode_llama3_8b_counters.json")
+COUNTERS_FUSED = os.path.join(ROOT, "profiles", "decode_append_llama3_8b_counters.json")
 
 
 def parse():
@@ -64,6 +70,9 @@ def parse():
                          "same bf16 draws as codes with fp32 scales)")
     ap.add_argument("--scale-mode", choices=["block", "tensor", "token"], default="block",
                     help="decode workload with a quantised pool: where the scales live")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode workload: the append and the decode as two launches "
+                         "(default: one launch per step, pkv_decode_append)")
     ap.add_argument("--window", type=int, default=0,
                     help="decode workload: sliding window (keys [ctx - window, ctx)); 0 = all")
     ap.add_argument("--calibrate", action="store_true",
@@ -146,6 +155,9 @@ def main():
     from paged_kv_cache_146_amd import workloads as W
 
     P = DEFAULT_PARTITION if a.partition is None else a.partition
+    # one launch per step where the fused kernel exists (bf16 pool, whole contexts,
+    # balanced mode); the append + decode pair otherwise
+    a.fused = not a.separate and a.kv == "bf16" and not a.window and P == -1
     wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
     dev = "cuda"
     desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
@@ -193,7 +205,14 @@ def main():
                                            wl.scale, partition_size=P, k_scale=ks, v_scale=vs,
                                            workspace=ws, out=out, q_dtype="bf16")
 
+    def fused():
+        pkv.pkv_decode_append(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len, k_new, v_new,
+                              wl.scale, workspace=ws, out=out, slot_mapping_out=slots)
+
     def step():
+        if a.fused:  # the append and the decode in one launch
+            fused()
+            return
         # slot mapping and scatter of the new tokens in one launch (the slots are
         # written out too), then the decode
         pkv.pkv_kv_cache_append(bt, seq_idx, pos_new, k_new, v_new, desc, k_pool, v_pool,
@@ -223,7 +242,8 @@ def main():
         step()
     torch.cuda.synchronize()
     step_ms, wall = timed(step, a.steps)
-    dec_ms, _ = timed(decode, a.steps)  # the dominant kernel alone, same conditions
+    # the dominant kernel alone, same conditions (fused: the step's one launch)
+    dec_ms, _ = timed(fused if a.fused else decode, a.steps)
 
     # parity spot check of this very output against the oracle on two sequences
     parity = None
@@ -244,13 +264,16 @@ def main():
     dec_us = float(np.mean(dec_ms) * 1e3)
     dbytes = decode_bytes(wl, a.window)
     sbytes = dbytes + write_bytes(wl)
-    achieved = dbytes / (dec_us * 1e-6) / 1e9
+    kbytes = sbytes if a.fused else dbytes  # algorithmic bytes of the timed kernel
+    achieved = kbytes / (dec_us * 1e-6) / 1e9
     traffic = None
-    if os.path.exists(COUNTERS):
-        c = json.load(open(COUNTERS))
+    cpath = COUNTERS_FUSED if a.fused else COUNTERS
+    if os.path.exists(cpath):
+        c = json.load(open(cpath))
         src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
         if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
-                and a.window == 0 and c.get("kv_dtype", "bf16") == wl.kv_dtype
+                and a.window == 0 and c.get("fused", False) == a.fused
+                and c.get("kv_dtype", "bf16") == wl.kv_dtype
                 and c.get("scale_mode", "block") == wl.scale_mode):
             traffic = c.get("hbm_bytes_per_launch")
 
@@ -280,18 +303,22 @@ def main():
             "window": a.window if a.window > 0 else None,
             "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
-            "step": "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) + paged_attention_decode",
+            "step": ("decode_append: slot mapping, store of the 64 new tokens and the decode in "
+                     "one launch" if a.fused else
+                     "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) "
+                     "+ paged_attention_decode"),
         },
         "algorithmic_bytes_per_step": sbytes,
         "decode_tokens_per_s": round(wl.num_seqs / (step_us * 1e-6), 1),
         "kv_tokens_per_s": round(float(wl.context_lens.sum()) / (step_us * 1e-6), 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": {0: "paged_decode_kernel", -1: "paged_decode_balanced_kernel"}.get(
-                P, "paged_decode_kernel + split_reduce_kernel"),
+            "kernel": ("paged_decode_balanced_kernel (fused with the append)" if a.fused else
+                       {0: "paged_decode_kernel", -1: "paged_decode_balanced_kernel"}.get(
+                           P, "paged_decode_kernel + split_reduce_kernel")),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(dec_us, 2),
+            "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(dec_us, 2),
         },
         "wall_s_timed_region": round(wall, 4),
         "parity_spot_check": parity,

@@ -40,7 +40,8 @@ EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_alloc_add_seq", "pkv_alloc_fork", "pkv_alloc_append", "pkv_alloc_free_seq",
            "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
            "pkv_copy_blocks", "pkv_decode_shared_workspace_bytes",
-           "pkv_paged_attention_decode_shared", "pkv_paged_attention_decode_window"]
+           "pkv_paged_attention_decode_shared", "pkv_paged_attention_decode_window",
+           "pkv_decode_append"]
 
 
 class PagedKVError(RuntimeError):
@@ -98,6 +99,8 @@ def lib():
                                                            I32, P]),
                     "pkv_decode_shared_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32,
                                                                          P]),
+                    "pkv_decode_append": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, I32, P, I32,
+                                                         P, P, F, P, SZ, P, P, P]),
                     "pkv_paged_attention_decode_window": (ctypes.c_int, [P, I32, I32, I32, P, P, P,
                                                                          P, P, P, I32, P, I32,
                                                                          F, I32, I32, P, SZ, P,
@@ -464,6 +467,31 @@ def pkv_paged_attention_decode_window(q, desc: PoolDesc, k_pool, v_pool, block_t
         float(scale), int(window), int(partition_size),
         _ptr(workspace, "workspace", allow_none=True), ws_bytes, _ptr(out, "out"),
         _stream(stream)), "pkv_paged_attention_decode_window")
+    return out
+
+
+def pkv_decode_append(q, desc: PoolDesc, k_pool, v_pool, block_table, context_lens,
+                      max_context_len: int, k_new, v_new, scale: float, workspace=None,
+                      out=None, slot_mapping_out=None, stream=None):
+    """One decode step in one launch: stores each sequence's newest token (k_new /
+    v_new [S][H_kv][D], position ctx - 1) and returns the balanced decode."""
+    torch = _torch()
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    qd = dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if workspace is None:
+        need = pkv_decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim,
+                                          max_context_len, -1)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = int(workspace.numel() * workspace.element_size())
+    _check(lib().pkv_decode_append(
+        _ptr(q, "q"), qd, S, Hq, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
+        _ptr(v_pool, "v_pool"), _ptr(block_table, "block_table"), int(block_table.shape[1]),
+        _ptr(context_lens, "context_lens"), int(max_context_len), _ptr(k_new, "k_new"),
+        _ptr(v_new, "v_new"), float(scale), _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(out, "out"), _ptr(slot_mapping_out, "slot_mapping_out", allow_none=True),
+        _stream(stream)), "pkv_decode_append")
     return out
 
 

@@ -481,6 +481,60 @@ int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t nu
   return rc == 0 ? PKV_OK : rc;
 }
 
+int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                      const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len, const void* k_new,
+                      const void* v_new, float scale, void* workspace, size_t workspace_bytes,
+                      void* out, int64_t* slot_mapping_out, void* stream) {
+  int rc = check_desc(pool);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
+  if (num_q_heads / pool->num_kv_heads > kMaxHeadsGroup) return PKV_EUNSUPPORTED;
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16 && q_dtype != PKV_BF16) return PKV_EINVAL;
+  // the new rows are stored as they are: a 16-bit pool of the query's type
+  if ((pool->kv_dtype != PKV_F16 && pool->kv_dtype != PKV_BF16) || q_dtype != pool->kv_dtype)
+    return PKV_EUNSUPPORTED;
+  if (max_context_len > (1 << 30)) return PKV_EUNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out || !k_new || !v_new)
+    return PKV_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      !aligned16(k_new) || !aligned16(v_new))
+    return PKV_EINVAL;
+  if (num_seqs > 65535 || pool->num_kv_heads > 65535) return PKV_EUNSUPPORTED;
+  int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+  if (cap > max_context_len) cap = max_context_len;
+
+  pkv::DecodeLaunch p = {};
+  p.q = q;
+  p.q_dtype = q_dtype;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.kv_dtype = pool->kv_dtype;
+  p.scale_mode = pool->scale_mode;
+  p.bstride = block_units(pool);
+  p.block_size = pool->block_size;
+  p.num_blocks = pool->num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.ctx_cap = (int)cap;
+  p.scale = scale;
+  p.fuse = 1;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.slot_out = slot_mapping_out;
+  return launch_balanced(p, workspace, workspace_bytes, stream);
+}
+
 int pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t shared_len,
                                       size_t* bytes) {

@@ -84,6 +84,13 @@ struct DecodeScalars {
   float* tail_sum;
   int window;       // > 0: a sequence of context c sees only the keys [c - window, c)
   long long bstride;  // 16-byte units from one block to the next in each pool
+  // decode fused with the append of each sequence's newest token (position ctx - 1):
+  // its K / V rows [S][H_kv][D], in the pool's 16-bit type, and where its slots go
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  int64_t* slot_out;
+  uint8_t* k_pool_w;  // the pools, for those stores
+  uint8_t* v_pool_w;
 };
 
 // 16-byte unit where block b's K pages start, and element where its V pages start
@@ -683,6 +690,48 @@ paged_decode_kernel(
   }
 }
 
+// ---- the newest token of a pair, stored by the decode (decode fused with append) -----
+// The K and V rows of kv head kvh of sequence s, from the caller's k_new / v_new,
+// for the slot of position pos, spread over the wave's lanes: lane L holds K piece
+// L (lanes below D/8) and V elements L and L + 64 (those below D).  load() only
+// requests them, so the stores can be issued later, after other requests.
+template <class C>
+struct NewRow {
+  u32x4 k;
+  uint16_t v[2];
+  int blk, off, s, kvh;
+
+  __device__ __forceinline__ void load(const DecodeScalars& sc, const int32_t* __restrict__ trow,
+                                       int pos, int s_, int kvh_, int lane) {
+    s = s_;
+    kvh = kvh_;
+    blk = trow[pos >> sc.blog2];
+    off = pos & ((1 << sc.blog2) - 1);
+    const size_t row = ((size_t)s * sc.Hkv + kvh) * C::Dim;  // element index of the rows
+    if (lane < C::NC) k = reinterpret_cast<const u32x4*>(sc.k_new)[row / C::E + lane];
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(sc.v_new) + row;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < C::Dim) v[i] = vn[lane + 64 * i];
+  }
+
+  // into the slot, as the cache write does (a table entry outside the pool skips it)
+  __device__ __forceinline__ void store(const DecodeScalars& sc, int lane) const {
+    const int B = 1 << sc.blog2;
+    const bool inside = blk >= 0 && blk < sc.num_blocks;
+    if (sc.slot_out && kvh == 0 && lane == 0) sc.slot_out[s] = inside ? (int64_t)blk * B + off : -1;
+    if (!inside) return;
+    const size_t blk16 = block_k16(sc, blk);
+    if (lane < C::NC)
+      reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off] = k;
+    uint16_t* vp =
+        reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E + (size_t)kvh * C::Dim * B + off;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) * B] = v[i];
+  }
+};
+
 // =================================================================================
 // Kernel B: balanced wavefront workers
 // =================================================================================
@@ -840,7 +889,11 @@ struct Pos {
   int u, s, kvh, j, nch, ctx, k, lo, st;
 };
 
-template <int KVT, int CT, int D, bool SMALLB>
+// FUSE: before its first load, each worker stores the newest token (position
+// ctx - 1, from sc.k_new / sc.v_new) of every pair whose last chunk lies in its
+// share, and waits for those stores; only that worker ever reads that chunk, so the
+// decode then reads the token from the pool like any other.
+template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_balanced_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
@@ -935,6 +988,56 @@ paged_decode_balanced_kernel(
   // a piece ends at the last chunk of its pair or of the worker's share
   auto piece_ends = [&](const Pos& p) { return p.j == p.nch - 1 || p.k + 1 >= n_units; };
   auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W + sc.tbl_off; };
+
+  // FUSE: the newest token of every pair whose last chunk is in this share is
+  // stored by this worker before it reads that chunk.  The memory counter is in
+  // order, so once the chunk loop has waited for a chunk requested after a store,
+  // that store has completed and every chunk requested afterwards sees it; only the
+  // first three chunks of the share can be requested before such a wait.
+  NewRow<C> carry[2];  // stored after the first chunk has been requested
+  int n_carry = 0;
+  if constexpr (FUSE) {
+    auto last_unit = [&](const Pos& p) { return uniform(prefix[p.s]) + (p.kvh + 1) * p.nch - 1; };
+    auto next_pair = [&](Pos& p) {  // false past the last sequence
+      if (++p.kvh < sc.Hkv) return true;
+      p.kvh = 0;
+      do {
+        ++p.s;
+      } while (p.s < sc.S && prefix[p.s + 1] == prefix[p.s]);
+      if (p.s >= sc.S) return false;
+      p.s = uniform(p.s);
+      p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
+      p.ctx = clamp_ctx(p.s);
+      return true;
+    };
+    const Pos p0 = locate(u_begin);
+    int n_ends = 0;  // pairs ending in the share, counted up to 3
+    for (Pos t = p0; n_ends < 3 && last_unit(t) < u_end;) {
+      ++n_ends;
+      if (!next_pair(t)) break;
+    }
+    const bool early = n_ends > 0 && last_unit(p0) < u_begin + 3;
+    if (SMALLB || early || n_ends > 2) {
+      // every row stored now, before any chunk is requested; a store into one of
+      // the first chunks is waited for
+      for (Pos t = p0; last_unit(t) < u_end;) {
+        NewRow<C> r;
+        r.load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
+        r.store(sc, lane);
+        if (!next_pair(t)) break;
+      }
+      if (early) __builtin_amdgcn_s_waitcnt(0);
+    } else if (n_ends > 0) {
+      // the rows are requested now and stored once the first chunk is requested
+      Pos t = p0;
+      carry[0].load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
+      n_carry = 1;
+      if (n_ends > 1 && next_pair(t)) {
+        carry[1].load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
+        n_carry = 2;
+      }
+    }
+  }
 
   State<C> st;
   state_init(st);
@@ -1077,6 +1180,10 @@ paged_decode_balanced_kernel(
     for (int k = 0; k + 1 < NB; ++k) {
       if (k > 0) pp[k] = advance(pp[k - 1]);
       issue(R[k], pp[k], pages_at(pp[k]), ksr[k], vsr[k]);
+    }
+    if constexpr (FUSE) {
+      if (n_carry > 0) carry[0].store(sc, lane);
+      if (n_carry > 1) carry[1].store(sc, lane);
     }
     pp[NB - 1] = advance(pp[NB - 2]);
     Pages en = pages_at(pp[NB - 1]);
@@ -1373,6 +1480,20 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
                        p.context_lens, p.part_out, p.part_max, p.part_sum, sc, pg);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
+  if (p.balanced && p.fuse) {  // decode fused with the append: 16-bit pools only
+    if constexpr (KVT == CT && (KVT == DT_F16 || KVT == DT_BF16)) {
+      const size_t lds = ((size_t)p.num_seqs + 1) * sizeof(int);
+      dim3 grid((sc.num_workers + kWaves - 1) / kWaves);
+      hipLaunchKernelGGL((paged_decode_balanced_kernel<KVT, CT, D, SMALLB, true>), grid,
+                         dim3(kThreads), lds, st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
+                         (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
+                         p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.counters,
+                         sc);
+      return hipGetLastError() == hipSuccess ? 0 : -5;
+    } else {
+      return -3;
+    }
+  }
   if (p.balanced) {
     const size_t lds = ((size_t)p.num_seqs + 1) * sizeof(int);
     dim3 grid((sc.num_workers + kWaves - 1) / kWaves);
@@ -1439,6 +1560,11 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.tail_sum = p.tail_sum;
   sc.window = p.window;
   sc.bstride = p.bstride;
+  sc.k_new = static_cast<const uint8_t*>(p.k_new);
+  sc.v_new = static_cast<const uint8_t*>(p.v_new);
+  sc.slot_out = p.slot_out;
+  sc.k_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.k_pool));
+  sc.v_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.v_pool));
   return sc;
 }
 

@@ -45,6 +45,11 @@ struct DecodeLaunch {
   int prefix = 0;
   int shared_len = 0, n_slices = 0, slice_chunks = 0;
   int window = 0;  // > 0: sliding-window decode (keys [ctx - window, ctx))
+  // balanced decode fused with the append of each sequence's newest token
+  int fuse = 0;
+  const void* k_new = nullptr;  // [S][H_kv][D], the pool's 16-bit type
+  const void* v_new = nullptr;
+  int64_t* slot_out = nullptr;  // optional [S]: the slots written
 };
 
 // Wavefront workers the balanced decode can keep resident on the current device
