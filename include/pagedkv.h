@@ -38,17 +38,21 @@
  * Physical pool layout (owned by this library; one pool for K, one for V, per
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
  *   K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ *   V pool: [num_blocks][num_kv_heads][block_size / TG][head_dim][TG],
+ *           TG = min(X, block_size) consecutive tokens of a dim per run
  *   scales of a quantised pool (K and V separately): float arrays whose shape
  *   the descriptor's scale_mode sets (pkv_scale_mode below)
  * (block strides other than the dense one: see pkv_pool_desc.block_stride).
  * One (block, kv head) page is contiguous in each pool.  The logical element
  * K[block][head][t][d] lives at K pool index
  *   (((block*num_kv_heads + head)*(head_dim/X) + d/X)*block_size + t)*X + d%X
- * and V[block][head][t][d] at ((block*num_kv_heads + head)*head_dim + d)*block_size + t.
+ * and V[block][head][t][d] at V pool index
+ *   (block*num_kv_heads + head)*block_size*head_dim + (t/TG)*TG*head_dim + d*TG + t%TG.
  * Both are the operand layouts of the matrix-core products: 16 bytes of one K
- * row (X consecutive dims of a token) and 16 bytes of one V column (16/E
- * consecutive tokens of a dim) are each one lane's load.
+ * row (X consecutive dims of a token) and a run of one V column (consecutive
+ * tokens of a dim) are a lane's loads.  A token's V row lies in one run group:
+ * its head_dim elements are TG elements apart, so storing a new token touches
+ * head_dim * TG * E / 64 lines of 64 bytes rather than head_dim.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

@@ -8,8 +8,8 @@ built, every call raises instead of falling back to anything else.
 
 Pools are raw byte tensors in the library's physical layout (see the header):
     K pool [num_blocks][num_kv_heads][head_dim/X][block_size][X]
-    V pool [num_blocks][num_kv_heads][block_size][head_dim]
-with X = 16 / element bytes.  ``alloc_pool`` sizes them with ``pkv_pool_bytes``.
+    V pool [num_blocks][num_kv_heads][block_size/TG][head_dim][TG]
+with X = 16 / element bytes and TG = min(X, block_size).  ``alloc_pool`` sizes them with ``pkv_pool_bytes``.
 """
 from __future__ import annotations
 

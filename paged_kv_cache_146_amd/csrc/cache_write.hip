@@ -11,8 +11,9 @@
 // The fused append computes each token's slot in the scatter itself (one launch
 // for both steps).  The scatter works in 16-byte source pieces: one thread moves one piece of
 // one (token, kv head) row.  In the K pool ([block][head][D/X][B][X]) the piece
-// lands as one 16-byte store; in the V pool ([block][head][D][B], tokens
-// contiguous per dim) its elements go to D-strided slots, one store each.  Bit
+// lands as one 16-byte store; in the V pool ([block][head][B/TG][D][TG], runs of
+// TG = min(X, B) tokens per dim) its elements go TG elements apart, one store
+// each.  Bit
 // copies for f32/f16/bf16 pools; for quantised pools the thread divides 16
 // source elements by their scale (IEEE fp32 division) and encodes them as OCP
 // E4M3 (nearest, ties to even, saturating) or as symmetric int8 (nearest, ties
@@ -71,6 +72,9 @@ __device__ __forceinline__ long long source_slot(const SlotSource& ss, long long
   return slot;
 }
 
+// log2 of a power of two
+__device__ __forceinline__ int log2_of(int x) { return 31 - __builtin_clz(x); }
+
 // Bit copy of one 16-byte piece (non-fp8 pools); ES = bytes per element.
 template <int ES>
 __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
@@ -97,15 +101,18 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_copy_kernel(
         reinterpret_cast<const u32x4*>(k)[src];
   } else {
     const u32x4 x = reinterpret_cast<const u32x4*>(v)[src];
-    // element (dim c E, token off)
-    const size_t d0 = blk16 * E + ((size_t)h * D + (size_t)c * E) * B + off;
+    // V page [B/TG][D][TG], TG = min(E, B): element (dim c E, token off), then the
+    // next dims TG elements apart
+    const int tgl = min(E == 4 ? 2 : 3, log2_of(B));
+    const size_t d0 = blk16 * E + (size_t)h * D * B +
+                      (((size_t)(off >> tgl) * D + (size_t)c * E) << tgl) + (off & ((1 << tgl) - 1));
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t w = x[e * ES / 4];
       if constexpr (ES == 4)
-        reinterpret_cast<uint32_t*>(v_pool)[d0 + (size_t)e * B] = w;
+        reinterpret_cast<uint32_t*>(v_pool)[d0 + ((size_t)e << tgl)] = w;
       else
-        reinterpret_cast<uint16_t*>(v_pool)[d0 + (size_t)e * B] =
+        reinterpret_cast<uint16_t*>(v_pool)[d0 + ((size_t)e << tgl)] =
             (uint16_t)(w >> (16 * (e & 1)));
     }
   }
@@ -162,10 +169,14 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_quant_kernel(
     const u32x4 packed = {w[0], w[1], w[2], w[3]};
     reinterpret_cast<u32x4*>(k_pool)[blk16 + ((size_t)h * NC + c) * B + off] = packed;
   } else {
-    // element (dim 16 c, token off); one-byte codes: 16 elements per 16-byte unit
-    const size_t d0 = blk16 * 16 + ((size_t)h * D + (size_t)c * 16) * B + off;
+    // one-byte codes, 16 per 16-byte unit; V page [B/TG][D][TG], TG = min(16, B):
+    // element (dim 16 c, token off), then the next dims TG elements apart
+    const int tgl = min(4, log2_of(B));
+    const size_t d0 = blk16 * 16 + (size_t)h * D * B +
+                      (((size_t)(off >> tgl) * D + (size_t)c * 16) << tgl) + (off & ((1 << tgl) - 1));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v_pool[d0 + (size_t)e * B] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+    for (int e = 0; e < 16; ++e)
+      v_pool[d0 + ((size_t)e << tgl)] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
   }
 }
 

@@ -15,8 +15,9 @@
 //   S^T = K . Q^T   A = 16 K rows (tokens) x 32 dims, from the K pool
 //                   [block][head][D/X][B][X]: one 16-byte piece per lane;
 //                   B = q, loaded once per (sequence, kv head).
-//   O^T = V^T . P^T A = 16 dims x 32 tokens, from the V pool [block][head][D][B]
-//                   (tokens contiguous per dim): one 16-byte piece per lane;
+//   O^T = V^T . P^T A = 16 dims x 32 tokens, from the V pool
+//                   [block][head][B/TG][D][TG] (runs of TG = min(X, B) tokens
+//                   per dim): four consecutive tokens of a dim per lane piece;
 //                   B = P, which S^T's output layout already leaves in place.
 // Lane L = 16 g + n.  Tile T's row n is token 16 T + n, so each K load of a
 // wavefront reads 16 consecutive tokens of four consecutive K pieces: 1 KB of
@@ -26,7 +27,7 @@
 // swaps, p = 2^(z - m) with log2(e) folded into the scale) feeds the second
 // product without any data exchange, and a lane's V operand is two runs of four
 // consecutive tokens of one dim (each V load of a wavefront: 16 dims x 16
-// tokens, contiguous in the V pool).  O^T leaves head n, dims 16 dt + 4 g + r in
+// tokens, 16-byte-or-longer runs of the V pool).  O^T leaves head n, dims 16 dt + 4 g + r in
 // the lane.  With block_size >= 16 the 16 tokens of a tile share one block, so
 // the table entries of a chunk are wave-uniform (scalar loads).
 //
@@ -117,6 +118,7 @@ struct Cfg {
   static constexpr int Dim = D;
   static constexpr int EB = Elem<KVT>::bytes;
   static constexpr int E = 16 / EB;           // elements per 16-byte piece (the pool's X)
+  static constexpr int ELOG = EB == 4 ? 2 : (EB == 2 ? 3 : 4);  // log2(E)
   static constexpr int NC = D / E;            // pieces per K row
   static constexpr int NPL = NC / 4;          // K pieces per lane per token (lane group g
                                               // takes pieces 4 q + g)
@@ -244,14 +246,16 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
                                         int kvh, const DecodeScalars& sc, int n, int g) {
   using VP = typename C::VPiece;
   const int B = 1 << sc.blog2;
+  // V page [B/E][D][E] (block_size >= 16 >= E): token t of dim d at (t/E * D + d) E + t%E
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
+    const int t = ((pg.off + 16 * T) & (B - 1)) + 4 * g;  // the lane's first token
     const uint8_t* vp = v_pool + block_k16(sc, pg.b[T]) * 16 +
-                        (((size_t)kvh * C::Dim + n) * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g) *
-                            C::EB;
+                        ((size_t)kvh * C::Dim * B + ((size_t)(t / C::E) * C::Dim + n) * C::E +
+                         (t % C::E)) * C::EB;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-      vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * B * C::EB);
+    for (int dt = 0; dt < C::NDT; ++dt)  // 16 dims on
+      vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * C::E * C::EB);
   }
 }
 
@@ -334,12 +338,14 @@ __device__ __forceinline__ void load_small(Chunk<C>& ch, float (&ks)[16], float 
       } else {
         ks[i] = vs[i] = 1.0f;
       }
-      // element of dim n
-      const size_t e0 = block_k16(sc, blk) * C::E + ((size_t)kvh * C::Dim + n) * B + (t & (B - 1));
+      // element of dim n: V page [B/TG][D][TG], TG = min(E, B) tokens per dim run
+      const int tgl = min(C::ELOG, sc.blog2), tb = t & (B - 1);
+      const size_t e0 = block_k16(sc, blk) * C::E + (size_t)kvh * C::Dim * B +
+                        (((size_t)(tb >> tgl) * C::Dim + n) << tgl) + (tb & ((1 << tgl) - 1));
       const int word = e * C::EB / 4, sh = (e * C::EB % 4) * 8;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
-        const size_t el = e0 + (size_t)16 * dt * B;
+        const size_t el = e0 + ((size_t)16 * dt << tgl);
         uint32_t x;
         if constexpr (C::EB == 4)
           x = reinterpret_cast<const uint32_t*>(v_pool)[el];
@@ -724,11 +730,14 @@ struct NewRow {
     const size_t blk16 = block_k16(sc, blk);
     if (lane < C::NC)
       reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off] = k;
-    uint16_t* vp =
-        reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E + (size_t)kvh * C::Dim * B + off;
+    // V page [B/TG][D][TG], TG = min(E, B)
+    const int tgl = min(C::ELOG, sc.blog2);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E +
+                   (size_t)kvh * C::Dim * B + ((size_t)(off >> tgl) * C::Dim << tgl) +
+                   (off & ((1 << tgl) - 1));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) * B] = v[i];
+      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) << tgl] = v[i];
   }
 };
 

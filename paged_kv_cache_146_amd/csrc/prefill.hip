@@ -96,7 +96,8 @@ __device__ __forceinline__ int pick4(const int (&v)[4], int i) {
 //     c = l / 16 + 4 i (tile w).
 //   V piece i: vp = 256 i + 64 w + l covers tokens [TP p, TP p + TP) of dim
 //     vp % D, p = vp / D (tile TP p / 16, the same for the whole wavefront as
-//     64 divides D).
+//     64 divides D).  A V page is [B/TP][D][TP] (block_size >= 16 >= TP), so the
+//     piece of tokens [t, t + TP) of dim d is the 16 bytes at (t/TP * D + d) * 16.
 template <int KVT, int D>
 struct PieceMap {
   using C = PCfg<KVT, D>;
@@ -119,7 +120,7 @@ struct PieceMap {
       const int vp = kPfThreads * i + 64 * wave + lane;
       v_p[i] = vp / D;
       v_d[i] = vp % D;
-      v_off[i] = (uint32_t)((v_d[i] * B + ((v_p[i] * C::TP) & (B - 1))) * C::EB);
+      v_off[i] = (uint32_t)(((((v_p[i] * C::TP) & (B - 1)) / C::TP) * D + v_d[i]) * 16);
     }
   }
 };
@@ -154,7 +155,7 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
     uint32_t off = pm.v_off[i];
     if (!full) {
       const int t = (min(base + t0, end - 1) & (B - 1)) & ~(C::TP - 1);
-      off = (uint32_t)((pm.v_d[i] * B + t) * C::EB);
+      off = (uint32_t)(((t / C::TP) * D + pm.v_d[i]) * 16);
     }
     r.v[i] = *reinterpret_cast<const u32x4*>(pb + off);
   }

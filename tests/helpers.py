@@ -53,9 +53,11 @@ def logical_k(k_bytes: np.ndarray, nb, B, H, D, dtype) -> np.ndarray:
 
 
 def logical_v(v_bytes: np.ndarray, nb, B, H, D, dtype) -> np.ndarray:
-    """V pool bytes in the library layout [nb][H][D][B] -> logical [nb][H][B][D] bits."""
-    a = np.ascontiguousarray(v_bytes).view(STORAGE[dtype]).reshape(nb, H, D, B)
-    return np.ascontiguousarray(a.transpose(0, 1, 3, 2))
+    """V pool bytes in the library layout [nb][H][B/TG][D][TG] (TG = min(16 / element
+    bytes, B) tokens of one dim per run) -> logical [nb][H][B][D] bits."""
+    TG = min(16 // ES[dtype], B)
+    a = np.ascontiguousarray(v_bytes).view(STORAGE[dtype]).reshape(nb, H, B // TG, D, TG)
+    return np.ascontiguousarray(a.transpose(0, 1, 2, 4, 3).reshape(nb, H, B, D))
 
 
 class GpuCase:
