@@ -1324,6 +1324,37 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
   }
 }
 
+// A merge of every one of a few slots per (sequence, query head) (the shared-prefix
+// decode's): one wavefront per row, lane L taking dims L, L + 64; the same weights
+// as split_reduce_kernel, exp(m_i - M) l_i.
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_slots_kernel(
+    const float* __restrict__ part_out, const float* __restrict__ part_max,
+    const float* __restrict__ part_sum, uint8_t* __restrict__ out, int out_dtype, int n_rows,
+    int max_parts) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);  // s * H_q + h
+  if (row >= n_rows) return;
+  const size_t base = (size_t)row * max_parts;
+  float M = -INFINITY;
+  for (int i = 0; i < max_parts; ++i) M = fmaxf(M, part_max[base + i]);
+  float L = 0.0f, acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  for (int i = 0; i < max_parts; ++i) {
+    const float l = part_sum[base + i];
+    const float w = l > 0.0f ? __builtin_amdgcn_exp2f((part_max[base + i] - M) * kLog2e) * l : 0.0f;
+    L += w;
+    const float* po = part_out + (base + i) * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, po[lane + 64 * k], acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    store_any(out, out_dtype, (size_t)row * D + lane + 64 * k, L > 0.0f ? acc[k] / L : 0.0f);
+}
+
 // =================================================================================
 // Kernel C: the shared prefix of a batch, read once per kv head
 // =================================================================================
@@ -1647,6 +1678,21 @@ int balanced_worker_capacity(int kv, int qd, int D, int block_size) {
 
 int launch_split_reduce(const ReduceLaunch& p, hipStream_t st) {
   if (p.max_parts > 8192) return -3;
+  if (!p.context_lens && p.max_parts <= 64) {  // every slot, few of them: a wavefront per row
+    const long long rows = (long long)p.num_seqs * p.num_q_heads;
+    dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
+    if (p.head_dim == 64)
+      hipLaunchKernelGGL(merge_slots_kernel<64>, grid, dim3(kThreads), 0, st, p.part_out,
+                         p.part_max, p.part_sum, (uint8_t*)p.out, p.out_dtype, (int)rows,
+                         p.max_parts);
+    else if (p.head_dim == 128)
+      hipLaunchKernelGGL(merge_slots_kernel<128>, grid, dim3(kThreads), 0, st, p.part_out,
+                         p.part_max, p.part_sum, (uint8_t*)p.out, p.out_dtype, (int)rows,
+                         p.max_parts);
+    else
+      return -3;
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+  }
   dim3 grid(p.num_q_heads, p.num_seqs);
   size_t lds = (size_t)p.max_parts * sizeof(float);
   if (p.head_dim == 64)
