@@ -52,6 +52,16 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_llama3_8b_counters.json")
 COUNTERS_FUSED = os.path.join(ROOT, "profiles", "decode_append_llama3_8b_counters.json")
 
 
+def source_hash(path) -> str:
+    """sha256 of a source file with its comments and blank space removed, so that
+    counters taken from it stay valid across comment-only edits."""
+    import re
+    txt = open(path).read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", " ", txt)
+    return hashlib.sha256(" ".join(txt.split()).encode()).hexdigest()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,7 +280,7 @@ def main():
     cpath = COUNTERS_FUSED if a.fused else COUNTERS
     if os.path.exists(cpath):
         c = json.load(open(cpath))
-        src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        src_hash = source_hash(DECODE_SRC)
         if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
                 and a.window == 0 and c.get("fused", False) == a.fused
                 and c.get("kv_dtype", "bf16") == wl.kv_dtype

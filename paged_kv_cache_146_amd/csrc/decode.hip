@@ -31,9 +31,9 @@
 // the lane.  With block_size >= 16 the 16 tokens of a tile share one block, so
 // the table entries of a chunk are wave-uniform (scalar loads).
 //
-// fp8 (OCP E4M3) pages are widened exactly to the query's 16-bit type before
-// the product; K's per-page scale multiplies the scores and V's is folded into
-// P.  P enters the second product as a hi + lo pair of the 16-bit type.  f32
+// fp8 (OCP E4M3) and int8 pages are widened exactly to the query's 16-bit type
+// before the product; K's scale (per page, per pool or per token) multiplies the
+// scores and V's is folded into P.  P enters the second product as a hi + lo pair of the 16-bit type.  f32
 // pools use the 16x16x4 f32 product with one k-slot per lane.
 //
 // Three ways to cut the work:
@@ -45,6 +45,13 @@
 //         worker finishes every pair it covers entirely and leaves a partial
 //         state for at most two pairs it shares with neighbours; those are
 //         merged by the last worker to finish one (a per-pair counter tells it).
+//   shared prefix — shared_prefix_kernel reads the blocks every sequence of the
+//         batch shares once per kv head, with 16/G sequences x G heads in the 16
+//         product columns; the balanced kernel takes the private tails and
+//         merge_slots_kernel merges the two.
+// Both main kernels also take a sliding window (a sequence's chunk grid starts
+// at its window's first 16-token tile), and the balanced one can store each
+// sequence's newest token itself before decoding (one launch per decode step).
 // Inside a wavefront the chunk loop is software-pipelined on single buffers:
 // the next chunk's K pieces are requested as soon as the current scores are
 // done and its V pieces as soon as the current P.V is done, the table entries
