@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
-    ap.add_argument("--workload", choices=["decode", "prefill", "copy", "shared-prefix"],
+    ap.add_argument("--workload", choices=["decode", "long", "prefill", "copy", "shared-prefix"],
                     default="decode")
     ap.add_argument("--kv", choices=["bf16", "fp8", "int8"], default="bf16",
                     help="decode workload: pool element type (quantised pools store the "
@@ -168,7 +168,13 @@ def main():
     # one launch per step where the fused kernel exists (bf16 pool, whole contexts,
     # balanced mode); the append + decode pair otherwise
     a.fused = not a.separate and a.kv == "bf16" and not a.window and P == -1
-    wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
+    if a.workload == "long":  # the long-context split-KV configuration
+        wl = W.long_context_decode(seed=3)
+        wl_text = ("long-context paged decode: 8 seqs, ctx U[32768,131072] (seed 3), H_q 64, "
+                   "H_kv 8, D 128, B 16, bf16 (one new token per sequence)")
+    else:
+        wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
+        wl_text = "llama3-8b-shaped paged decode layer (one new token per sequence)"
     dev = "cuda"
     desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
                          wl.scale_mode)
@@ -278,7 +284,9 @@ def main():
     achieved = kbytes / (dec_us * 1e-6) / 1e9
     traffic = None
     cpath = COUNTERS_FUSED if a.fused else COUNTERS
-    if os.path.exists(cpath):
+    if a.workload != "decode":
+        cpath = ""  # the counters were taken on the Llama-3-8B-shaped workload
+    if cpath and os.path.exists(cpath):
         c = json.load(open(cpath))
         src_hash = source_hash(DECODE_SRC)
         if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
@@ -304,8 +312,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama3-8b-shaped paged decode layer (one new token per sequence)",
-            "num_seqs": wl.num_seqs, "context_lens": "U[128,4096], seed 2",
+            "workload": wl_text,
+            "num_seqs": wl.num_seqs,
+            "context_lens": "U[32768,131072], seed 3" if a.workload == "long" else "U[128,4096], seed 2",
             "sum_context": int(wl.context_lens.sum()), "H_q": wl.num_q_heads,
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
             "kv_dtype": wl.kv_dtype,
@@ -313,10 +322,10 @@ def main():
             "window": a.window if a.window > 0 else None,
             "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
-            "step": ("decode_append: slot mapping, store of the 64 new tokens and the decode in "
-                     "one launch" if a.fused else
-                     "kv_cache_append (slot mapping + scatter of the 64 new tokens, one launch) "
-                     "+ paged_attention_decode"),
+            "step": ("decode_append: slot mapping, store of the %d new tokens and the decode in "
+                     "one launch" % wl.num_seqs if a.fused else
+                     "kv_cache_append (slot mapping + scatter of the %d new tokens, one launch) "
+                     "+ paged_attention_decode" % wl.num_seqs),
         },
         "algorithmic_bytes_per_step": sbytes,
         "decode_tokens_per_s": round(wl.num_seqs / (step_us * 1e-6), 1),
@@ -740,8 +749,8 @@ def _oracle_pool(oracle, wl):
 
 
 def cpu_baseline(wl, budget_s, window=0):
-    """The oracle as it stands, on the same workload, on this host's cores: the write of
-    the 64 new tokens plus decode attention for a bounded prefix of the sequences."""
+    """The oracle as it stands, on the same workload, on this host's cores: whole steps
+    (the write of the new tokens plus decode attention of every sequence)."""
     import oracle
     opool = _oracle_pool(oracle, wl)
     rows = wl.decode_new_token_rows()
@@ -759,8 +768,8 @@ def cpu_baseline(wl, budget_s, window=0):
     step_bytes = decode_bytes(wl, window) + write_bytes(wl)
     return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d whole steps of the same workload (write of the 64 new tokens + decode "
-                      "of all 64 sequences), %.1f s" % (steps, t_used),
+            "sample": "%d whole steps of the same workload (write of the %d new tokens + decode "
+                      "of all %d sequences), %.1f s" % (steps, wl.num_seqs, wl.num_seqs, t_used),
             "us_per_step": round(step_s * 1e6, 1)}
 
 
