@@ -80,3 +80,48 @@ def test_fused_rejects_other_pools():
         pkv.pkv_decode_append(case.q, case.desc, case.k_pool, case.v_pool, case.block_table,
                               case.context_lens, wl.max_context_len, kn, kn, wl.scale)
     assert e.value.status == -3
+
+
+def test_fused_graph_replay():
+    """The fused step captured in a graph and replayed (as a serving loop does), with an
+    eager call between replays: every replay stores the same tokens and gives the
+    oracle's output."""
+    import torch
+    import paged_kv_cache_146_amd as pkv
+    wl = W.llama3_8b_decode(small=True)
+    w2, rows = _without_newest(wl)
+    case = GpuCase(w2)
+    r = np.where(rows >= 0, rows, 0)
+    k_new = torch_bits(wl.k_src[r], wl.src_dtype)
+    v_new = torch_bits(wl.v_src[r], wl.src_dtype)
+    ws = torch.full((pkv.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                                    wl.head_dim, wl.max_context_len, -1),),
+                    0xFF, dtype=torch.uint8, device="cuda")
+    out = case.nan_out()
+    opool = oracle_pool(wl)
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale)
+
+    def step(o):
+        return pkv.pkv_decode_append(case.q, case.desc, case.k_pool, case.v_pool,
+                                     case.block_table, case.context_lens, wl.max_context_len,
+                                     k_new, v_new, wl.scale, workspace=ws, out=o)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out)
+    for rep in range(3):
+        out.view(torch.uint8).fill_(0xFF)
+        graph.replay()
+        torch.cuda.synchronize()
+        print(assert_close(to_f64(out, wl.q_dtype), ref, "replay %d" % rep))
+        if rep == 1:
+            print(assert_close(to_f64(step(case.nan_out()), wl.q_dtype), ref, "eager between"))
+    gk, gv = case.logical_pools()
+    assert np.array_equal(gk.view(np.uint8), opool.k.view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), opool.v.view(np.uint8))
