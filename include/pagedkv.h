@@ -273,7 +273,9 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
 /* [P1 §4.1, §4] One decode step in one launch: the write path's append of each
  * sequence's newest token followed by decode, i.e. the same pool bytes and output
  * as pkv_kv_cache_append (positions ctx_s - 1) then pkv_paged_attention_decode
- * (balanced).  The newest token's K and V are taken straight from k_new / v_new
+ * with the same partition_size, which is PKV_PARTITION_BALANCED or 0 (unsplit;
+ * other positive multiples of 64 are PKV_EUNSUPPORTED: fixed partitions take the
+ * two calls).  The newest token's K and V are taken straight from k_new / v_new
  * for the attention (the pool's copy of that slot is neither read nor waited
  * for) and stored into slot block_table[s][(ctx_s - 1) / B] * B + (ctx_s - 1) % B
  * by the same launch; a table entry outside the pool skips the store (slot -1).
@@ -281,15 +283,16 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
  *   Supported: f16 or bf16 pools with q of the same type (else PKV_EUNSUPPORTED).
  *   context_lens count the new token (ctx_s >= 1 for a sequence that has one;
  *   ctx_s = 0 stores nothing and gives zeros); their clamping, the workspace
- *   (pkv_decode_workspace_bytes with PKV_PARTITION_BALANCED) and the errors are
- *   those of pkv_paged_attention_decode.
+ *   (pkv_decode_workspace_bytes with the same partition_size; none for 0) and
+ *   the errors are those of pkv_paged_attention_decode.
  *   slot_mapping_out: optional device int64 [num_seqs], the slots written. */
 int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                       const pkv_pool_desc* pool, void* k_pool, void* v_pool,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t max_context_len, const void* k_new,
-                      const void* v_new, float scale, void* workspace, size_t workspace_bytes,
-                      void* out, int64_t* slot_mapping_out, void* stream);
+                      const void* v_new, float scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, void* out, int64_t* slot_mapping_out,
+                      void* stream);
 
 /* [P1 §1.1 table, §7] Sliding-window (local) decode: as pkv_paged_attention_decode,
  * but the query of sequence s (at position p = ctx_s - 1) sees only the keys of

@@ -100,7 +100,7 @@ def lib():
                     "pkv_decode_shared_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32,
                                                                          P]),
                     "pkv_decode_append": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, I32, P, I32,
-                                                         P, P, F, P, SZ, P, P, P]),
+                                                         P, P, F, I32, P, SZ, P, P, P]),
                     "pkv_paged_attention_decode_window": (ctypes.c_int, [P, I32, I32, I32, P, P, P,
                                                                          P, P, P, I32, P, I32,
                                                                          F, I32, I32, P, SZ, P,
@@ -471,25 +471,28 @@ def pkv_paged_attention_decode_window(q, desc: PoolDesc, k_pool, v_pool, block_t
 
 
 def pkv_decode_append(q, desc: PoolDesc, k_pool, v_pool, block_table, context_lens,
-                      max_context_len: int, k_new, v_new, scale: float, workspace=None,
-                      out=None, slot_mapping_out=None, stream=None):
+                      max_context_len: int, k_new, v_new, scale: float,
+                      partition_size: int = -1, workspace=None, out=None,
+                      slot_mapping_out=None, stream=None):
     """One decode step in one launch: stores each sequence's newest token (k_new /
-    v_new [S][H_kv][D], position ctx - 1) and returns the balanced decode."""
+    v_new [S][H_kv][D], position ctx - 1) and returns the decode (balanced: -1, or
+    unsplit: 0)."""
     torch = _torch()
     S, Hq = int(q.shape[0]), int(q.shape[1])
     qd = dtype_code(q.dtype)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    if workspace is None:
-        need = pkv_decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim,
-                                          max_context_len, -1)
+    need = pkv_decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_dim,
+                                      max_context_len, partition_size)
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = int(workspace.numel() * workspace.element_size())
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
     _check(lib().pkv_decode_append(
         _ptr(q, "q"), qd, S, Hq, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
         _ptr(v_pool, "v_pool"), _ptr(block_table, "block_table"), int(block_table.shape[1]),
         _ptr(context_lens, "context_lens"), int(max_context_len), _ptr(k_new, "k_new"),
-        _ptr(v_new, "v_new"), float(scale), _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(v_new, "v_new"), float(scale), int(partition_size),
+        _ptr(workspace, "workspace", allow_none=True), ws_bytes,
         _ptr(out, "out"), _ptr(slot_mapping_out, "slot_mapping_out", allow_none=True),
         _stream(stream)), "pkv_decode_append")
     return out

@@ -485,9 +485,14 @@ int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       const pkv_pool_desc* pool, void* k_pool, void* v_pool,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t max_context_len, const void* k_new,
-                      const void* v_new, float scale, void* workspace, size_t workspace_bytes,
-                      void* out, int64_t* slot_mapping_out, void* stream) {
+                      const void* v_new, float scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, void* out, int64_t* slot_mapping_out,
+                      void* stream) {
   int rc = check_desc(pool);
+  if (partition_size != PKV_PARTITION_BALANCED && partition_size != 0) {
+    if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
+    return PKV_EUNSUPPORTED;  // fixed partitions: append and decode are two calls
+  }
   if (rc != PKV_OK) return rc;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
     return PKV_EINVAL;
@@ -532,7 +537,14 @@ int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t 
   p.k_new = k_new;
   p.v_new = v_new;
   p.slot_out = slot_mapping_out;
-  return launch_balanced(p, workspace, workspace_bytes, stream);
+  if (partition_size == PKV_PARTITION_BALANCED)
+    return launch_balanced(p, workspace, workspace_bytes, stream);
+  p.split = 0;  // unsplit: one workgroup per (sequence, kv head)
+  p.max_parts = 1;
+  p.part_size = (int)((cap + 63) / 64 * 64);
+  if (p.part_size == 0) p.part_size = 64;
+  rc = pkv::launch_decode(p, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
 }
 
 int pkv_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -547,10 +547,57 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
   }
 }
 
+// ---- the newest token of a pair, stored by the decode (decode fused with append) -----
+// The K and V rows of kv head kvh of sequence s, from the caller's k_new / v_new,
+// for the slot of position pos, spread over the wave's lanes: lane L holds K piece
+// L (lanes below D/8) and V elements L and L + 64 (those below D).  load() only
+// requests them, so the stores can be issued later, after other requests.
+template <class C>
+struct NewRow {
+  u32x4 k;
+  uint16_t v[2];
+  int blk, off, s, kvh;
+
+  __device__ __forceinline__ void load(const DecodeScalars& sc, const int32_t* __restrict__ trow,
+                                       int pos, int s_, int kvh_, int lane) {
+    s = s_;
+    kvh = kvh_;
+    blk = trow[pos >> sc.blog2];
+    off = pos & ((1 << sc.blog2) - 1);
+    const size_t row = ((size_t)s * sc.Hkv + kvh) * C::Dim;  // element index of the rows
+    if (lane < C::NC) k = reinterpret_cast<const u32x4*>(sc.k_new)[row / C::E + lane];
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(sc.v_new) + row;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < C::Dim) v[i] = vn[lane + 64 * i];
+  }
+
+  // into the slot, as the cache write does (a table entry outside the pool skips it)
+  __device__ __forceinline__ void store(const DecodeScalars& sc, int lane) const {
+    const int B = 1 << sc.blog2;
+    const bool inside = blk >= 0 && blk < sc.num_blocks;
+    if (sc.slot_out && kvh == 0 && lane == 0) sc.slot_out[s] = inside ? (int64_t)blk * B + off : -1;
+    if (!inside) return;
+    const size_t blk16 = block_k16(sc, blk);
+    if (lane < C::NC)
+      reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off] = k;
+    // V page [B/TG][D][TG], TG = min(E, B)
+    const int tgl = min(C::ELOG, sc.blog2);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E +
+                   (size_t)kvh * C::Dim * B + ((size_t)(off >> tgl) * C::Dim << tgl) +
+                   (off & ((1 << tgl) - 1));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) << tgl] = v[i];
+  }
+};
+
 // =================================================================================
 // Kernel A: one workgroup per (partition, kv head, sequence)
 // =================================================================================
-template <int KVT, int CT, int D, bool SMALLB>
+// FUSE (unsplit only): the wave that reads a pair's last chunk first stores the
+// newest token (position ctx - 1, from sc.k_new / sc.v_new) into its slot.
+template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
@@ -605,6 +652,26 @@ paged_decode_kernel(
   const int nch = (t_end - t_begin + 63) >> 6;
   const int cnt = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;  // chunks wave, wave+4, ...
   auto base_of = [&](int i) { return t_begin + 64 * (wave + kWaves * min(i, cnt - 1)); };
+  // FUSE: only the wave that reads the last chunk stores the newest token.  The
+  // memory counter is in order, so a chunk requested after that wave has waited for
+  // a chunk requested after the stores sees them.  Its first two chunks can be
+  // requested before such a wait: when the last chunk is one of them, the stores go
+  // first and are waited for; otherwise the rows are requested first and stored
+  // once the first chunk has been requested (SMALLB: stored at once, chunk 0 is
+  // waited for before chunk 1 is requested).
+  NewRow<C> carry;
+  bool carried = false;
+  if constexpr (FUSE) {
+    if (wave == (nch - 1) % kWaves) {
+      carry.load(sc, trow, ctx - 1, s, kvh, lane);
+      if (SMALLB || nch - 1 < wave + 2 * kWaves) {
+        carry.store(sc, lane);
+        if (!SMALLB || nch - 1 == wave) __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        carried = true;
+      }
+    }
+  }
 
   if constexpr (SMALLB) {
     for (int i = 0; i < cnt; ++i) {
@@ -634,6 +701,8 @@ paged_decode_kernel(
       if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
       issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
     }
+    if constexpr (FUSE)
+      if (carried) carry.store(sc, lane);
     Pages p1 = pages_of(trow, base_of(1), t_end, sc);
     for (int i = 0; i < cnt; ++i) {
       const int b0 = base_of(i);
@@ -702,51 +771,6 @@ paged_decode_kernel(
     }
   }
 }
-
-// ---- the newest token of a pair, stored by the decode (decode fused with append) -----
-// The K and V rows of kv head kvh of sequence s, from the caller's k_new / v_new,
-// for the slot of position pos, spread over the wave's lanes: lane L holds K piece
-// L (lanes below D/8) and V elements L and L + 64 (those below D).  load() only
-// requests them, so the stores can be issued later, after other requests.
-template <class C>
-struct NewRow {
-  u32x4 k;
-  uint16_t v[2];
-  int blk, off, s, kvh;
-
-  __device__ __forceinline__ void load(const DecodeScalars& sc, const int32_t* __restrict__ trow,
-                                       int pos, int s_, int kvh_, int lane) {
-    s = s_;
-    kvh = kvh_;
-    blk = trow[pos >> sc.blog2];
-    off = pos & ((1 << sc.blog2) - 1);
-    const size_t row = ((size_t)s * sc.Hkv + kvh) * C::Dim;  // element index of the rows
-    if (lane < C::NC) k = reinterpret_cast<const u32x4*>(sc.k_new)[row / C::E + lane];
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(sc.v_new) + row;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) v[i] = vn[lane + 64 * i];
-  }
-
-  // into the slot, as the cache write does (a table entry outside the pool skips it)
-  __device__ __forceinline__ void store(const DecodeScalars& sc, int lane) const {
-    const int B = 1 << sc.blog2;
-    const bool inside = blk >= 0 && blk < sc.num_blocks;
-    if (sc.slot_out && kvh == 0 && lane == 0) sc.slot_out[s] = inside ? (int64_t)blk * B + off : -1;
-    if (!inside) return;
-    const size_t blk16 = block_k16(sc, blk);
-    if (lane < C::NC)
-      reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off] = k;
-    // V page [B/TG][D][TG], TG = min(E, B)
-    const int tgl = min(C::ELOG, sc.blog2);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E +
-                   (size_t)kvh * C::Dim * B + ((size_t)(off >> tgl) * C::Dim << tgl) +
-                   (off & ((1 << tgl) - 1));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) << tgl] = v[i];
-  }
-};
 
 // =================================================================================
 // Kernel B: balanced wavefront workers
@@ -1551,6 +1575,17 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
   dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
+  if (p.fuse) {  // unsplit decode fused with the append: 16-bit pools only
+    if constexpr (KVT == CT && (KVT == DT_F16 || KVT == DT_BF16)) {
+      hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB, true>), grid, dim3(kThreads), 0,
+                         st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
+                         (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
+                         p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.part_sum, sc);
+      return hipGetLastError() == hipSuccess ? 0 : -5;
+    } else {
+      return -3;
+    }
+  }
   hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB>), grid, dim3(kThreads), 0, st,
                      (const uint8_t*)p.q, (const uint8_t*)p.k_pool, (const uint8_t*)p.v_pool,
                      p.k_scale, p.v_scale, p.block_table, p.context_lens, (uint8_t*)p.out,
