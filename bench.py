@@ -48,8 +48,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention µs/step + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_146_amd", "csrc", "decode.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "decode_llama3_8b_counters.json")
-COUNTERS_FUSED = os.path.join(ROOT, "profiles", "decode_append_llama3_8b_counters.json")
+# FETCH_SIZE / WRITE_SIZE per decode launch, one record per measured configuration
+COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 
 def source_hash(path) -> str:
@@ -68,7 +68,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-KV partition size (0 = unsplit, -1 = balanced; default balanced)")
+                    help="split-KV partition size (0 = unsplit, -1 = balanced; default: unsplit "
+                         "for the decode workload over a 16-bit pool, balanced otherwise)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -108,9 +109,15 @@ def calibrate():
 
 
 # the decode mode per workload: unsplit (one workgroup per sequence and kv head) for
-# the Llama-3-8B-shaped batch, where it is the faster; balanced split-KV for the long
-# contexts (8 sequences: too few pairs to fill the chip unsplit)
+# the Llama-3-8B-shaped batch over a 16-bit pool, where it is the faster; balanced
+# split-KV for an fp8 / int8 pool (each key costs more ALU work to widen, so the even
+# split of the work over all CUs wins) and for the long contexts (8 sequences: too few
+# pairs to fill the chip unsplit)
 DEFAULT_PARTITION = {"decode": 0, "long": -1}
+
+
+def default_partition(workload, kv):
+    return -1 if kv in ("fp8", "int8") else DEFAULT_PARTITION[workload]
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}  # pool bytes per element
 
 
@@ -167,7 +174,7 @@ def main():
     import paged_kv_cache_146_amd as pkv
     from paged_kv_cache_146_amd import workloads as W
 
-    P = DEFAULT_PARTITION[a.workload] if a.partition is None else a.partition
+    P = default_partition(a.workload, a.kv) if a.partition is None else a.partition
     # one launch per step where the fused kernel exists (bf16 pool, whole contexts,
     # balanced mode); the append + decode pair otherwise
     a.fused = not a.separate and a.kv == "bf16" and not a.window and P in (-1, 0)
@@ -269,8 +276,8 @@ def main():
     parity = None
     try:
         import oracle
-        opool = _oracle_pool(oracle, wl)
         sel = np.array([0, int(np.argmax(wl.context_lens))], np.int32)
+        opool = _oracle_pool(oracle, wl, sel)
         ref = oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
                                   seqs=sel, window=a.window)
         got = out.float().cpu().numpy().astype(np.float64)[sel]
@@ -287,17 +294,14 @@ def main():
     kbytes = sbytes if a.fused else dbytes  # algorithmic bytes of the timed kernel
     achieved = kbytes / (dec_us * 1e-6) / 1e9
     traffic = None
-    cpath = COUNTERS_FUSED if a.fused else COUNTERS
-    if a.workload != "decode":
-        cpath = ""  # the counters were taken on the Llama-3-8B-shaped workload
-    if cpath and os.path.exists(cpath):
-        c = json.load(open(cpath))
-        src_hash = source_hash(DECODE_SRC)
-        if (c.get("decode_src_sha256") == src_hash and c.get("partition_size") == P
-                and a.window == 0 and c.get("fused", False) == a.fused
-                and c.get("kv_dtype", "bf16") == wl.kv_dtype
-                and c.get("scale_mode", "block") == wl.scale_mode):
-            traffic = c.get("hbm_bytes_per_launch")
+    if os.path.exists(COUNTERS):
+        # valid only for the configuration and the decode source they were taken on
+        want = {"workload": a.workload, "partition_size": P, "fused": a.fused,
+                "kv_dtype": wl.kv_dtype, "scale_mode": wl.scale_mode, "window": a.window,
+                "decode_src_sha256": source_hash(DECODE_SRC)}
+        for c in json.load(open(COUNTERS))["records"]:
+            if all(c.get(k) == v for k, v in want.items()):
+                traffic = c["hbm_bytes_per_launch"]
 
     res = {
         "metric": METRIC,
@@ -626,9 +630,9 @@ def shared_main(a):
     parity = None
     try:
         import oracle
-        opool = _oracle_pool(oracle, wl)
         sel = np.array([0, int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))],
                        np.int32)
+        opool = _oracle_pool(oracle, wl, sel)
         ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens,
                                   wl.scale, seqs=sel)
         got = out.float().cpu().numpy().astype(np.float64)[sel]
@@ -658,7 +662,7 @@ def shared_main(a):
         "per_sequence_balanced_decode_us": round(plain_us, 2),
         "roofline": {"bound": "hbm",
                      "kernel": "shared_prefix_kernel + paged_decode_balanced_kernel (tails) + "
-                               "split_reduce_kernel, one call",
+                               "merge_slots_kernel, one call",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(dec_us, 2)},
@@ -742,13 +746,17 @@ def cpu_baseline_prefill(wl, budget_s):
                       % (done, done * 37 // total, t_used)}
 
 
-def _oracle_pool(oracle, wl):
-    """The oracle's pool for the decode workload, filled by the oracle's own write path."""
+def _oracle_pool(oracle, wl, seqs=None):
+    """The oracle's pool for the decode workload, filled by the oracle's own write path:
+    every stored token, or only those stored under `seqs` (enough to decode those
+    sequences: a shared prefix is stored under sequence 0, so 0 must be among them)."""
     opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
                         scale_mode=wl.scale_mode)
     opool.k_scale, opool.v_scale = wl.k_scale, wl.v_scale
-    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq, wl.fill_pos, wl.block_size)
-    oracle.kv_cache_write(opool, osl, wl.k_src, wl.v_src, wl.src_dtype)
+    keep = slice(None) if seqs is None else np.isin(wl.fill_seq, seqs)
+    osl = oracle.slot_mapping(wl.block_table, wl.fill_seq[keep], wl.fill_pos[keep],
+                              wl.block_size)
+    oracle.kv_cache_write(opool, osl, wl.k_src[keep], wl.v_src[keep], wl.src_dtype)
     return opool
 
 
