@@ -99,6 +99,7 @@ struct DecodeScalars {
   int64_t* slot_out;
   uint8_t* k_pool_w;  // the pools, for those stores
   uint8_t* v_pool_w;
+  int lpt;  // unsplit workgroup kernel, S <= kThreads: sequences go out longest first
 };
 
 // 16-byte unit where block b's K pages start, and element where its V pages start
@@ -597,6 +598,31 @@ struct NewRow {
 // =================================================================================
 // FUSE (unsplit only): the wave that reads a pair's last chunk first stores the
 // newest token (position ctx - 1, from sc.k_new / sc.v_new) into its slot.
+// The sequence with the r-th longest context (ties to the lower index), for S <=
+// kThreads: thread t counts the sequences that go before sequence t.  The unsplit
+// kernel runs one workgroup per CU and the hardware hands workgroups out in launch
+// order as CUs free up, so taking the longest contexts first (longest processing
+// time first) leaves the short ones to fill the end of the launch.  Called by the
+// whole workgroup; the ranks form a permutation, so exactly one thread matches r.
+__device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int r) {
+  __shared__ int c_lds[kThreads];
+  __shared__ int pick;
+  const int t = threadIdx.x;
+  if (t < S) c_lds[t] = context_lens[t];
+  __syncthreads();
+  if (t < S) {
+    const int c = c_lds[t];
+    int before = 0;
+    for (int u = 0; u < S; ++u) {
+      const int cu = c_lds[u];
+      before += (cu > c) | ((cu == c) & (u < t));
+    }
+    if (before == r) pick = t;
+  }
+  __syncthreads();
+  return uniform(pick);
+}
+
 template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
@@ -613,7 +639,8 @@ paged_decode_kernel(
   __shared__ float c_m[kWaves][16];
   __shared__ float c_l[kWaves][16];
 
-  const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int part = blockIdx.x, kvh = blockIdx.y;
+  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, blockIdx.z) : blockIdx.z;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
 
@@ -1647,6 +1674,7 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.slot_out = p.slot_out;
   sc.k_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.k_pool));
   sc.v_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.v_pool));
+  sc.lpt = !p.balanced && !p.prefix && p.max_parts == 1 && p.num_seqs <= kThreads;
   return sc;
 }
 
