@@ -593,11 +593,6 @@ struct NewRow {
   }
 };
 
-// =================================================================================
-// Kernel A: one workgroup per (partition, kv head, sequence)
-// =================================================================================
-// FUSE (unsplit only): the wave that reads a pair's last chunk first stores the
-// newest token (position ctx - 1, from sc.k_new / sc.v_new) into its slot.
 // The sequence with the r-th longest context (ties to the lower index), for S <=
 // kThreads: thread t counts the sequences that go before sequence t.  The unsplit
 // kernel runs one workgroup per CU and the hardware hands workgroups out in launch
@@ -623,6 +618,11 @@ __device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int 
   return uniform(pick);
 }
 
+// =================================================================================
+// Kernel A: one workgroup per (partition, kv head, sequence)
+// =================================================================================
+// FUSE (unsplit only): the wave that reads a pair's last chunk first stores the
+// newest token (position ctx - 1, from sc.k_new / sc.v_new) into its slot.
 template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
