@@ -68,8 +68,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-KV partition size (0 = unsplit, -1 = balanced; default: unsplit "
-                         "for the decode workload over a 16-bit pool, balanced otherwise)")
+                    help="split-KV partition size (0 = unsplit, -1 = balanced; default: "
+                         "pkv_decode_partition_size over a 16-bit pool, balanced over "
+                         "an 8-bit one)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -108,16 +109,15 @@ def calibrate():
                       "copies": 5}), flush=True)
 
 
-# the decode mode per workload: unsplit (one workgroup per sequence and kv head) for
-# the Llama-3-8B-shaped batch over a 16-bit pool, where it is the faster; balanced
-# split-KV for an fp8 / int8 pool (each key costs more ALU work to widen, so the even
-# split of the work over all CUs wins) and for the long contexts (8 sequences: too few
-# pairs to fill the chip unsplit)
-DEFAULT_PARTITION = {"decode": 0, "long": -1}
-
-
-def default_partition(workload, kv):
-    return -1 if kv in ("fp8", "int8") else DEFAULT_PARTITION[workload]
+def default_partition(pkv, wl):
+    """The decode mode: over a 16-bit pool, the library's choice from the host's
+    context lengths (unsplit for the Llama-3-8B-shaped batch, whose 512 pairs fill the
+    CUs; one round of fixed partitions for the 8 long contexts); balanced split-KV
+    over an fp8 / int8 pool, where each key costs more ALU work to widen and the even
+    split of the work over all CUs wins."""
+    if wl.kv_dtype in ("fp8", "int8"):
+        return -1
+    return pkv.pkv_decode_partition_size(wl.context_lens, wl.num_kv_heads, wl.max_context_len)
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}  # pool bytes per element
 
 
@@ -174,10 +174,6 @@ def main():
     import paged_kv_cache_146_amd as pkv
     from paged_kv_cache_146_amd import workloads as W
 
-    P = default_partition(a.workload, a.kv) if a.partition is None else a.partition
-    # one launch per step where the fused kernel exists (bf16 pool, whole contexts,
-    # balanced mode); the append + decode pair otherwise
-    a.fused = not a.separate and a.kv == "bf16" and not a.window and P in (-1, 0)
     if a.workload == "long":  # the long-context split-KV configuration
         wl = W.long_context_decode(seed=3)
         wl_text = ("long-context paged decode: 8 seqs, ctx U[32768,131072] (seed 3), H_q 64, "
@@ -185,6 +181,10 @@ def main():
     else:
         wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
         wl_text = "llama3-8b-shaped paged decode layer (one new token per sequence)"
+    P = default_partition(pkv, wl) if a.partition is None else a.partition
+    # the append inside the decode's launch where the fused kernel exists (bf16 pool,
+    # whole contexts); the append + decode pair otherwise
+    a.fused = not a.separate and a.kv == "bf16" and not a.window
     dev = "cuda"
     desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
                          wl.scale_mode)
@@ -237,7 +237,7 @@ def main():
                               slot_mapping_out=slots)
 
     def step():
-        if a.fused:  # the append and the decode in one launch
+        if a.fused:  # the append inside the decode's launch
             fused()
             return
         # slot mapping and scatter of the new tokens in one launch (the slots are
@@ -331,7 +331,8 @@ def main():
             "num_blocks": wl.num_blocks, "partition_size": P,
             "caches": "warm" if a.no_flush else "flushed before every step",
             "step": ("decode_append: slot mapping, store of the %d new tokens and the decode in "
-                     "one launch" % wl.num_seqs if a.fused else
+                     "one launch%s" % (wl.num_seqs, " + the partitions' reduce" if P > 0 else "")
+                     if a.fused else
                      "kv_cache_append (slot mapping + scatter of the %d new tokens, one launch) "
                      "+ paged_attention_decode" % wl.num_seqs),
         },

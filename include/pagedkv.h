@@ -228,6 +228,28 @@ int pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t nu
                                int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                                size_t* bytes);
 
+/* [P1 §4] Partition size for a decode step, from the context lengths as the host
+ * holds them (a serving loop knows them before it launches).  The unsplit and
+ * fixed-partition decodes run one workgroup per CU, handed out in launch order,
+ * so the step is fastest when the workgroups fill the CUs in few rounds of even
+ * work:
+ *   - 0 (unsplit, longest contexts first) when the (sequence, kv head) pairs with a
+ *     token already number at least num_cus, or when no split would cut anything;
+ *   - else the smallest multiple of 64, P >= 256 (a 64-token chunk for each of a
+ *     workgroup's four wavefronts), with num_kv_heads * sum_s ceil(ctx_s / P) <=
+ *     num_cus (one round of workgroups); 0 if that P cuts no context.
+ *   context_lens: HOST int32 [num_seqs], clamped to [0, max_context_len] as the
+ *     decode clamps them.
+ *   num_cus: compute units of the device the step runs on; <= 0 asks the current
+ *     HIP device.
+ *   partition_size: out, 0 or a positive multiple of 64, for
+ *     pkv_paged_attention_decode / pkv_decode_append.
+ * Errors: PKV_EINVAL (negative sizes, num_kv_heads < 1, null pointers), PKV_EHIP
+ * (no current device to ask). */
+int pkv_decode_partition_size(const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_kv_heads, int32_t max_context_len, int32_t num_cus,
+                              int32_t* partition_size);
+
 /* [P1 §4] Paged decode attention, one query token per sequence.
  * For sequence s and query head h (kv head h / (num_q_heads / num_kv_heads)):
  *   z_t = scale * <q[s][h], K_t>,  t < ctx_s, K_t/V_t found through
@@ -273,17 +295,18 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
 /* [P1 §4.1, §4] One decode step in one launch: the write path's append of each
  * sequence's newest token followed by decode, i.e. the same pool bytes and output
  * as pkv_kv_cache_append (positions ctx_s - 1) then pkv_paged_attention_decode
- * with the same partition_size, which is PKV_PARTITION_BALANCED or 0 (unsplit;
- * other positive multiples of 64 are PKV_EUNSUPPORTED: fixed partitions take the
- * two calls).  The newest token's K and V are taken straight from k_new / v_new
- * for the attention (the pool's copy of that slot is neither read nor waited
- * for) and stored into slot block_table[s][(ctx_s - 1) / B] * B + (ctx_s - 1) % B
- * by the same launch; a table entry outside the pool skips the store (slot -1).
+ * with the same partition_size (PKV_PARTITION_BALANCED, 0, or a positive multiple
+ * of 64: fixed partitions add the reduce launch).  The wavefront that reads the
+ * newest token's chunk first stores its K and V rows (from k_new / v_new) into slot
+ * block_table[s][(ctx_s - 1) / B] * B + (ctx_s - 1) % B and then reads them back
+ * from the pool like any other key; a table entry outside the pool skips the
+ * store (slot -1).
  *   k_new, v_new: device [num_seqs][num_kv_heads][head_dim] of the pool's type.
  *   Supported: f16 or bf16 pools with q of the same type (else PKV_EUNSUPPORTED).
  *   context_lens count the new token (ctx_s >= 1 for a sequence that has one;
- *   ctx_s = 0 stores nothing and gives zeros); their clamping, the workspace
- *   (pkv_decode_workspace_bytes with the same partition_size; none for 0) and
+ *   ctx_s = 0 stores nothing, leaves slot_mapping_out[s] as it was and gives
+ *   zeros); their clamping, the workspace (pkv_decode_workspace_bytes with the
+ *   same partition_size; none for 0) and
  *   the errors are those of pkv_paged_attention_decode.
  *   slot_mapping_out: optional device int64 [num_seqs], the slots written. */
 int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,

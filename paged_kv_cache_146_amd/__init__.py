@@ -35,7 +35,8 @@ PKV_ENOBLOCKS = -6
 
 EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_validate_block_table", "pkv_slot_mapping", "pkv_kv_cache_write",
-           "pkv_kv_cache_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
+           "pkv_kv_cache_append", "pkv_decode_workspace_bytes", "pkv_decode_partition_size",
+           "pkv_paged_attention_decode",
            "pkv_split_kv_reduce", "pkv_paged_prefill", "pkv_alloc_create", "pkv_alloc_destroy",
            "pkv_alloc_add_seq", "pkv_alloc_fork", "pkv_alloc_append", "pkv_alloc_free_seq",
            "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
@@ -92,6 +93,7 @@ def lib():
                     "pkv_kv_cache_append": (ctypes.c_int, [P, I32, I32, P, P, I32, P, P, I32, P,
                                                            P, P, P, P, P, P]),
                     "pkv_decode_workspace_bytes": (ctypes.c_int, [I32, I32, I32, I32, I32, I32, P]),
+                    "pkv_decode_partition_size": (ctypes.c_int, [P, I32, I32, I32, I32, P]),
                     "pkv_paged_attention_decode": (ctypes.c_int, [P, I32, I32, I32, P, P, P, P, P,
                                                                   P, I32, P, I32, F, I32, P, SZ,
                                                                   P, P]),
@@ -383,6 +385,21 @@ def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, ma
     return out.value
 
 
+def pkv_decode_partition_size(context_lens, num_kv_heads: int, max_context_len: int,
+                              num_cus: int = 0) -> int:
+    """The library's partition size for a decode step (0: unsplit), from HOST context
+    lengths (a sequence of ints or an int32 numpy array); num_cus <= 0 asks the
+    current device."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    out = ctypes.c_int32()
+    _check(lib().pkv_decode_partition_size(c.ctypes.data if c.size else None, int(c.size),
+                                           int(num_kv_heads), int(max_context_len),
+                                           int(num_cus), ctypes.byref(out)),
+           "pkv_decode_partition_size")
+    return out.value
+
+
 def pkv_paged_attention_decode(q, desc: PoolDesc, k_pool, v_pool, block_table, context_lens,
                                max_context_len: int, scale: float, partition_size: int = 0,
                                k_scale=None, v_scale=None, workspace=None, out=None,
@@ -474,9 +491,10 @@ def pkv_decode_append(q, desc: PoolDesc, k_pool, v_pool, block_table, context_le
                       max_context_len: int, k_new, v_new, scale: float,
                       partition_size: int = -1, workspace=None, out=None,
                       slot_mapping_out=None, stream=None):
-    """One decode step in one launch: stores each sequence's newest token (k_new /
-    v_new [S][H_kv][D], position ctx - 1) and returns the decode (balanced: -1, or
-    unsplit: 0)."""
+    """One decode step: stores each sequence's newest token (k_new / v_new
+    [S][H_kv][D], position ctx - 1) in the decode's launch and returns the decode
+    (balanced: -1, unsplit: 0, fixed partitions: a positive multiple of 64, which
+    adds the reduce launch)."""
     torch = _torch()
     S, Hq = int(q.shape[0]), int(q.shape[1])
     qd = dtype_code(q.dtype)

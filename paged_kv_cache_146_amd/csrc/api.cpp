@@ -6,6 +6,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "internal.hpp"
@@ -380,6 +381,92 @@ int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
                                            out, stream);
 }
 
+int pkv_decode_partition_size(const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_kv_heads, int32_t max_context_len, int32_t num_cus,
+                              int32_t* partition_size) {
+  if (!partition_size || num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0)
+    return PKV_EINVAL;
+  if (num_seqs > 0 && !context_lens) return PKV_EINVAL;
+  if (num_cus <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        num_cus < 1)
+      return PKV_EHIP;
+  }
+  int64_t live = 0, longest = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t c = std::min<int64_t>(std::max<int32_t>(context_lens[s], 0), max_context_len);
+    live += c > 0;
+    longest = std::max(longest, c);
+  }
+  *partition_size = 0;
+  if (live * num_kv_heads >= num_cus) return PKV_OK;  // the pairs fill the CUs already
+  // workgroups at P = 64 k tokens; non-increasing in k, and at most num_cus once
+  // every sequence is one partition (k = ceil(longest / 64)).  At least 4 chunks
+  // (k >= 4), one for each wavefront of a workgroup.
+  auto groups = [&](int64_t k) {
+    int64_t n = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int64_t c = std::min<int64_t>(std::max<int32_t>(context_lens[s], 0), max_context_len);
+      n += (c + 64 * k - 1) / (64 * k);
+    }
+    return n * num_kv_heads;
+  };
+  int64_t lo = 4, hi = std::max<int64_t>(4, (longest + 63) / 64);
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (groups(mid) <= num_cus)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  if (64 * lo < longest) *partition_size = (int32_t)(64 * lo);  // else nothing is cut
+  return PKV_OK;
+}
+
+// Fixed partitions of partition_size tokens: the decode writes each partition's
+// (normalised output, log-sum-exp) into the workspace, then the reduce merges them
+// into p.out.  The workspace layout follows max_context_len (the documented P_max).
+static int launch_partitioned(pkv::DecodeLaunch& p, int32_t partition_size,
+                              int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  size_t need = 0;
+  int rc = pkv_decode_workspace_bytes(p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim,
+                                      max_context_len, partition_size, &need);
+  if (rc != PKV_OK) return rc;
+  const int max_parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  p.max_parts = max_parts;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return PKV_EINVAL;
+  const size_t n_part = (size_t)p.num_seqs * p.num_q_heads * max_parts;
+  float* ws = static_cast<float*>(workspace);
+  p.split = 1;
+  p.part_size = partition_size;
+  p.part_out = ws;
+  p.part_max = ws ? ws + n_part * p.head_dim : nullptr;
+  p.part_sum = ws ? p.part_max + n_part : nullptr;
+  if (max_parts > 0) {
+    rc = pkv::launch_decode(p, as_stream(stream));
+    if (rc != 0) return rc;
+  }
+  pkv::ReduceLaunch r;
+  r.part_out = p.part_out;
+  r.part_max = p.part_max;
+  r.part_sum = p.part_sum;
+  r.context_lens = p.context_lens;
+  r.out = p.out;
+  r.out_dtype = p.q_dtype;
+  r.num_seqs = p.num_seqs;
+  r.num_q_heads = p.num_q_heads;
+  r.head_dim = p.head_dim;
+  r.part_size = partition_size;
+  r.max_parts = max_parts;
+  rc = pkv::launch_split_reduce(r, as_stream(stream));
+  return rc == 0 ? PKV_OK : rc;
+}
+
 int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t num_seqs,
                                       int32_t num_q_heads, const pkv_pool_desc* pool,
                                       const void* k_pool, const void* v_pool,
@@ -445,40 +532,8 @@ int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t nu
     return rc == 0 ? PKV_OK : rc;
   }
 
-  // workspace layout follows max_context_len (the documented P_max)
-  size_t need = 0;
-  rc = pkv_decode_workspace_bytes(num_seqs, num_q_heads, pool->num_kv_heads, pool->head_dim,
-                                  max_context_len, partition_size, &need);
-  if (rc != PKV_OK) return rc;
-  const int max_parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
-  p.max_parts = max_parts;
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return PKV_EINVAL;
-  const size_t n_part = (size_t)num_seqs * num_q_heads * max_parts;
-  float* ws = static_cast<float*>(workspace);
-  p.split = 1;
-  p.part_size = partition_size;
-  p.part_out = ws;
-  p.part_max = ws ? ws + n_part * pool->head_dim : nullptr;
-  p.part_sum = ws ? p.part_max + n_part : nullptr;
-  if (max_parts > 0) {
-    rc = pkv::launch_decode(p, as_stream(stream));
-    if (rc != 0) return rc;
-  }
-  pkv::ReduceLaunch r;
-  r.part_out = p.part_out;
-  r.part_max = p.part_max;
-  r.part_sum = p.part_sum;
-  r.context_lens = context_lens;
-  r.out = out;
-  r.out_dtype = q_dtype;
-  r.num_seqs = num_seqs;
-  r.num_q_heads = num_q_heads;
-  r.head_dim = pool->head_dim;
-  r.part_size = partition_size;
-  r.max_parts = max_parts;
-  rc = pkv::launch_split_reduce(r, as_stream(stream));
-  return rc == 0 ? PKV_OK : rc;
+  return launch_partitioned(p, partition_size, max_context_len, workspace, workspace_bytes,
+                            stream);
 }
 
 int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
@@ -489,10 +544,9 @@ int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t 
                       size_t workspace_bytes, void* out, int64_t* slot_mapping_out,
                       void* stream) {
   int rc = check_desc(pool);
-  if (partition_size != PKV_PARTITION_BALANCED && partition_size != 0) {
-    if (partition_size < 0 || partition_size % 64 != 0) return PKV_EINVAL;
-    return PKV_EUNSUPPORTED;  // fixed partitions: append and decode are two calls
-  }
+  if (partition_size != PKV_PARTITION_BALANCED &&
+      (partition_size < 0 || partition_size % 64 != 0))
+    return PKV_EINVAL;
   if (rc != PKV_OK) return rc;
   if (num_seqs < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
     return PKV_EINVAL;
@@ -539,6 +593,9 @@ int pkv_decode_append(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t 
   p.slot_out = slot_mapping_out;
   if (partition_size == PKV_PARTITION_BALANCED)
     return launch_balanced(p, workspace, workspace_bytes, stream);
+  if (partition_size > 0)  // the store goes with the partition holding the newest token
+    return launch_partitioned(p, partition_size, max_context_len, workspace, workspace_bytes,
+                              stream);
   p.split = 0;  // unsplit: one workgroup per (sequence, kv head)
   p.max_parts = 1;
   p.part_size = (int)((cap + 63) / 64 * 64);

@@ -99,7 +99,9 @@ struct DecodeScalars {
   int64_t* slot_out;
   uint8_t* k_pool_w;  // the pools, for those stores
   uint8_t* v_pool_w;
-  int lpt;  // unsplit workgroup kernel, S <= kThreads: sequences go out longest first
+  int lpt;     // workgroup kernel, S <= kThreads: sequences go out longest first
+  int kv_x;    // workgroup kernel grid (kv head, sequence, partition), else
+               // (partition, kv head, sequence) (more than 65535 partitions)
 };
 
 // 16-byte unit where block b's K pages start, and element where its V pages start
@@ -594,10 +596,11 @@ struct NewRow {
 };
 
 // The sequence with the r-th longest context (ties to the lower index), for S <=
-// kThreads: thread t counts the sequences that go before sequence t.  The unsplit
+// kThreads: thread t counts the sequences that go before sequence t.  The workgroup
 // kernel runs one workgroup per CU and the hardware hands workgroups out in launch
 // order as CUs free up, so taking the longest contexts first (longest processing
-// time first) leaves the short ones to fill the end of the launch.  Called by the
+// time first) leaves the short ones to fill the end of the launch; with fixed
+// partitions each partition index is a slice of the launch, taken the same way.  Called by the
 // whole workgroup; the ranks form a permutation, so exactly one thread matches r.
 __device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int r) {
   __shared__ int c_lds[kThreads];
@@ -621,8 +624,9 @@ __device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int 
 // =================================================================================
 // Kernel A: one workgroup per (partition, kv head, sequence)
 // =================================================================================
-// FUSE (unsplit only): the wave that reads a pair's last chunk first stores the
-// newest token (position ctx - 1, from sc.k_new / sc.v_new) into its slot.
+// FUSE: the wave that reads a pair's last chunk (in the workgroup whose partition
+// reaches the end of the context) first stores the newest token (position ctx - 1,
+// from sc.k_new / sc.v_new) into its slot.
 template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
@@ -639,8 +643,13 @@ paged_decode_kernel(
   __shared__ float c_m[kWaves][16];
   __shared__ float c_l[kWaves][16];
 
-  const int part = blockIdx.x, kvh = blockIdx.y;
-  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, blockIdx.z) : blockIdx.z;
+  // grid (kv head, sequence, partition): launch order runs over the kv heads first,
+  // so with H_kv a multiple of 8 every XCD (workgroups go to the 8 XCDs round-robin)
+  // takes the same kv head of every (sequence, partition), the same work
+  const int part = sc.kv_x ? blockIdx.z : blockIdx.x;
+  const int kvh = sc.kv_x ? blockIdx.x : blockIdx.y;
+  const int sidx = sc.kv_x ? blockIdx.y : blockIdx.z;
+  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, sidx) : sidx;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
 
@@ -689,7 +698,7 @@ paged_decode_kernel(
   NewRow<C> carry;
   bool carried = false;
   if constexpr (FUSE) {
-    if (wave == (nch - 1) % kWaves) {
+    if (t_end == ctx && wave == (nch - 1) % kWaves) {
       carry.load(sc, trow, ctx - 1, s, kvh, lane);
       if (SMALLB || nch - 1 < wave + 2 * kWaves) {
         carry.store(sc, lane);
@@ -1601,8 +1610,9 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
                        p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.counters, sc);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
-  dim3 grid(p.max_parts, p.num_kv_heads, p.num_seqs);
-  if (p.fuse) {  // unsplit decode fused with the append: 16-bit pools only
+  const dim3 grid = sc.kv_x ? dim3(p.num_kv_heads, p.num_seqs, p.max_parts)
+                            : dim3(p.max_parts, p.num_kv_heads, p.num_seqs);
+  if (p.fuse) {  // decode fused with the append: 16-bit pools only
     if constexpr (KVT == CT && (KVT == DT_F16 || KVT == DT_BF16)) {
       hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB, true>), grid, dim3(kThreads), 0,
                          st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
@@ -1674,7 +1684,8 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.slot_out = p.slot_out;
   sc.k_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.k_pool));
   sc.v_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.v_pool));
-  sc.lpt = !p.balanced && !p.prefix && p.max_parts == 1 && p.num_seqs <= kThreads;
+  sc.lpt = !p.balanced && !p.prefix && p.num_seqs <= kThreads;
+  sc.kv_x = p.max_parts <= 65535;
   return sc;
 }
 

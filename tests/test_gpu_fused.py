@@ -1,5 +1,6 @@
 """GPU parity of the fused decode step (pkv_decode_append): the newest token of each
-sequence is stored into its slot and attended to in the same launch.
+sequence is stored into its slot and attended to in the same launch (with fixed
+partitions, followed by the reduce launch).
 
 "03 | PagedAttention and the KV-cache memory system" §4.1 (the new token's K/V go to
 its slot through the slot mapping) and §4 (decode over the whole context).  The pool
@@ -50,22 +51,25 @@ def _run(wl, P=-1):
     got = slots.cpu().numpy()
     live = wl.context_lens > 0
     assert np.array_equal(got[live], want[live])
+    assert np.all(got[~live] == -7), "a sequence with no token must leave its slot entry"
+
     ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale)
     return assert_close(to_f64(out, wl.q_dtype), ref, "%s P=%d" % (wl.name, P))
 
 
-@pytest.mark.parametrize("P", [-1, 0])
+@pytest.mark.parametrize("P", [-1, 0, 128])
 def test_fused_llama3_small(P):
     print(_run(W.llama3_8b_decode(small=True), P))
 
 
-@pytest.mark.parametrize("P", [-1, 0])
+@pytest.mark.parametrize("P", [-1, 0, 128])
 @pytest.mark.parametrize("kv,Hq,Hkv,D,B", [
     ("bf16", 8, 2, 128, 16), ("f16", 4, 4, 64, 32), ("bf16", 8, 2, 64, 4), ("f16", 16, 1, 128, 64),
     ("bf16", 24, 8, 128, 8)])
 def test_fused_edge_contexts(kv, Hq, Hkv, D, B, P):
     """ctx in {0, 1, ...}: the newest token alone in its chunk, at a chunk or block
-    boundary, and sequences with no token at all."""
+    boundary, and sequences with no token at all; with 128-token partitions, also
+    alone in its partition (129) and at a partition's end (128)."""
     ctx = sorted({0, 1, 2, B - 1, B, B + 1, 63, 64, 65, 128, 129, 500, 1000})
     wl = W.make_decode("fused %s B%d" % (kv, B), 700 + B + Hq, ctx_lens=ctx, Hq=Hq, Hkv=Hkv,
                        D=D, B=B, kv_dtype=kv, spare_frac=0.1)
@@ -84,7 +88,7 @@ def test_fused_rejects_other_pools():
     assert e.value.status == -3
     bf = W.make_decode("fused bf16", 6, ctx_lens=[3, 9], Hq=4, Hkv=2, D=64, B=16, kv_dtype="bf16")
     cb = GpuCase(bf)
-    for P, status in ((512, -3), (100, -1), (-2, -1)):  # fixed partitions: two calls
+    for P, status in ((100, -1), (-2, -1), (32, -1)):  # not a multiple of 64, not a mode
         with pytest.raises(pkv.PagedKVError) as e:
             pkv.pkv_decode_append(cb.q, cb.desc, cb.k_pool, cb.v_pool, cb.block_table,
                                   cb.context_lens, bf.max_context_len, kn, kn, bf.scale,
@@ -92,7 +96,7 @@ def test_fused_rejects_other_pools():
         assert e.value.status == status
 
 
-@pytest.mark.parametrize("P", [-1, 0])
+@pytest.mark.parametrize("P", [-1, 0, 128])
 def test_fused_graph_replay(P):
     """The fused step captured in a graph and replayed (as a serving loop does), with an
     eager call between replays: every replay stores the same tokens and gives the

@@ -129,6 +129,48 @@ def test_decode_workspace_bytes():
         pkv.pkv_decode_workspace_bytes(2, 6, 4, 64, 100, 64)  # heads not divisible
 
 
+def _partition_by_scan(ctx, hkv, max_ctx, cus):
+    """The documented rule by linear scan over every candidate size."""
+    c = np.clip(np.asarray(ctx, np.int64), 0, max_ctx)
+    if int((c > 0).sum()) * hkv >= cus:
+        return 0
+    longest = int(c.max()) if c.size else 0
+    P = 256
+    while hkv * int(np.sum((c + P - 1) // P)) > cus:
+        P += 64
+    return P if P < longest else 0
+
+
+def test_decode_partition_size():
+    # the long-context batch (8 seqs, U[32768, 131072], seed 3): 22528-token partitions
+    # give 248 workgroups on 256 CUs; 22464 would give 264
+    ctx = np.random.default_rng(3).integers(32768, 131072 + 1, size=8)
+    assert pkv.pkv_decode_partition_size(ctx, 8, 131072, 256) == 22528
+    assert 8 * int(np.sum(-(-ctx // 22464))) > 256 >= 8 * int(np.sum(-(-ctx // 22528)))
+    # the Llama-3-8B-shaped batch: 512 pairs already fill 256 CUs
+    c2 = np.random.default_rng(2).integers(128, 4096 + 1, size=64)
+    assert pkv.pkv_decode_partition_size(c2, 8, 4096, 256) == 0
+    # nothing to cut, or no sequences: unsplit
+    assert pkv.pkv_decode_partition_size([], 8, 4096, 256) == 0
+    assert pkv.pkv_decode_partition_size([0, 0, 200], 1, 4096, 256) == 0
+    assert pkv.pkv_decode_partition_size([100, 3000], 1, 4096, 256) == 256  # the floor
+    # lengths past max_context_len count as max_context_len; negative ones as 0
+    assert (pkv.pkv_decode_partition_size([10 ** 6, -5], 2, 65536, 64)
+            == pkv.pkv_decode_partition_size([65536, 0], 2, 65536, 64))
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        n = int(rng.integers(0, 40))
+        hi = int(rng.choice([64, 1000, 20000, 200000]))
+        ctx = rng.integers(-10, hi, size=n).astype(np.int32)
+        hkv, cus = int(rng.integers(1, 9)), int(rng.choice([8, 64, 256, 304]))
+        max_ctx = int(rng.integers(0, hi + 1))
+        assert (pkv.pkv_decode_partition_size(ctx, hkv, max_ctx, cus)
+                == _partition_by_scan(ctx, hkv, max_ctx, cus)), (ctx, hkv, max_ctx, cus)
+    for args in (([1], 0, 10, 8), ([1], 1, -1, 8)):
+        with pytest.raises(pkv.PagedKVError):
+            pkv.pkv_decode_partition_size(*args)
+
+
 def test_validate_block_table():
     bt = np.array([[3, 1, 9], [0, 2, 9]], np.int32)
     pkv.pkv_validate_block_table(bt, [9, 5], 4, 10)
