@@ -269,7 +269,8 @@ int pkv_decode_partition_size(const int32_t* context_lens, int32_t num_seqs,
  *   max_context_len: host-known upper bound on context_lens (sizes the grid).
  *   partition_size: 0 = one pass per (sequence, kv head); a positive multiple
  *      of 64 = the context is split into partitions of that many tokens,
- *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]);
+ *      scanned in parallel and merged by log-sum-exp (split-KV, [P1 §4]; at most
+ *      8192 partitions of max_context_len, else PKV_EUNSUPPORTED);
  *      PKV_PARTITION_BALANCED = the 64-token chunks of all (sequence, kv head)
  *      pairs are cut into equal contiguous shares, one per resident wavefront,
  *      and the pairs that shares split are merged by log-sum-exp (same

@@ -437,6 +437,7 @@ static int launch_partitioned(pkv::DecodeLaunch& p, int32_t partition_size,
                                       max_context_len, partition_size, &need);
   if (rc != PKV_OK) return rc;
   const int max_parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+  if (max_parts > pkv::kMaxPartitions) return PKV_EUNSUPPORTED;  // the reduce's limit
   p.max_parts = max_parts;
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_EWORKSPACE;
   if (need > 0 && !aligned16(workspace)) return PKV_EINVAL;

@@ -99,9 +99,7 @@ struct DecodeScalars {
   int64_t* slot_out;
   uint8_t* k_pool_w;  // the pools, for those stores
   uint8_t* v_pool_w;
-  int lpt;     // workgroup kernel, S <= kThreads: sequences go out longest first
-  int kv_x;    // workgroup kernel grid (kv head, sequence, partition), else
-               // (partition, kv head, sequence) (more than 65535 partitions)
+  int lpt;  // workgroup kernel, S <= kThreads: sequences go out longest first
 };
 
 // 16-byte unit where block b's K pages start, and element where its V pages start
@@ -646,10 +644,8 @@ paged_decode_kernel(
   // grid (kv head, sequence, partition): launch order runs over the kv heads first,
   // so with H_kv a multiple of 8 every XCD (workgroups go to the 8 XCDs round-robin)
   // takes the same kv head of every (sequence, partition), the same work
-  const int part = sc.kv_x ? blockIdx.z : blockIdx.x;
-  const int kvh = sc.kv_x ? blockIdx.x : blockIdx.y;
-  const int sidx = sc.kv_x ? blockIdx.y : blockIdx.z;
-  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, sidx) : sidx;
+  const int part = blockIdx.z, kvh = blockIdx.x;
+  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, blockIdx.y) : blockIdx.y;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
 
@@ -1610,8 +1606,8 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
                        p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.counters, sc);
     return hipGetLastError() == hipSuccess ? 0 : -5;
   }
-  const dim3 grid = sc.kv_x ? dim3(p.num_kv_heads, p.num_seqs, p.max_parts)
-                            : dim3(p.max_parts, p.num_kv_heads, p.num_seqs);
+  if (p.max_parts > 65535) return -3;  // grid z (the reduce takes at most 8192)
+  const dim3 grid(p.num_kv_heads, p.num_seqs, p.max_parts);
   if (p.fuse) {  // decode fused with the append: 16-bit pools only
     if constexpr (KVT == CT && (KVT == DT_F16 || KVT == DT_BF16)) {
       hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB, true>), grid, dim3(kThreads), 0,
@@ -1685,7 +1681,6 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.k_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.k_pool));
   sc.v_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.v_pool));
   sc.lpt = !p.balanced && !p.prefix && p.num_seqs <= kThreads;
-  sc.kv_x = p.max_parts <= 65535;
   return sc;
 }
 
@@ -1758,7 +1753,7 @@ int balanced_worker_capacity(int kv, int qd, int D, int block_size) {
 }
 
 int launch_split_reduce(const ReduceLaunch& p, hipStream_t st) {
-  if (p.max_parts > 8192) return -3;
+  if (p.max_parts > kMaxPartitions) return -3;
   if (!p.context_lens && p.max_parts <= 64) {  // every slot, few of them: a wavefront per row
     const long long rows = (long long)p.num_seqs * p.num_q_heads;
     dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));

@@ -8,6 +8,9 @@
 
 namespace pkv {
 
+// most partitions per sequence the split-KV reduce takes (its weights sit in LDS)
+constexpr int kMaxPartitions = 8192;
+
 struct DecodeLaunch {
   const void* q;
   int q_dtype;

@@ -214,3 +214,42 @@ def test_shared_prefix_full_sampled():
     wl = W.shared_prefix_decode()
     seqs = np.array([0, 1, 100, 255] + [int(np.argmin(wl.context_lens))], np.int32)
     print(_run(wl, [0, 512, -1], seqs=seqs))
+
+
+def test_8192_partitions():
+    """64-token partitions with max_context_len = 8192 x 64, the most partitions the
+    reduce takes: a grid of 8192 partition slices, nearly all empty; the plain decode
+    and the fused step match the oracle."""
+    import paged_kv_cache_146_amd as pkv
+    from test_gpu_fused import _without_newest
+    from helpers import torch_bits
+    wl = W.make_decode("8192 partitions", 97, ctx_lens=[300, 5, 129, 0], Hq=4, Hkv=2, D=64,
+                       B=16, kv_dtype="bf16")
+    big = 8192 * 64
+    case = GpuCase(wl)
+    opool = oracle_pool(wl)
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale)
+    out = pkv.pkv_paged_attention_decode(case.q, case.desc, case.k_pool, case.v_pool,
+                                         case.block_table, case.context_lens, big, wl.scale,
+                                         partition_size=64, out=case.nan_out(),
+                                         q_dtype=wl.q_dtype)
+    print(assert_close(to_f64(out, wl.q_dtype), ref, "8192 partitions"))
+    w2, rows = _without_newest(wl)
+    c2 = GpuCase(w2)
+    r = np.where(rows >= 0, rows, 0)
+    out = pkv.pkv_decode_append(c2.q, c2.desc, c2.k_pool, c2.v_pool, c2.block_table,
+                                c2.context_lens, big, torch_bits(wl.k_src[r], wl.src_dtype),
+                                torch_bits(wl.v_src[r], wl.src_dtype), wl.scale,
+                                partition_size=64, out=c2.nan_out())
+    _check_pools(c2, opool)
+    print(assert_close(to_f64(out, wl.q_dtype), ref, "8192 partitions, fused"))
+
+
+def test_partition_size_from_the_device():
+    """num_cus <= 0 asks the current device: the same choice as passing its CU count."""
+    import torch
+    import paged_kv_cache_146_amd as pkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ctx = np.random.default_rng(3).integers(32768, 131072 + 1, size=8)
+    assert pkv.pkv_decode_partition_size(ctx, 8, 131072) == \
+        pkv.pkv_decode_partition_size(ctx, 8, 131072, cus)

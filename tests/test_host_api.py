@@ -207,6 +207,12 @@ def test_decode_argument_errors_caught_on_host():
     assert _decode_raw() == -1                        # NULL device pointers
     assert _decode_raw(num_seqs=0) == 0               # nothing to do
     assert _decode_raw(maxc=(1 << 30) + 1) == -3
+    # more than 8192 partitions: refused before anything is launched (the pointers
+    # are never dereferenced); 8192 pass on to the workspace check
+    fake = ctypes.c_void_p(1 << 16)
+    ptrs = dict(q=fake, k=fake, v=fake, bt=fake, cl=fake, out=fake, P=64)
+    assert _decode_raw(maxc=8192 * 64 + 1, **ptrs) == -3
+    assert _decode_raw(maxc=8192 * 64, **ptrs) == -4  # PKV_EWORKSPACE
 
 
 def test_write_and_prefill_argument_errors_caught_on_host():
