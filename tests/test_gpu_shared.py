@@ -78,6 +78,18 @@ def test_contexts_shorter_than_the_prefix():
     print(_check(wl, [256, 128], case=case))
 
 
+def test_contexts_inside_an_unaligned_prefix_tile():
+    """B 4 and declared shared lengths that are not multiples of 16 (92, 84): contexts
+    that end inside the last 16-token tile before the shared length (81, 85, 90) have
+    an empty tail, as do 92 and 0."""
+    wl = W.make_decode("unaligned shared length", 93, num_seqs=10, Hq=8, Hkv=2, D=64, B=4,
+                       kv_dtype="bf16", shared_prefix=96, tail_range=(1, 80))
+    wl.context_lens = wl.context_lens.copy()
+    wl.context_lens[[0, 1, 2, 3, 4, 5]] = [81, 85, 90, 92, 84, 0]
+    case = GpuCase(wl)
+    print(_check(wl, [92, 84], case=case))
+
+
 def test_long_prefix_many_slices_and_workspace_reuse():
     """A 4096-token prefix over 24 sequences (several prefix slices), twice in a row on a
     workspace filled with garbage, and against the plain balanced decode."""
