@@ -573,7 +573,9 @@ struct NewRow {
       if (lane + 64 * i < C::Dim) v[i] = vn[lane + 64 * i];
   }
 
-  // into the slot, as the cache write does (a table entry outside the pool skips it)
+  // into the slot, as the cache write does (a table entry outside the pool skips it);
+  // non-temporal: no later read in the launch but the owner's, and the lines need
+  // not stay in the caches
   __device__ __forceinline__ void store(const DecodeScalars& sc, int lane) const {
     const int B = 1 << sc.blog2;
     const bool inside = blk >= 0 && blk < sc.num_blocks;
@@ -581,7 +583,8 @@ struct NewRow {
     if (!inside) return;
     const size_t blk16 = block_k16(sc, blk);
     if (lane < C::NC)
-      reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off] = k;
+      __builtin_nontemporal_store(
+          k, &reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off]);
     // V page [B/TG][D][TG], TG = min(E, B)
     const int tgl = min(C::ELOG, sc.blog2);
     uint16_t* vp = reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E +
@@ -589,7 +592,7 @@ struct NewRow {
                    (off & ((1 << tgl) - 1));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) vp[(size_t)(lane + 64 * i) << tgl] = v[i];
+      if (lane + 64 * i < C::Dim) __builtin_nontemporal_store(v[i], &vp[(size_t)(lane + 64 * i) << tgl]);
   }
 };
 
