@@ -37,9 +37,12 @@
 // pools use the 16x16x4 f32 product with one k-slot per lane.
 //
 // Three ways to cut the work:
-//   unsplit / fixed partitions — one workgroup (4 waves) per (partition, kv
-//         head, sequence); the waves take chunks round-robin and merge in LDS;
-//         partitions are merged by split_reduce_kernel.
+//   unsplit / fixed partitions — one workgroup (4 waves) per (kv head,
+//         sequence, partition), kv heads first in launch order (workgroups go to
+//         the 8 XCDs round-robin, so with H_kv a multiple of 8 each XCD takes one
+//         kv head of every item) and, up to 256 sequences, longest context first;
+//         the waves take chunks round-robin and merge in LDS; partitions are
+//         merged by split_reduce_kernel.
 //   balanced — the chunks of all (sequence, kv head) pairs form one stream that
 //         is cut into equal contiguous shares, one per wavefront ("worker").  A
 //         worker finishes every pair it covers entirely and leaves a partial
@@ -50,13 +53,16 @@
 //         product columns; the balanced kernel takes the private tails and
 //         merge_slots_kernel merges the two.
 // Both main kernels also take a sliding window (a sequence's chunk grid starts
-// at its window's first 16-token tile), and the balanced one can store each
-// sequence's newest token itself before decoding (one launch per decode step).
-// Inside a wavefront the chunk loop is software-pipelined on single buffers:
-// the next chunk's K pieces are requested as soon as the current scores are
-// done and its V pieces as soon as the current P.V is done, the table entries
-// one chunk further ahead; two waves share each SIMD, so one computes while the
-// other waits.
+// at its window's first 16-token tile), and both can store each sequence's
+// newest token themselves before decoding it (the fused decode step).
+// The workgroup kernel's chunk loop is software-pipelined on one buffer: the
+// next chunk's K pieces are requested as soon as the current scores are done
+// and its V pieces as soon as the current P.V is done, the table entries one
+// chunk further ahead.  The balanced kernel's runs on two buffers (the next
+// chunk in flight while the current one is computed).  Both are compiled for
+// one wavefront per SIMD, whose registers hold the buffers: buffers beyond the
+// 256 architectural registers would live in AGPRs, and their copies cost more
+// than the deeper pipeline gains.
 #include "device.hpp"
 #include "internal.hpp"
 #include "tile.hpp"
