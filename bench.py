@@ -47,19 +47,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention µs/step + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_146_amd", "csrc", "decode.hip")
+# the sources the decode kernels are compiled from
+DECODE_SRC = [os.path.join(ROOT, "paged_kv_cache_146_amd", "csrc", f)
+              for f in ("decode.hip", "tile.hpp", "device.hpp", "internal.hpp")]
 # FETCH_SIZE / WRITE_SIZE per decode launch, one record per measured configuration
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 
-def source_hash(path) -> str:
-    """sha256 of a source file with its comments and blank space removed, so that
-    counters taken from it stay valid across comment-only edits."""
+def source_hash(paths) -> str:
+    """sha256 of source files with their comments and blank space removed, so that
+    counters taken from them stay valid across comment-only edits."""
     import re
-    txt = open(path).read()
-    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
-    txt = re.sub(r"//[^\n]*", " ", txt)
-    return hashlib.sha256(" ".join(txt.split()).encode()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        txt = open(path).read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(" ".join(txt.split()).encode() + b"\0")
+    return h.hexdigest()
 
 
 def parse():

@@ -85,23 +85,25 @@ __device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
 // eight int8 codes (two words) -> eight CT values; exact, as every int8 value is
 // an integer of at most 8 bits.  f16: each byte, sign bit flipped (u = x + 128),
 // becomes the f16 1024 + u by its bits, and a packed subtraction of 1152 leaves x.
-// bf16: the same with the f32 2^23 + u, then a conversion that is exact.
+// bf16: each byte sign-extended and converted to f32 (one instruction per code:
+// the conversion reads the byte in place), then a conversion that is exact.
 template <int CT>
 __device__ __forceinline__ u32x4 i8x8(uint32_t w0, uint32_t w1) {
-  const uint32_t w[2] = {w0 ^ 0x80808080u, w1 ^ 0x80808080u};
+  const uint32_t w[2] = {w0, w1};
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {  // bytes 2 hp, 2 hp + 1
-      const uint32_t u0 = (w[i] >> (16 * hp)) & 0xffu, u1 = (w[i] >> (16 * hp + 8)) & 0xffu;
       if constexpr (CT == DT_F16) {
+        const uint32_t x = w[i] ^ 0x80808080u;
+        const uint32_t u0 = (x >> (16 * hp)) & 0xffu, u1 = (x >> (16 * hp + 8)) & 0xffu;
         const f16x2 h = __builtin_bit_cast(f16x2, 0x64006400u | u0 | (u1 << 16));
         r[2 * i + hp] = __builtin_bit_cast(uint32_t, h - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
       } else {
         static_assert(CT == DT_BF16, "int8 widens to f16 or bf16");
-        const float a = __uint_as_float(0x4b000000u | u0) - 8388736.0f;  // 2^23 + 128
-        const float b = __uint_as_float(0x4b000000u | u1) - 8388736.0f;
+        const float a = (float)(signed char)(w[i] >> (16 * hp));
+        const float b = (float)(signed char)(w[i] >> (16 * hp + 8));
         r[2 * i + hp] = pack2<DT_BF16>(a, b);
       }
     }
