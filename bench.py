@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--separate", action="store_true",
                     help="decode workload: the append and the decode as two launches "
                          "(default: one launch per step, pkv_decode_append)")
+    ap.add_argument("--kv-block-major", action="store_true",
+                    help="decode workloads: one allocation holding each block's K pages "
+                         "then its V pages (block_stride = both), instead of two pools")
     ap.add_argument("--window", type=int, default=0,
                     help="decode workload: sliding window (keys [ctx - window, ctx)); 0 = all")
     ap.add_argument("--calibrate", action="store_true",
@@ -191,9 +194,18 @@ def main():
     # whole contexts); the append + decode pair otherwise
     a.fused = not a.separate and a.kv == "bf16" and not a.window
     dev = "cuda"
-    desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
-                         wl.scale_mode)
-    k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
+    if a.kv_block_major:  # [block][K pages | V pages]: a block's K and V in one run
+        dense = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                              wl.kv_dtype, wl.scale_mode)
+        page = pkv.pkv_pool_bytes(dense)[0] // wl.num_blocks
+        desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                             wl.kv_dtype, wl.scale_mode, block_stride=2 * page)
+        both = torch.full((wl.num_blocks * 2 * page,), 0xFF, dtype=torch.uint8, device=dev)
+        k_pool, v_pool = both, both[page:]
+    else:
+        desc = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
+                             wl.kv_dtype, wl.scale_mode)
+        k_pool, v_pool = pkv.alloc_pool(desc, fill_byte=0xFF)
     ks = torch.from_numpy(wl.k_scale).to(dev) if wl.k_scale is not None else None
     vs = torch.from_numpy(wl.v_scale).to(dev) if wl.v_scale is not None else None
     bt = torch.from_numpy(wl.block_table).to(dev)
@@ -299,7 +311,7 @@ def main():
     kbytes = sbytes if a.fused else dbytes  # algorithmic bytes of the timed kernel
     achieved = kbytes / (dec_us * 1e-6) / 1e9
     traffic = None
-    if os.path.exists(COUNTERS):
+    if os.path.exists(COUNTERS) and not a.kv_block_major:  # records: two pools
         # valid only for the configuration and the decode source they were taken on
         want = {"workload": a.workload, "partition_size": P, "fused": a.fused,
                 "kv_dtype": wl.kv_dtype, "scale_mode": wl.scale_mode, "window": a.window,
@@ -331,6 +343,8 @@ def main():
             "sum_context": int(wl.context_lens.sum()), "H_q": wl.num_q_heads,
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
             "kv_dtype": wl.kv_dtype,
+            "pool_layout": ("one allocation, each block's K pages then its V pages"
+                            if a.kv_block_major else "separate K and V pools"),
             "scale_mode": wl.scale_mode if wl.kv_dtype in ("fp8", "int8") else None,
             "window": a.window if a.window > 0 else None,
             "num_blocks": wl.num_blocks, "partition_size": P,
