@@ -253,3 +253,32 @@ def test_partition_size_from_the_device():
     ctx = np.random.default_rng(3).integers(32768, 131072 + 1, size=8)
     assert pkv.pkv_decode_partition_size(ctx, 8, 131072) == \
         pkv.pkv_decode_partition_size(ctx, 8, 131072, cus)
+
+
+def test_sequence_order_invariance_bitwise():
+    """Permuting the batch's sequences (q, table rows, lengths; the same slots) permutes
+    the output bit for bit in the unsplit and fixed-partition modes: their workgroups take
+    sequences by rank of context length, and each computes its (sequence, kv head,
+    partition) the same way whatever the order (the balanced mode cuts the work by
+    position in the batch, so only its values are order-free)."""
+    import torch
+    wl = W.make_decode("order", 92, ctx_range=(1, 900), num_seqs=9, Hq=16, Hkv=4, D=128, B=16,
+                       kv_dtype="bf16", spare_frac=0.3)
+    wl.context_lens = wl.context_lens.copy()
+    wl.context_lens[[2, 5]] = wl.context_lens[7]  # ties in length
+    a = GpuCase(wl)
+    perm = np.random.default_rng(7).permutation(wl.num_seqs)
+    inv = np.argsort(perm)
+    wl2 = W.Workload(**{**wl.__dict__})
+    wl2.q = wl.q[perm]
+    wl2.block_table = np.ascontiguousarray(wl.block_table[perm])
+    wl2.context_lens = np.ascontiguousarray(wl.context_lens[perm])
+    wl2.fill_seq = inv[wl.fill_seq].astype(np.int32)
+    b = GpuCase(wl2)
+    for P in (0, 128):
+        oa = a.decode(partition_size=P).cpu()
+        ob = b.decode(partition_size=P).cpu()
+        assert torch.equal(oa[torch.from_numpy(perm)].view(torch.int16), ob.view(torch.int16)), P
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, oracle_pool(wl), wl.block_table, wl.context_lens,
+                              wl.scale)
+    print(assert_close(to_f64(b.decode(partition_size=-1), wl.q_dtype), ref[perm], "balanced"))
