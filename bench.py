@@ -180,7 +180,7 @@ def main():
         sys.exit(2)
     import torch
     import paged_kv_cache_146_amd as pkv
-    from paged_kv_cache_146_amd import workloads as W
+    import workloads as W
 
     if a.workload == "long":  # the long-context split-KV configuration
         wl = W.long_context_decode(seed=3)
@@ -391,7 +391,7 @@ def prefill_flops(wl) -> float:
 def prefill_main(a):
     import torch
     import paged_kv_cache_146_amd as pkv
-    from paged_kv_cache_146_amd import workloads as W
+    import workloads as W
 
     wl = W.fp8_chunked_prefill(seed=5)
     dev = "cuda"
@@ -577,7 +577,7 @@ def shared_main(a):
     balanced decode of the same batch is timed beside it."""
     import torch
     import paged_kv_cache_146_amd as pkv
-    from paged_kv_cache_146_amd import workloads as W
+    import workloads as W
 
     wl = W.shared_prefix_decode(seed=4)
     shared_len = wl.shared_blocks * wl.block_size

@@ -16,8 +16,10 @@ Only the tests use this module; it shares nothing with the library's allocator.
 reference counts of shared prefix blocks.
 
 Where the pages are silent (the order in which a finished sequence's blocks go
-back to the free list), the model takes the library's documented choice:
-reverse table order, so the sequence's first block is handed out next.
+back to the free list) the model takes this reading: the pages hand out the last
+element of the free list, and a release pushes the sequence's blocks in reverse
+table order, so that the list gives them back in the order the sequence took
+them (its first block is handed out next).
 """
 from __future__ import annotations
 

@@ -10,6 +10,7 @@
 #include <atomic>
 
 #include "internal.hpp"
+#include "slot.hpp"
 
 namespace {
 
@@ -127,18 +128,15 @@ int pkv_pool_bytes(const pkv_pool_desc* pool, size_t* k_bytes, size_t* v_bytes,
   return PKV_OK;
 }
 
-// "KV Cache: capacity, layout, lifecycle", Page-table addressing: the page's
-// reference, with its ValueError cases as PKV_EINVAL and IndexError as PKV_ERANGE.
+// The slot rule the write kernels use (slot.hpp), on one host-side table row:
+// a bad argument is PKV_EINVAL and an unmapped logical block PKV_ERANGE.
 int pkv_physical_slot(const int32_t* table, int32_t table_len, int32_t block_size,
                       int64_t token_pos, int64_t* slot) {
   if (!slot || table_len < 0 || (table_len > 0 && !table)) return PKV_EINVAL;
-  if (block_size <= 0 || token_pos < 0) return PKV_EINVAL;
-  const int64_t logical = token_pos / block_size;
-  const int64_t offset = token_pos % block_size;
-  if (logical >= table_len) return PKV_ERANGE;
-  const int64_t phys = table[logical];
-  if (phys < 0) return PKV_EINVAL;
-  *slot = phys * block_size + offset;
+  const pkv::SlotLookup r = pkv::lookup_slot(table, table_len, block_size, token_pos);
+  if (r.fault == pkv::kSlotUnmapped) return PKV_ERANGE;
+  if (r.fault != pkv::kSlotOk) return PKV_EINVAL;
+  *slot = r.slot;
   return PKV_OK;
 }
 
@@ -448,8 +446,12 @@ static int launch_partitioned(pkv::DecodeLaunch& p, int32_t partition_size,
   p.part_out = ws;
   p.part_max = ws ? ws + n_part * p.head_dim : nullptr;
   p.part_sum = ws ? p.part_max + n_part : nullptr;
-  if (max_parts > 0) {
+  if (max_parts > 0 || p.fuse) {
+    // (fused with the append and max_context_len == 0: one empty partition slice
+    // appends the new tokens and writes no partial)
+    if (max_parts == 0) p.max_parts = 1;
     rc = pkv::launch_decode(p, as_stream(stream));
+    p.max_parts = max_parts;
     if (rc != 0) return rc;
   }
   pkv::ReduceLaunch r;
@@ -464,6 +466,7 @@ static int launch_partitioned(pkv::DecodeLaunch& p, int32_t partition_size,
   r.head_dim = p.head_dim;
   r.part_size = partition_size;
   r.max_parts = max_parts;
+  r.ctx_cap = p.ctx_cap;  // no partition past the decode's clamp was written
   rc = pkv::launch_split_reduce(r, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }
@@ -729,6 +732,7 @@ int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t nu
   r.head_dim = pool->head_dim;
   r.part_size = 1;
   r.max_parts = sp.max_parts;
+  r.ctx_cap = 0x7fffffff;
   rc = pkv::launch_split_reduce(r, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }
@@ -757,6 +761,7 @@ int pkv_split_kv_reduce(const float* part_out, const float* part_max, const floa
   r.head_dim = head_dim;
   r.part_size = partition_size;
   r.max_parts = max_partitions;
+  r.ctx_cap = 0x7fffffff;  // only max_partitions * partition_size clamps here
   int rc = pkv::launch_split_reduce(r, as_stream(stream));
   return rc == 0 ? PKV_OK : rc;
 }

@@ -20,26 +20,23 @@
 // to even, clamped to +-127).
 #include "device.hpp"
 #include "internal.hpp"
+#include "slot.hpp"
 
 namespace pkv {
 
 constexpr int kWriteThreads = 256;
 
-// slot of token i: table[s][pos / B] * B + pos mod B, or -1 (padding) wherever
-// the host reference raises (sequence out of range, negative position, logical
-// block past the table, negative table entry)
+// slot of token i by the pool's address rule (slot.hpp) on its sequence's table
+// row, or -1 (padding) for a sequence out of range and wherever the rule faults
 __device__ __forceinline__ long long token_slot(const int32_t* __restrict__ block_table,
                                                 int num_seqs, int W,
                                                 const int32_t* __restrict__ seq_idx,
                                                 const int32_t* __restrict__ positions,
                                                 long long i, int B) {
   const int s = seq_idx[i];
-  const int pos = positions[i];
-  if (s < 0 || s >= num_seqs || pos < 0) return -1;
-  const int j = pos / B;
-  if (j >= W) return -1;
-  const int phys = block_table[(size_t)s * W + j];
-  return phys >= 0 ? (long long)phys * B + (pos - j * B) : -1;
+  if (s < 0 || s >= num_seqs) return -1;
+  const SlotLookup r = lookup_slot(block_table + (size_t)s * W, W, B, positions[i]);
+  return r.fault == kSlotOk ? r.slot : -1;
 }
 
 __global__ __launch_bounds__(kWriteThreads) void slot_mapping_kernel(

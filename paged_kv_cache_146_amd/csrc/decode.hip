@@ -103,8 +103,6 @@ struct DecodeScalars {
   const uint8_t* k_new;
   const uint8_t* v_new;
   int64_t* slot_out;
-  uint8_t* k_pool_w;  // the pools, for those stores
-  uint8_t* v_pool_w;
   int lpt;  // workgroup kernel, S <= kThreads: sequences go out longest first
 };
 
@@ -554,53 +552,99 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
   }
 }
 
-// ---- the newest token of a pair, stored by the decode (decode fused with append) -----
-// The K and V rows of kv head kvh of sequence s, from the caller's k_new / v_new,
-// for the slot of position pos, spread over the wave's lanes: lane L holds K piece
-// L (lanes below D/8) and V elements L and L + 64 (those below D).  load() only
-// requests them, so the stores can be issued later, after other requests.
+// ---- the newest token of a pair (decode fused with the append) -------------------
+// Its K and V rows come from the caller (k_new / v_new [S][H_kv][D], the pool's
+// 16-bit type).  The wave that reads the pair's last visible chunk does not read
+// that token back from the pool: once the chunk's loads have arrived it replaces
+// the token's K pieces and V elements in its registers by the caller's row
+// (patch_k, patch_v).  So no read of the launch depends on the store of the new
+// row into the pool, and the store may complete at any time before the launch
+// ends.  Between its load and its use the row sits in LDS, 2 NC pieces of 16
+// bytes: K pieces 0 .. NC-1 (8 dims each), then V pieces 0 .. NC-1 (8 dims each).
+
+// lane L < NC loads K piece L of the row, NC <= L < 2 NC the V piece L - NC
 template <class C>
-struct NewRow {
-  u32x4 k;
-  uint16_t v[2];
-  int blk, off, s, kvh;
+__device__ __forceinline__ u32x4 new_row_load(const DecodeScalars& sc, int s, int kvh, int lane) {
+  const size_t row = ((size_t)s * sc.Hkv + kvh) * C::NC;  // in 16-byte pieces
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if (lane < C::NC)
+    w = reinterpret_cast<const u32x4*>(sc.k_new)[row + lane];
+  else if (lane < 2 * C::NC)
+    w = reinterpret_cast<const u32x4*>(sc.v_new)[row + lane - C::NC];
+  return w;
+}
 
-  __device__ __forceinline__ void load(const DecodeScalars& sc, const int32_t* __restrict__ trow,
-                                       int pos, int s_, int kvh_, int lane) {
-    s = s_;
-    kvh = kvh_;
-    blk = trow[pos >> sc.blog2];
-    off = pos & ((1 << sc.blog2) - 1);
-    const size_t row = ((size_t)s * sc.Hkv + kvh) * C::Dim;  // element index of the rows
-    if (lane < C::NC) k = reinterpret_cast<const u32x4*>(sc.k_new)[row / C::E + lane];
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(sc.v_new) + row;
+// Store the row held in LDS into the slot of position pos of the sequence, as the
+// append does: no store (slot -1) when pos / B is past the table or the table
+// entry lies outside the pool; slot_out receives the slot.  The pool pointers are
+// the kernel's own (const only for the decode's reads).
+template <class C>
+__device__ __forceinline__ void new_row_store(const DecodeScalars& sc, const uint8_t* k_pool,
+                                              const uint8_t* v_pool, const int32_t* trow,
+                                              const u32x4* row, int pos, int s, int kvh,
+                                              int lane) {
+  const int B = 1 << sc.blog2;
+  const int j = pos >> sc.blog2, off = pos & (B - 1);
+  const int blk = j < sc.W ? trow[j] : -1;
+  const bool inside = blk >= 0 && blk < sc.num_blocks;
+  if (sc.slot_out && kvh == 0 && lane == 0) sc.slot_out[s] = inside ? (int64_t)blk * B + off : -1;
+  if (!inside) return;
+  const size_t blk16 = block_k16(sc, blk);
+  u32x4* kp = reinterpret_cast<u32x4*>(const_cast<uint8_t*>(k_pool));
+  if (lane < C::NC) __builtin_nontemporal_store(row[lane], &kp[blk16 + ((size_t)kvh * C::NC + lane) * B + off]);
+  // V page [B/TG][D][TG], TG = min(E, B): dims lane and lane + 64
+  const uint16_t* vrow = reinterpret_cast<const uint16_t*>(row + C::NC);
+  const int tgl = min(C::ELOG, sc.blog2);
+  uint16_t* vp = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(v_pool)) + blk16 * C::E +
+                 (size_t)kvh * C::Dim * B + ((size_t)(off >> tgl) * C::Dim << tgl) +
+                 (off & ((1 << tgl) - 1));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) v[i] = vn[lane + 64 * i];
-  }
+  for (int i = 0; i < 2; ++i)
+    if (lane + 64 * i < C::Dim)
+      __builtin_nontemporal_store(vrow[lane + 64 * i], &vp[(size_t)(lane + 64 * i) << tgl]);
+}
 
-  // into the slot, as the cache write does (a table entry outside the pool skips it);
-  // non-temporal: no later read in the launch but the owner's, and the lines need
-  // not stay in the caches
-  __device__ __forceinline__ void store(const DecodeScalars& sc, int lane) const {
-    const int B = 1 << sc.blog2;
-    const bool inside = blk >= 0 && blk < sc.num_blocks;
-    if (sc.slot_out && kvh == 0 && lane == 0) sc.slot_out[s] = inside ? (int64_t)blk * B + off : -1;
-    if (!inside) return;
-    const size_t blk16 = block_k16(sc, blk);
-    if (lane < C::NC)
-      __builtin_nontemporal_store(
-          k, &reinterpret_cast<u32x4*>(sc.k_pool_w)[blk16 + ((size_t)kvh * C::NC + lane) * B + off]);
-    // V page [B/TG][D][TG], TG = min(E, B)
-    const int tgl = min(C::ELOG, sc.blog2);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(sc.v_pool_w) + blk16 * C::E +
-                   (size_t)kvh * C::Dim * B + ((size_t)(off >> tgl) * C::Dim << tgl) +
-                   (off & ((1 << tgl) - 1));
+// The newest token is key r (0 <= r < 64, wave-uniform) of the chunk in registers.
+// K: tile r / 16, row r % 16, so lanes n = r % 16 hold its pieces 4 pq + g.
+template <class C>
+__device__ __forceinline__ void patch_k(u32x4 (&kr)[C::NK], const u32x4* row, int r, int n, int g) {
+  const int T = r >> 4;
+  const bool mine = n == (r & 15);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (lane + 64 * i < C::Dim) __builtin_nontemporal_store(v[i], &vp[(size_t)(lane + 64 * i) << tgl]);
+  for (int pq = 0; pq < C::NPL; ++pq) {
+    const u32x4 x = row[4 * pq + g];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t == T) kr[t * C::NPL + pq] = mine ? x : kr[t * C::NPL + pq];
   }
-};
+}
+
+// V: piece [dt][T] of lane (n, g) holds dim 16 dt + n at keys 16 T + 4 g + (0..3),
+// two 16-bit elements per word; the lanes g = (r % 16) / 4 hold key r as element r % 4.
+template <class C>
+__device__ __forceinline__ void patch_v(typename C::VPiece (&vr)[C::NV], const u32x4* row, int r,
+                                        int n, int g) {
+  static_assert(C::EB == 2, "the fused step stores 16-bit pools");
+  const uint16_t* vrow = reinterpret_cast<const uint16_t*>(row + C::NC);
+  const int T = r >> 4, wd = (r >> 1) & 1, sh = 16 * (r & 1);
+  const bool mine = g == ((r >> 2) & 3);
+  const uint32_t keep = ~(0xffffu << sh);
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) {
+    const uint32_t x = (uint32_t)vrow[16 * dt + n] << sh;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t == T) {
+        auto& pc = vr[dt * 4 + t];
+        const uint32_t w = wd ? pc[1] : pc[0];
+        const uint32_t nw = mine ? (w & keep) | x : w;
+        if (wd)
+          pc[1] = nw;
+        else
+          pc[0] = nw;
+      }
+  }
+}
 
 // The sequence with the r-th longest context (ties to the lower index), for S <=
 // kThreads: thread t counts the sequences that go before sequence t.  The workgroup
@@ -631,9 +675,10 @@ __device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int 
 // =================================================================================
 // Kernel A: one workgroup per (partition, kv head, sequence)
 // =================================================================================
-// FUSE: the wave that reads a pair's last chunk (in the workgroup whose partition
-// reaches the end of the context) first stores the newest token (position ctx - 1,
-// from sc.k_new / sc.v_new) into its slot.
+// FUSE: the wave that reads a pair's last visible chunk (in the workgroup whose
+// partition reaches the end of the clamped context) also appends the newest token
+// (position ctx - 1, from sc.k_new / sc.v_new): it stores the row into its slot at
+// the start and patches it into its registers at that chunk.
 template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
@@ -649,6 +694,7 @@ paged_decode_kernel(
   __shared__ float c_acc[kWaves][16][D];
   __shared__ float c_m[kWaves][16];
   __shared__ float c_l[kWaves][16];
+  __shared__ u32x4 new_lds[FUSE ? 2 * C::NC : 1];  // the appended row (FUSE)
 
   // grid (kv head, sequence, partition): launch order runs over the kv heads first,
   // so with H_kv a multiple of 8 every XCD (workgroups go to the 8 XCDs round-robin)
@@ -658,12 +704,22 @@ paged_decode_kernel(
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
 
-  int ctx = context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > sc.ctx_cap ? sc.ctx_cap : ctx);
+  const int ctx_raw = max(context_lens[s], 0);
+  const int ctx = min(ctx_raw, sc.ctx_cap);
   const int lo = window_lo(ctx, sc.window);
   const int t_begin = max(part * sc.part_size, lo & ~15);
   const int t_end = min(part * sc.part_size + sc.part_size, ctx);
   if (t_begin >= t_end) {
+    if constexpr (FUSE) {
+      // a new token past a clamped context of 0 is still appended (by partition 0)
+      if (part == 0 && ctx == 0 && ctx_raw > 0 && wave == 0) {
+        const u32x4 w = new_row_load<C>(sc, s, kvh, lane);
+        if (lane < 2 * C::NC) new_lds[lane] = w;
+        wave_lds_sync();
+        new_row_store<C>(sc, k_pool, v_pool, block_table + (size_t)s * sc.W, new_lds, ctx_raw - 1,
+                         s, kvh, lane);
+      }
+    }
     if (!sc.split && part == 0) {  // empty context: zeros
       for (int i = threadIdx.x; i < sc.G * D; i += kThreads) {
         size_t o = ((size_t)s * sc.Hq + (size_t)kvh * sc.G) * D + i;
@@ -693,34 +749,40 @@ paged_decode_kernel(
   const int nch = (t_end - t_begin + 63) >> 6;
   const int cnt = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;  // chunks wave, wave+4, ...
   auto base_of = [&](int i) { return t_begin + 64 * (wave + kWaves * min(i, cnt - 1)); };
-  // FUSE: only the wave that reads the last chunk stores the newest token.  The
-  // memory counter is in order, so a chunk requested after that wave has waited for
-  // a chunk requested after the stores sees them.  Its first two chunks can be
-  // requested before such a wait: when the last chunk is one of them, the stores go
-  // first and are waited for; otherwise the rows are requested first and stored
-  // once the first chunk has been requested (SMALLB: stored at once, chunk 0 is
-  // waited for before chunk 1 is requested).
-  NewRow<C> carry;
-  bool carried = false;
-  if constexpr (FUSE) {
-    if (t_end == ctx && wave == (nch - 1) % kWaves) {
-      carry.load(sc, trow, ctx - 1, s, kvh, lane);
-      if (SMALLB || nch - 1 < wave + 2 * kWaves) {
-        carry.store(sc, lane);
-        if (!SMALLB || nch - 1 == wave) __builtin_amdgcn_s_waitcnt(0);
-      } else {
-        carried = true;
+  // FUSE: the wave that reads the last chunk requests the new row first (its first
+  // chunk's loads go out behind it), parks it in LDS, stores it into the pool and,
+  // when the newest token is visible (the context was not clamped), patches it into
+  // its last chunk; r_new is that token's key index in the chunk.
+  const bool fuse_wave = FUSE && t_end == ctx && wave == (nch - 1) % kWaves;
+  const bool patch = fuse_wave && ctx == ctx_raw;
+  const int r_new = ctx - 1 - base_of(cnt - 1);
+  u32x4 new_w;
+  if constexpr (FUSE)
+    if (fuse_wave) new_w = new_row_load<C>(sc, s, kvh, lane);
+  auto park_and_store = [&]() {
+    if constexpr (FUSE) {
+      if (fuse_wave) {
+        issue_point();  // behind the first chunk's requests
+        if (lane < 2 * C::NC) new_lds[lane] = new_w;
+        wave_lds_sync();
+        new_row_store<C>(sc, k_pool, v_pool, trow, new_lds, ctx_raw - 1, s, kvh, lane);
       }
     }
-  }
+  };
 
   if constexpr (SMALLB) {
+    park_and_store();
     for (int i = 0; i < cnt; ++i) {
       const int base = base_of(i);
       Chunk<C> ch;
       float ks[16], vs[16];
       load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow, base, t_end, kvh, sc, n, g,
                     lo);
+      if constexpr (FUSE)
+        if (patch && i == cnt - 1) {
+          patch_k<C>(ch.k, new_lds, r_new, n, g);
+          patch_v<C>(ch.v, new_lds, r_new, n, g);
+        }
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
       chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g,
@@ -742,12 +804,14 @@ paged_decode_kernel(
       if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
       issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
     }
-    if constexpr (FUSE)
-      if (carried) carry.store(sc, lane);
+    park_and_store();
     Pages p1 = pages_of(trow, base_of(1), t_end, sc);
     for (int i = 0; i < cnt; ++i) {
       const int b0 = base_of(i);
       const bool more = i + 1 < cnt;
+      const bool patch_now = FUSE && patch && !more;
+      if constexpr (FUSE)
+        if (patch_now) patch_k<C>(R.k, new_lds, r_new, n, g);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, R.k, qop);
       issue_point();
@@ -761,6 +825,8 @@ paged_decode_kernel(
         p2 = pages_of(trow, base_of(i + 2), t_end, sc);
       }
       issue_point();
+      if constexpr (FUSE)
+        if (patch_now) patch_v<C>(R.v, new_lds, r_new, n, g);
       chunk_softmax_pv<C, KVT, CT>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0),
                                    g, 64, lo - b0);
       issue_point();
@@ -884,6 +950,10 @@ __device__ __forceinline__ int worker_of(int u, int U, int NWe) {
 // finisher leaves (epoch, 0) behind, so no zero-fill is ever needed and replays
 // of the same call stay correct.  Lock-free: a failed exchange means another
 // worker made progress; nothing waits on anyone.
+// Memory order: each successful exchange releases (agent scope) the worker's
+// stores of its piece; the exchanges on one counter form a release sequence, so
+// the winner's acquire fence, after its own exchange read the last of them, makes
+// every piece of the pair visible to its merge.
 __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch, uint32_t npieces) {
   unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   while (true) {
@@ -892,9 +962,11 @@ __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch,
     const bool last = n2 >= npieces;
     const unsigned long long nw = ((unsigned long long)epoch << 32) | (last ? 0u : n2);
     unsigned long long expected = old;
-    if (__hip_atomic_compare_exchange_strong(c, &expected, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
+    if (__hip_atomic_compare_exchange_strong(c, &expected, nw, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return last ? 1 : 0;
+    }
     old = expected;
   }
 }
@@ -970,10 +1042,10 @@ struct Pos {
   int u, s, kvh, j, nch, ctx, k, lo, st;
 };
 
-// FUSE: before its first load, each worker stores the newest token (position
-// ctx - 1, from sc.k_new / sc.v_new) of every pair whose last chunk lies in its
-// share, and waits for those stores; only that worker ever reads that chunk, so the
-// decode then reads the token from the pool like any other.
+// FUSE: the worker that reads a pair's last chunk also appends the pair's newest
+// token (position ctx - 1, from sc.k_new / sc.v_new): the row is requested with
+// that chunk's loads, stored into its slot when the chunk is computed, and patched
+// into the chunk's registers (never read back from the pool).
 template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_balanced_kernel(
@@ -987,6 +1059,7 @@ paged_decode_balanced_kernel(
 
   extern __shared__ int prefix[];  // [S + 1]
   __shared__ int tmp[kThreads];
+  __shared__ u32x4 new_lds[kWaves][FUSE ? 2 * C::NC : 1];  // each wave's appended row (FUSE)
 
   unit_prefix(context_lens, sc.S, sc.ctx_off, sc.ctx_cap, sc.window, sc.Hkv, prefix, tmp);
   const int U = prefix[sc.S];
@@ -1006,6 +1079,20 @@ paged_decode_balanced_kernel(
       } else {
         for (int i = threadIdx.x; i < sc.Hq * D; i += kThreads)
           store_any(out, CT, (size_t)s0 * sc.Hq * D + i, 0.0f);
+      }
+      if constexpr (FUSE) {
+        // a new token past a clamped context of 0 is still appended
+        const int raw = max(context_lens[s0], 0);
+        const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+        if (raw > 0)
+          for (int h = wv; h < sc.Hkv; h += kWaves) {
+            const u32x4 w = new_row_load<C>(sc, s0, h, ln);
+            if (ln < 2 * C::NC) new_lds[wv][ln] = w;
+            wave_lds_sync();
+            new_row_store<C>(sc, k_pool, v_pool, block_table + (size_t)s0 * sc.W, new_lds[wv],
+                             raw - 1, s0, h, ln);
+            wave_lds_sync();
+          }
       }
     }
   }
@@ -1070,55 +1157,22 @@ paged_decode_balanced_kernel(
   auto piece_ends = [&](const Pos& p) { return p.j == p.nch - 1 || p.k + 1 >= n_units; };
   auto trow_of = [&](const Pos& p) { return block_table + (size_t)p.s * sc.W + sc.tbl_off; };
 
-  // FUSE: the newest token of every pair whose last chunk is in this share is
-  // stored by this worker before it reads that chunk.  The memory counter is in
-  // order, so once the chunk loop has waited for a chunk requested after a store,
-  // that store has completed and every chunk requested afterwards sees it; only the
-  // first three chunks of the share can be requested before such a wait.
-  NewRow<C> carry[2];  // stored after the first chunk has been requested
-  int n_carry = 0;
-  if constexpr (FUSE) {
-    auto last_unit = [&](const Pos& p) { return uniform(prefix[p.s]) + (p.kvh + 1) * p.nch - 1; };
-    auto next_pair = [&](Pos& p) {  // false past the last sequence
-      if (++p.kvh < sc.Hkv) return true;
-      p.kvh = 0;
-      do {
-        ++p.s;
-      } while (p.s < sc.S && prefix[p.s + 1] == prefix[p.s]);
-      if (p.s >= sc.S) return false;
-      p.s = uniform(p.s);
-      p.nch = uniform((prefix[p.s + 1] - prefix[p.s]) / sc.Hkv);
-      p.ctx = clamp_ctx(p.s);
-      return true;
-    };
-    const Pos p0 = locate(u_begin);
-    int n_ends = 0;  // pairs ending in the share, counted up to 3
-    for (Pos t = p0; n_ends < 3 && last_unit(t) < u_end;) {
-      ++n_ends;
-      if (!next_pair(t)) break;
-    }
-    const bool early = n_ends > 0 && last_unit(p0) < u_begin + 3;
-    if (SMALLB || early || n_ends > 2) {
-      // every row stored now, before any chunk is requested; a store into one of
-      // the first chunks is waited for
-      for (Pos t = p0; last_unit(t) < u_end;) {
-        NewRow<C> r;
-        r.load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
-        r.store(sc, lane);
-        if (!next_pair(t)) break;
-      }
-      if (early) __builtin_amdgcn_s_waitcnt(0);
-    } else if (n_ends > 0) {
-      // the rows are requested now and stored once the first chunk is requested
-      Pos t = p0;
-      carry[0].load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
-      n_carry = 1;
-      if (n_ends > 1 && next_pair(t)) {
-        carry[1].load(sc, trow_of(t), t.ctx - 1, t.s, t.kvh, lane);
-        n_carry = 2;
+  // FUSE: append the newest token of the pair whose last chunk is at p (the row
+  // w was requested with that chunk) and, when that token is visible, patch it
+  // into the chunk's registers
+  auto append_at = [&](const Pos& p, const u32x4& w, Chunk<C>& ch, int base) {
+    if constexpr (FUSE) {
+      u32x4* row = new_lds[wave];
+      if (lane < 2 * C::NC) row[lane] = w;
+      wave_lds_sync();
+      const int raw = max(context_lens[p.s], 0);
+      new_row_store<C>(sc, k_pool, v_pool, trow_of(p), row, raw - 1, p.s, p.kvh, lane);
+      if (raw == p.ctx) {
+        patch_k<C>(ch.k, row, p.ctx - 1 - base, n, g);
+        patch_v<C>(ch.v, row, p.ctx - 1 - base, n, g);
       }
     }
-  }
+  };
 
   State<C> st;
   state_init(st);
@@ -1129,10 +1183,10 @@ paged_decode_balanced_kernel(
   int piece_j0 = pc.j, piece_u0 = pc.u;
 
   // Shared pairs whose piece this worker has published but not yet counted: at
-  // most the first and the last piece of the share.  A piece is counted only
-  // after its stores have completed; the wait for that comes at the end of the
-  // share, where no prefetched chunk is in flight (the vector-memory counter
-  // covers loads and stores alike, so an earlier wait would drain the pipeline).
+  // most the first and the last piece of the share.  The count (a release of the
+  // piece's stores) comes at the end of the share, where no prefetched chunk is in
+  // flight: a release waits for all of the wave's outstanding memory operations,
+  // loads included, so an earlier count would drain the pipeline.
   int pend_s0 = 0, pend_k0 = 0, pend_n0 = 0, pend_s1 = 0, pend_k1 = 0, pend_n1 = 0;
   int n_pend = 0;
   auto claim = [&](int ps, int pk, int pn) {
@@ -1143,13 +1197,16 @@ paged_decode_balanced_kernel(
     const int wa = worker_of(seg_first, U, NWe);
     const int wb = worker_of(seg_first + pn - 1, U, NWe);
     int last = 0;
+    wave_sync();  // every lane's stores of the piece come before lane 0's release
     if (lane == 0)
       last = claim_last(counters + (size_t)ps * sc.Hkv + pk, sc.epoch, (uint32_t)(wb - wa + 1));
     last = uniform(last);  // lane 0's answer
-    if (last) merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
+    if (last) {
+      wave_sync();  // lane 0's acquire comes before every lane's reads of the pieces
+      merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
+    }
   };
   auto claim_pending = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);  // every store of the pieces has completed
     if (n_pend > 0) claim(pend_s0, pend_k0, pend_n0);
     if (n_pend > 1) claim(pend_s1, pend_k1, pend_n1);
     n_pend = 0;
@@ -1215,6 +1272,8 @@ paged_decode_balanced_kernel(
       const int base = pc.st + 64 * pc.j;
       load_small<C>(ch, ks, vs, k_pool, v_pool, k_scale, v_scale, trow_of(pc), base, pc.ctx,
                     pc.kvh, sc, n, g, pc.lo);
+      if constexpr (FUSE)
+        if (pc.j == pc.nch - 1) append_at(pc, new_row_load<C>(sc, pc.s, pc.kvh, lane), ch, base);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
       chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, pc.ctx - base),
@@ -1248,8 +1307,11 @@ paged_decode_balanced_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) ksr[k][i] = vsr[k][i] = 1.0f;
     pp[0] = pc;
+    u32x4 nwr[NB];  // FUSE: the new row of the pair whose last chunk is in buffer k
     auto issue = [&](Chunk<C>& dst, const Pos& p, const Pages& pg, float (&ks)[16],
-                     float (&vs)[16]) {
+                     float (&vs)[16], u32x4& nw) {
+      if constexpr (FUSE)
+        if (p.j == p.nch - 1) nw = new_row_load<C>(sc, p.s, p.kvh, lane);
       issue_k<C>(dst.k, k_pool, pg, p.kvh, sc, n, g);
       issue_v<C>(dst.v, v_pool, pg, p.kvh, sc, n, g);
       if constexpr (kFp8) chunk_scales(ks, vs, k_scale, v_scale, pg, p.kvh, sc, g);
@@ -1260,11 +1322,7 @@ paged_decode_balanced_kernel(
 #pragma unroll
     for (int k = 0; k + 1 < NB; ++k) {
       if (k > 0) pp[k] = advance(pp[k - 1]);
-      issue(R[k], pp[k], pages_at(pp[k]), ksr[k], vsr[k]);
-    }
-    if constexpr (FUSE) {
-      if (n_carry > 0) carry[0].store(sc, lane);
-      if (n_carry > 1) carry[1].store(sc, lane);
+      issue(R[k], pp[k], pages_at(pp[k]), ksr[k], vsr[k], nwr[k]);
     }
     pp[NB - 1] = advance(pp[NB - 2]);
     Pages en = pages_at(pp[NB - 1]);
@@ -1282,18 +1340,20 @@ paged_decode_balanced_kernel(
       Pages en2 = en;
       Pos pnext = pp[NB - 1];
       if (fetch) {
-        issue(fill, pp[NB - 1], en, ksr[f], vsr[f]);
+        issue(fill, pp[NB - 1], en, ksr[f], vsr[f], nwr[f]);
         pnext = advance(pp[NB - 1]);
         en2 = pages_at(pnext);
       }
       issue_point();
+      const int base0 = p0.st + 64 * p0.j;
+      if constexpr (FUSE)
+        if (p0.j == p0.nch - 1) append_at(p0, nwr[c], cur, base0);
       f32x4 S[4];
       chunk_qk<C, KVT, CT>(S, cur.k, qop);
       issue_point();
       const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
       if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
       issue_point();
-      const int base0 = p0.st + 64 * p0.j;
       chunk_softmax_pv<C, KVT, CT>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
                                    min(64, p0.ctx - base0), g, 64, p0.lo - base0);
       issue_point();
@@ -1330,14 +1390,16 @@ paged_decode_balanced_kernel(
 
 // =================================================================================
 // Split-KV reduce for fixed partitions: one workgroup per (query head, sequence).
-// Without context_lens every one of the max_parts slots is merged (empty ones,
-// with exp-sum 0, weigh nothing).
+// A sequence's partitions are those of its context clamped to ctx_cap (the clamp
+// the decode applied; the decode writes no partition past it).  Without
+// context_lens every one of the max_parts slots is merged (empty ones, with
+// exp-sum 0, weigh nothing).
 // =================================================================================
 template <int D>
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_max,
     const float* __restrict__ part_sum, const int32_t* __restrict__ context_lens,
-    uint8_t* __restrict__ out, int out_dtype, int Hq, int part_size, int max_parts) {
+    uint8_t* __restrict__ out, int out_dtype, int Hq, int part_size, int max_parts, int ctx_cap) {
   extern __shared__ float w_lds[];  // [max_parts] merge weights
   __shared__ float red[kWaves];
   __shared__ float o_lds[kWaves][D];
@@ -1345,7 +1407,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int np = max_parts;
   if (context_lens) {
-    const long long cap = (long long)max_parts * part_size;
+    const long long cap = min((long long)max_parts * part_size, (long long)ctx_cap);
     long long ctx = context_lens[s];
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     np = (int)((ctx + part_size - 1) / part_size);
@@ -1687,8 +1749,6 @@ DecodeScalars scalars_of(const DecodeLaunch& p) {
   sc.k_new = static_cast<const uint8_t*>(p.k_new);
   sc.v_new = static_cast<const uint8_t*>(p.v_new);
   sc.slot_out = p.slot_out;
-  sc.k_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.k_pool));
-  sc.v_pool_w = static_cast<uint8_t*>(const_cast<void*>(p.v_pool));
   sc.lpt = !p.balanced && !p.prefix && p.num_seqs <= kThreads;
   return sc;
 }
@@ -1783,11 +1843,11 @@ int launch_split_reduce(const ReduceLaunch& p, hipStream_t st) {
   if (p.head_dim == 64)
     hipLaunchKernelGGL(split_reduce_kernel<64>, grid, dim3(kThreads), lds, st, p.part_out,
                        p.part_max, p.part_sum, p.context_lens, (uint8_t*)p.out, p.out_dtype,
-                       p.num_q_heads, p.part_size, p.max_parts);
+                       p.num_q_heads, p.part_size, p.max_parts, p.ctx_cap);
   else if (p.head_dim == 128)
     hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(kThreads), lds, st, p.part_out,
                        p.part_max, p.part_sum, p.context_lens, (uint8_t*)p.out, p.out_dtype,
-                       p.num_q_heads, p.part_size, p.max_parts);
+                       p.num_q_heads, p.part_size, p.max_parts, p.ctx_cap);
   else
     return -3;
   return hipGetLastError() == hipSuccess ? 0 : -5;

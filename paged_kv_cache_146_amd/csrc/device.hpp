@@ -179,11 +179,14 @@ __device__ __forceinline__ void issue_point() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// order this wave's LDS writes before its later LDS reads (wave-local exchange)
-__device__ __forceinline__ void wave_lds_sync() {
+// Synchronise the lanes of this wave: every lane's memory operations before the
+// call happen before every lane's operations after it (a wave-local exchange
+// through LDS, or one lane's release / acquire on behalf of the wave).
+__device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+__device__ __forceinline__ void wave_lds_sync() { wave_sync(); }
 
 }  // namespace pkv

@@ -70,6 +70,7 @@ struct ReduceLaunch {
   void* out;
   int out_dtype;
   int num_seqs, num_q_heads, head_dim, part_size, max_parts;
+  int ctx_cap;  // contexts are clamped to this many tokens (the decode's clamp)
 };
 int launch_split_reduce(const ReduceLaunch& p, hipStream_t stream);
 

@@ -8,7 +8,7 @@ import math
 import numpy as np
 
 import oracle
-from paged_kv_cache_146_amd.workloads import STORAGE, Workload
+from workloads import STORAGE, Workload
 
 ATOL, RTOL = 2e-3, 1e-2  # |gpu - oracle| <= ATOL + RTOL * |oracle|, element-wise
 ES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
@@ -101,19 +101,21 @@ class GpuCase:
         out.view(torch.uint8).fill_(0xFF)
         return out
 
-    def decode(self, partition_size=None, out=None, workspace=None, window=None):
+    def decode(self, partition_size=None, out=None, workspace=None, window=None, q=None):
+        """q: another query tensor of the same shape (default: the workload's)."""
         import paged_kv_cache_146_amd as pkv
         P = self.wl.partition_size if partition_size is None else partition_size
+        q = self.q if q is None else q
         if out is None:
             out = self.nan_out()
         if window is not None:
             return pkv.pkv_paged_attention_decode_window(
-                self.q, self.desc, self.k_pool, self.v_pool, self.block_table,
+                q, self.desc, self.k_pool, self.v_pool, self.block_table,
                 self.context_lens, self.wl.max_context_len, self.wl.scale, window,
                 partition_size=P, k_scale=self.k_scale, v_scale=self.v_scale, out=out,
                 q_dtype=self.wl.q_dtype, workspace=workspace)
         return pkv.pkv_paged_attention_decode(
-            self.q, self.desc, self.k_pool, self.v_pool, self.block_table, self.context_lens,
+            q, self.desc, self.k_pool, self.v_pool, self.block_table, self.context_lens,
             self.wl.max_context_len, self.wl.scale, partition_size=P, k_scale=self.k_scale,
             v_scale=self.v_scale, out=out, q_dtype=self.wl.q_dtype, workspace=workspace)
 
@@ -174,5 +176,58 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
+def _f32_of(bits, dtype):
+    from workloads import storage_to_f32
+    return storage_to_f32(bits, dtype) if dtype != "f32" else np.asarray(bits, np.float32)
+
+
+def peaked(wl: Workload, factor: float) -> Workload:
+    """The workload with every query scaled by a power of two (exact in every query
+    type): the softmax sharpens, |out| grows towards single value rows, and the
+    relative term of the tolerance, not the absolute one, decides."""
+    from workloads import to_storage
+    w = Workload(**{**wl.__dict__})
+    w.q = to_storage(_f32_of(wl.q, wl.q_dtype) * np.float32(factor), wl.q_dtype)
+    w.name = "%s, q x %g" % (wl.name, factor)
+    return w
+
+
+def plant_keys(wl: Workload, where: str = "edges") -> tuple:
+    """The workload with one planted key per sequence (of 16-bit pools): at a block
+    edge about three quarters into the context, a K row along the sum of the G queries
+    of its kv head, scaled so that its score sits near log(ctx) above the others' (it
+    then carries roughly half of the softmax weight, a different share per head),
+    and a V row that no other key resembles (4 + d / 64 in dim d).  A kernel that
+    skips that key, reads it from the wrong slot, or pairs it with the wrong V row
+    moves the output by O(1).  Returns (workload, planted positions)."""
+    from workloads import to_storage
+    assert wl.kv_dtype in ("f16", "bf16") and wl.src_dtype == wl.kv_dtype
+    w = Workload(**{**wl.__dict__})
+    w.k_src, w.v_src = wl.k_src.copy(), wl.v_src.copy()
+    B, G, D = wl.block_size, wl.group, wl.head_dim
+    q = _f32_of(wl.q, wl.q_dtype).reshape(wl.num_seqs, wl.num_kv_heads, G, D)
+    index = {(int(s), int(p)): i for i, (s, p) in enumerate(zip(wl.fill_seq, wl.fill_pos))}
+    pos = np.full(wl.num_seqs, -1, np.int64)
+    for s in range(wl.num_seqs):
+        c = int(wl.context_lens[s])
+        if c < 2:
+            continue
+        t = max(1, (3 * c // 4) // B * B)          # first key of a block
+        t = t - 1 if s % 2 == 0 else min(t, c - 1)  # or the last key of the one before
+        i = index.get((s, t))
+        if i is None:  # a shared-prefix token is stored once, under sequence 0
+            continue
+        qs = q[s].sum(axis=1)                                 # [Hkv][D]
+        dots = np.einsum("hgd,hd->h", q[s], qs) / G           # mean score direction
+        alpha = (np.log(c) + 0.5) / (wl.scale * np.maximum(dots, 1.0))
+        k = alpha[:, None] * qs
+        v = np.broadcast_to(4.0 + np.arange(D, dtype=np.float32) / 64.0, (wl.num_kv_heads, D))
+        w.k_src[i] = to_storage(k.astype(np.float32), wl.kv_dtype)
+        w.v_src[i] = to_storage(np.ascontiguousarray(v, np.float32), wl.kv_dtype)
+        pos[s] = t
+    w.name = wl.name + ", planted keys"
+    return w, pos
+
+
 __all__ = ["GpuCase", "oracle_pool", "assert_close", "torch_bits", "bits_of", "to_f64",
-           "logical_k", "logical_v", "ceil_div", "math"]
+           "logical_k", "logical_v", "ceil_div", "math", "peaked", "plant_keys"]

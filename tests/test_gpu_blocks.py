@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from helpers import assert_close, to_f64, torch_bits
-from paged_kv_cache_146_amd.workloads import to_storage
+from workloads import to_storage
 
 pytestmark = pytest.mark.gpu
 

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from helpers import assert_close, logical_k, logical_v, oracle_pool, to_f64, torch_bits
-from paged_kv_cache_146_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 L = 3

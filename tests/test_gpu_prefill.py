@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import GpuCase, assert_close, oracle_pool, to_f64
-from paged_kv_cache_146_amd import workloads as W
+from helpers import GpuCase, assert_close, oracle_pool, peaked, to_f64
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -67,10 +67,14 @@ def test_prefill_rows_past_the_context_are_zero():
     print(_run(wl, causal=True))
 
 
-def test_fp8_prefill_full_sampled():
+@pytest.mark.parametrize("factor", [1, 4, 8])
+def test_fp8_prefill_full_sampled(factor):
     # the full chunked-prefill workload in its bench launch configuration; rows sampled
-    # at the chunk edges (first, last) and inside, for every sequence
+    # at the chunk edges (first, last) and inside, for every sequence; q x 4 and x 8
+    # (exact) sharpen the softmax so that the relative tolerance decides
     wl = W.fp8_chunked_prefill()
+    if factor != 1:
+        wl = peaked(wl, factor)
     cu = wl.cu_seqlens_q
     rng = np.random.default_rng(7)
     rows = []

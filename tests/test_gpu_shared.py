@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from helpers import GpuCase, assert_close, oracle_pool, to_f64
-from paged_kv_cache_146_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -124,3 +124,25 @@ def test_shared_argument_errors():
     with pytest.raises(pkv.PagedKVError) as e:
         _shared(case, 32, workspace=small)
     assert e.value.status == -4
+
+
+def test_shared_prefix_config_full():
+    """The full shared-prefix configuration (256 sequences sharing a 2048-token prefix,
+    private tails U[0, 512], MHA fp16, B 32) in bench.py's launch: the shared decode
+    against the oracle's plain decode on sampled sequences (the longest and shortest
+    tails among them), pool written bit for bit."""
+    wl = W.shared_prefix_decode()
+    case = GpuCase(wl)
+    opool = oracle_pool(wl)
+    gk, gv = case.logical_pools()
+    assert np.array_equal(gk.view(np.uint8), opool.k.view(np.uint8)), "K pool differs"
+    assert np.array_equal(gv.view(np.uint8), opool.v.view(np.uint8)), "V pool differs"
+    seqs = np.array(sorted({0, 1, 100, 255, int(np.argmin(wl.context_lens)),
+                            int(np.argmax(wl.context_lens))}), np.int32)
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens,
+                              wl.scale, seqs=seqs)
+    shared_len = wl.shared_blocks * wl.block_size
+    assert shared_len == 2048
+    for call in range(2):  # the same workspace twice
+        out = to_f64(_shared(case, shared_len), wl.q_dtype)[seqs]
+        print(assert_close(out, ref, "%s shared decode, call %d" % (wl.name, call)))

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from helpers import GpuCase, assert_close, oracle_pool, to_f64
-from paged_kv_cache_146_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 

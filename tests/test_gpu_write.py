@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from helpers import logical_k, logical_v, torch_bits
-from paged_kv_cache_146_amd.workloads import to_storage
+from workloads import to_storage
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -23,7 +23,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from paged_kv_cache_146_amd.workloads import NAN_BITS, to_storage
+from workloads import NAN_BITS, to_storage
 
 
 def _values(bits, dtype, scale=None):

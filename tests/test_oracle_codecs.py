@@ -120,3 +120,28 @@ def test_int8_encode_vs_numpy():
     assert oracle.int8_encode(np.array([np.nan], np.float32))[0] == 0
     assert list(oracle.int8_encode(np.array([0.5, 1.5, 2.5, -0.5, -2.5], np.float32))) == \
         [0, 2, 2, 0, -2]
+
+
+def test_int8_encode_by_integer_arithmetic():
+    """Every quarter step in [-140, 140] (exact in fp32): the nearest integer with
+    ties to even, clamped to [-127, 127], computed with integers only (floor division
+    and the remainder of 4 k by 4), so the pin shares no rounding routine with the
+    encoder ([P1] §8.1: int8 codes with an fp32 scale; symmetric, no zero point)."""
+    ks = np.arange(-560, 561, dtype=np.int64)          # x = k / 4
+    x = (ks / 4).astype(np.float32)
+    want = []
+    for k in ks.tolist():
+        q, r = divmod(k, 4)                             # k = 4 q + r, 0 <= r < 4
+        if r > 2 or (r == 2 and q % 2 == 1):
+            q += 1
+        want.append(max(-127, min(127, q)))
+    assert np.array_equal(oracle.int8_encode(x).astype(np.int64), np.array(want))
+
+
+def test_int8_encode_vs_python_round():
+    """Python's round() on a float is exact and breaks ties to even: an independent
+    routine for random values across the clamp."""
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(20000) * 80).astype(np.float32)
+    want = [max(-127, min(127, round(float(v)))) for v in x]
+    assert np.array_equal(oracle.int8_encode(x).astype(np.int64), np.array(want))
