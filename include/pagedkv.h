@@ -31,9 +31,11 @@
  *     each call) so that a bad entry can corrupt results but never memory
  *     outside the caller's buffers.
  *   - All entry points are thread-safe.  The only process-wide state is a
- *     per-device cache of device properties and an atomic call counter that
- *     tags balanced-mode calls.  The block allocator (pkv_alloc_*) is host
- *     bookkeeping with one lock per allocator.
+ *     per-device cache of device properties, an atomic call counter that tags
+ *     balanced-mode calls, and the scratch array of
+ *     pkv_paged_attention_decode_noalloc (one per device) with its resolved
+ *     addresses.  The block allocator (pkv_alloc_*) is host bookkeeping with one
+ *     lock per allocator.
  *
  * Physical pool layout (owned by this library; one pool for K, one for V, per
  * layer).  With E = bytes per element and X = 16 / E elements per 16 bytes:
@@ -375,6 +377,33 @@ int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t nu
                                       const int32_t* context_lens, int32_t max_context_len,
                                       int32_t shared_len, float scale, void* workspace,
                                       size_t workspace_bytes, void* out, void* stream);
+
+/* Bytes of the device array behind pkv_paged_attention_decode_noalloc (one per
+ * device, held until the process ends). */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): pkv_paged_attention_decode
+ * without the workspace argument.  The split-KV scratch is a device array owned by
+ * the library, PKV_NOALLOC_SCRATCH_BYTES bytes on each device the call runs on;
+ * its address is resolved on the first call made with that device current
+ * (a caller that captures makes one call before capturing).  No call allocates or
+ * frees anything.  Every argument and partition mode as in
+ * pkv_paged_attention_decode: 0 uses no scratch; fixed partitions need
+ * pkv_decode_workspace_bytes(...) bytes, and a call that needs more than the array
+ * returns PKV_EWORKSPACE before touching the device; the balanced mode runs as
+ * many wavefront workers as the array holds.  All calls on one device share the
+ * array, which keeps the last call's contents (no call needs it cleared): calls
+ * that overlap in time on one device race, so issue them on one stream or order
+ * their streams.  Errors as pkv_paged_attention_decode, plus PKV_EWORKSPACE. */
+int pkv_paged_attention_decode_noalloc(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                       int32_t num_q_heads, const pkv_pool_desc* pool,
+                                       const void* k_pool, const void* v_pool,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       float scale, int32_t partition_size, void* out,
+                                       void* stream);
 
 /* [P1 §4] Log-sum-exp merge of split-KV partitions.  For sequence s, head h,
  * partitions i < min(ceil(ctx_s / partition_size), max_partitions) with state

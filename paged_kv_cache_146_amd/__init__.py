@@ -42,7 +42,7 @@ EXPORTS = ["pkv_strerror", "pkv_version", "pkv_pool_bytes", "pkv_physical_slot",
            "pkv_alloc_block_table", "pkv_alloc_refcount", "pkv_alloc_free_blocks",
            "pkv_copy_blocks", "pkv_decode_shared_workspace_bytes",
            "pkv_paged_attention_decode_shared", "pkv_paged_attention_decode_window",
-           "pkv_decode_append"]
+           "pkv_decode_append", "pkv_paged_attention_decode_noalloc"]
 
 
 class PagedKVError(RuntimeError):
@@ -122,6 +122,9 @@ def lib():
                     "pkv_alloc_refcount": (ctypes.c_int, [P, I32, P]),
                     "pkv_alloc_free_blocks": (ctypes.c_int, [P, P, I32, P]),
                     "pkv_copy_blocks": (ctypes.c_int, [P, I32, P, P, P, P, P, P]),
+                    "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [P, I32, I32, I32, P, P,
+                                                                          P, P, P, P, I32, P,
+                                                                          I32, F, I32, P, P]),
                 }
                 for name, (res, args) in sigs.items():
                     fn = getattr(L, name)
@@ -421,6 +424,28 @@ def pkv_paged_attention_decode(q, desc: PoolDesc, k_pool, v_pool, block_table, c
         int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
         float(scale), int(partition_size), _ptr(workspace, "workspace", allow_none=True),
         ws_bytes, _ptr(out, "out"), _stream(stream)), "pkv_paged_attention_decode")
+    return out
+
+
+def pkv_paged_attention_decode_noalloc(q, desc: PoolDesc, k_pool, v_pool, block_table,
+                                       context_lens, max_context_len: int, scale: float,
+                                       partition_size: int = 0, k_scale=None, v_scale=None,
+                                       out=None, q_dtype=None, stream=None):
+    """pkv_paged_attention_decode with its split-KV scratch in the library's own device
+    array (no workspace argument, nothing allocated by the call); `out` must be given
+    by callers that cannot allocate."""
+    torch = _torch()
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    qd = dtype_code(q_dtype if q_dtype is not None else q.dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        _ptr(q, "q"), qd, S, Hq, ctypes.byref(desc), _ptr(k_pool, "k_pool"),
+        _ptr(v_pool, "v_pool"), _ptr(k_scale, "k_scale", allow_none=True),
+        _ptr(v_scale, "v_scale", allow_none=True), _ptr(block_table, "block_table"),
+        int(block_table.shape[1]), _ptr(context_lens, "context_lens"), int(max_context_len),
+        float(scale), int(partition_size), _ptr(out, "out"), _stream(stream)),
+        "pkv_paged_attention_decode_noalloc")
     return out
 
 

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.cpp", "allocator.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "allocator.cpp", "cache_write.hip", "decode.hip", "prefill.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
