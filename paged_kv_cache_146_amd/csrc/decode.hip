@@ -237,7 +237,11 @@ __device__ __forceinline__ Pages pages_of(const int32_t* __restrict__ trow, int 
   return pg;
 }
 
-template <class C>
+// The decode reads each K/V byte once per step, so its page loads carry the
+// non-temporal hint (STREAM = true): the lines stream through the caches instead
+// of being kept there.  The shared-prefix kernel, whose column tiles re-read the
+// prefix from their XCD's L2, loads with the default policy.
+template <class C, bool STREAM = true>
 __device__ __forceinline__ void issue_k(u32x4 (&kr)[C::NK], const uint8_t* __restrict__ k_pool,
                                         const Pages& pg, int kvh, const DecodeScalars& sc, int n,
                                         int g) {
@@ -248,11 +252,16 @@ __device__ __forceinline__ void issue_k(u32x4 (&kr)[C::NK], const uint8_t* __res
     const u32x4* kp = reinterpret_cast<const u32x4*>(k_pool) + page +
                       ((pg.off + 16 * T) & (B - 1)) + n + (size_t)g * B;
 #pragma unroll
-    for (int pq = 0; pq < C::NPL; ++pq) kr[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
+    for (int pq = 0; pq < C::NPL; ++pq) {
+      if constexpr (STREAM)
+        kr[T * C::NPL + pq] = __builtin_nontemporal_load(&kp[(size_t)pq * 4 * B]);
+      else
+        kr[T * C::NPL + pq] = kp[(size_t)pq * 4 * B];
+    }
   }
 }
 
-template <class C>
+template <class C, bool STREAM = true>
 __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
                                         const uint8_t* __restrict__ v_pool, const Pages& pg,
                                         int kvh, const DecodeScalars& sc, int n, int g) {
@@ -266,8 +275,13 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
                         ((size_t)kvh * C::Dim * B + ((size_t)(t / C::E) * C::Dim + n) * C::E +
                          (t % C::E)) * C::EB;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)  // 16 dims on
-      vr[dt * 4 + T] = *reinterpret_cast<const VP*>(vp + (size_t)16 * dt * C::E * C::EB);
+    for (int dt = 0; dt < C::NDT; ++dt) {  // 16 dims on
+      const VP* a = reinterpret_cast<const VP*>(vp + (size_t)16 * dt * C::E * C::EB);
+      if constexpr (STREAM)
+        vr[dt * 4 + T] = __builtin_nontemporal_load(a);
+      else
+        vr[dt * 4 + T] = *a;
+    }
   }
 }
 
@@ -750,28 +764,28 @@ paged_decode_kernel(
   const int cnt = nch > wave ? (nch - wave + kWaves - 1) / kWaves : 0;  // chunks wave, wave+4, ...
   auto base_of = [&](int i) { return t_begin + 64 * (wave + kWaves * min(i, cnt - 1)); };
   // FUSE: the wave that reads the last chunk requests the new row first (its first
-  // chunk's loads go out behind it), parks it in LDS, stores it into the pool and,
-  // when the newest token is visible (the context was not clamped), patches it into
-  // its last chunk; r_new is that token's key index in the chunk.
+  // chunk's loads go out behind it), parks it in LDS, patches it into its last chunk
+  // when the newest token is visible (the context was not clamped; r_new is that
+  // token's key index in the chunk), and stores it into the pool after its chunk
+  // loop (stores issued while the launch streams cost more than stores at its end).
   const bool fuse_wave = FUSE && t_end == ctx && wave == (nch - 1) % kWaves;
   const bool patch = fuse_wave && ctx == ctx_raw;
   const int r_new = ctx - 1 - base_of(cnt - 1);
   u32x4 new_w;
   if constexpr (FUSE)
     if (fuse_wave) new_w = new_row_load<C>(sc, s, kvh, lane);
-  auto park_and_store = [&]() {
+  auto park_new_row = [&]() {
     if constexpr (FUSE) {
       if (fuse_wave) {
         issue_point();  // behind the first chunk's requests
         if (lane < 2 * C::NC) new_lds[lane] = new_w;
         wave_lds_sync();
-        new_row_store<C>(sc, k_pool, v_pool, trow, new_lds, ctx_raw - 1, s, kvh, lane);
       }
     }
   };
 
   if constexpr (SMALLB) {
-    park_and_store();
+    park_new_row();
     for (int i = 0; i < cnt; ++i) {
       const int base = base_of(i);
       Chunk<C> ch;
@@ -804,7 +818,7 @@ paged_decode_kernel(
       if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
       issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
     }
-    park_and_store();
+    park_new_row();
     Pages p1 = pages_of(trow, base_of(1), t_end, sc);
     for (int i = 0; i < cnt; ++i) {
       const int b0 = base_of(i);
@@ -840,6 +854,9 @@ paged_decode_kernel(
       }
     }
   }
+
+  if constexpr (FUSE)
+    if (fuse_wave) new_row_store<C>(sc, k_pool, v_pool, trow, new_lds, ctx_raw - 1, s, kvh, lane);
 
   // ---- merge the four waves' states in LDS ------------------------------------------
   const float lw = sum_groups(st.l);
@@ -950,10 +967,11 @@ __device__ __forceinline__ int worker_of(int u, int U, int NWe) {
 // finisher leaves (epoch, 0) behind, so no zero-fill is ever needed and replays
 // of the same call stay correct.  Lock-free: a failed exchange means another
 // worker made progress; nothing waits on anyone.
-// Memory order: each successful exchange releases (agent scope) the worker's
-// stores of its piece; the exchanges on one counter form a release sequence, so
-// the winner's acquire fence, after its own exchange read the last of them, makes
-// every piece of the pair visible to its merge.
+// Memory order: the pieces and the counter are touched only by agent-scope atomic
+// operations, ordered by a wait on the wave's outstanding stores before the
+// exchange and by the exchange's returned value before the merge's loads (the
+// caller, the claim in paged_decode_balanced_kernel, explains why no release /
+// acquire pair is used).
 __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch, uint32_t npieces) {
   unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   while (true) {
@@ -962,11 +980,9 @@ __device__ __forceinline__ int claim_last(unsigned long long* c, uint32_t epoch,
     const bool last = n2 >= npieces;
     const unsigned long long nw = ((unsigned long long)epoch << 32) | (last ? 0u : n2);
     unsigned long long expected = old;
-    if (__hip_atomic_compare_exchange_strong(c, &expected, nw, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)) {
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (__hip_atomic_compare_exchange_strong(c, &expected, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
       return last ? 1 : 0;
-    }
     old = expected;
   }
 }
@@ -1196,15 +1212,23 @@ paged_decode_balanced_kernel(
     const int seg_first = uniform(prefix[ps]) + pk * pn;
     const int wa = worker_of(seg_first, U, NWe);
     const int wb = worker_of(seg_first + pn - 1, U, NWe);
+    // Publish, then claim.  The partial states were stored with agent-scope atomic
+    // stores (coherent across the XCDs' L2 caches); the wait below holds the claim
+    // until every store of the wave has completed at that scope, and the compiler
+    // barriers keep the compiler from moving memory operations across the claim.
+    // The winner's merge loads are agent-scope atomic loads issued only after the
+    // exchange has returned.  (A release exchange plus an acquire fence would say
+    // the same in the language's memory model, but on this chip they add a
+    // write-back of the whole L2 before every claim and an invalidation of it in
+    // every merge; measured, that slows the balanced decode by 40-50%.)
     int last = 0;
-    wave_sync();  // every lane's stores of the piece come before lane 0's release
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
     if (lane == 0)
       last = claim_last(counters + (size_t)ps * sc.Hkv + pk, sc.epoch, (uint32_t)(wb - wa + 1));
     last = uniform(last);  // lane 0's answer
-    if (last) {
-      wave_sync();  // lane 0's acquire comes before every lane's reads of the pieces
-      merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
-    }
+    asm volatile("" ::: "memory");
+    if (last) merge_pair<CT, D>(slot_out, slot_ml, out, sc, ps, pk, seg_first, wa, wb, U, NWe, n, g);
   };
   auto claim_pending = [&]() {
     if (n_pend > 0) claim(pend_s0, pend_k0, pend_n0);
@@ -1579,9 +1603,9 @@ __global__ __launch_bounds__(kThreads) void shared_prefix_kernel(
     for (int i = 0; i < 16; ++i) ks0[i] = vs0[i] = 1.0f;
     {
       const Pages p0 = pages_of(trow, base_of(0), t_end, sc);
-      issue_k<C>(R.k, k_pool, p0, kvh, sc, n, g);
+      issue_k<C, false>(R.k, k_pool, p0, kvh, sc, n, g);
       if constexpr (kFp8) chunk_scales(ks0, vs0, k_scale, v_scale, p0, kvh, sc, g);
-      issue_v<C>(R.v, v_pool, p0, kvh, sc, n, g);
+      issue_v<C, false>(R.v, v_pool, p0, kvh, sc, n, g);
     }
     Pages p1 = pages_of(trow, base_of(1), t_end, sc);
     for (int i = 0; i < cnt; ++i) {
@@ -1595,7 +1619,7 @@ __global__ __launch_bounds__(kThreads) void shared_prefix_kernel(
       for (int k = 0; k < 16; ++k) ks1[k] = vs1[k] = 1.0f;
       Pages p2 = p1;
       if (more) {
-        issue_k<C>(R.k, k_pool, p1, kvh, sc, n, g);
+        issue_k<C, false>(R.k, k_pool, p1, kvh, sc, n, g);
         if constexpr (kFp8) chunk_scales(ks1, vs1, k_scale, v_scale, p1, kvh, sc, g);
         p2 = pages_of(trow, base_of(i + 2), t_end, sc);
       }
@@ -1603,7 +1627,7 @@ __global__ __launch_bounds__(kThreads) void shared_prefix_kernel(
       chunk_softmax_pv<C, KVT, CT, true>(st, S, R.v, sc.scale_log2, ks0, vs0,
                                          min(64, t_end - b0), g, lim - b0);
       issue_point();
-      if (more) issue_v<C>(R.v, v_pool, p1, kvh, sc, n, g);
+      if (more) issue_v<C, false>(R.v, v_pool, p1, kvh, sc, n, g);
       issue_point();
       p1 = p2;
 #pragma unroll
