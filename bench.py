@@ -80,7 +80,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle leg")
-    ap.add_argument("--workload", choices=["decode", "long", "prefill", "copy", "shared-prefix"],
+    ap.add_argument("--workload", choices=["decode", "long", "tiny", "prefill", "copy",
+                                           "shared-prefix"],
                     default="decode")
     ap.add_argument("--kv", choices=["bf16", "fp8", "int8"], default="bf16",
                     help="decode workload: pool element type (quantised pools store the "
@@ -133,7 +134,7 @@ def decode_bytes(wl, window=0) -> int:
     """Algorithmic bytes of one decode launch: every K/V element of every sequence's
     visible keys once (the whole context, or its sliding window), q and out once, the
     used block-table entries and the lengths."""
-    e = 2  # bf16
+    e = W_ELEM[wl.q_dtype]  # q and out
     if window <= 0:
         nblk = sum(math.ceil(int(c) / wl.block_size) for c in wl.context_lens)
         return (wl.kv_bytes() + 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * e
@@ -154,7 +155,7 @@ def write_bytes(wl) -> int:
     """Slot mapping (seq, pos, table entry in; slot out) + scatter (bf16 K/V rows in, pool
     rows out, and for a quantised pool the K and V scale of every (token, kv head))."""
     S = wl.num_seqs
-    src_row = wl.num_kv_heads * wl.head_dim * 2
+    src_row = wl.num_kv_heads * wl.head_dim * W_ELEM[wl.src_dtype]
     pool_row = wl.num_kv_heads * wl.head_dim * W_ELEM[wl.kv_dtype]
     scales = 2 * wl.num_kv_heads * 4 if wl.kv_dtype in ("fp8", "int8") else 0
     return S * (4 + 4 + 4 + 8) + S * (8 + 2 * src_row + 2 * pool_row + scales)
@@ -186,13 +187,17 @@ def main():
         wl = W.long_context_decode(seed=3)
         wl_text = ("long-context paged decode: 8 seqs, ctx U[32768,131072] (seed 3), H_q 64, "
                    "H_kv 8, D 128, B 16, bf16 (one new token per sequence)")
+    elif a.workload == "tiny":  # the two-sequence fp32 case: launch latency, not bytes
+        wl = W.tiny_decode(seed=1)
+        wl_text = ("tiny paged decode: 2 seqs, ctx {5, 11}, H_q 4, H_kv 2, D 64, B 4, fp32, "
+                   "8 physical blocks (one new token per sequence)")
     else:
         wl = W.llama3_8b_decode(seed=2, kv_dtype=a.kv, scale_mode=a.scale_mode)
         wl_text = "llama3-8b-shaped paged decode layer (one new token per sequence)"
     P = default_partition(pkv, wl) if a.partition is None else a.partition
     # the append inside the decode's launch where the fused kernel exists (bf16 pool,
     # whole contexts); the append + decode pair otherwise
-    a.fused = not a.separate and a.kv == "bf16" and not a.window
+    a.fused = not a.separate and wl.kv_dtype in ("f16", "bf16") and not a.window
     dev = "cuda"
     if a.kv_block_major:  # [block][K pages | V pages]: a block's K and V in one run
         dense = pkv.pool_desc(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim,
@@ -211,8 +216,13 @@ def main():
     bt = torch.from_numpy(wl.block_table).to(dev)
     cl = torch.from_numpy(wl.context_lens).to(dev)
 
-    def bits(x):
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    def bits(x, dt=None):
+        dt = dt or wl.src_dtype
+        a_ = np.ascontiguousarray(x)
+        if dt == "f32":
+            return torch.from_numpy(a_.view(np.float32)).to(dev)
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        return torch.from_numpy(a_.view(np.int16)).view(tdt).to(dev)
 
     # fill the pool through the library's write path (not timed)
     slab = 1 << 17
@@ -222,8 +232,8 @@ def main():
         sl = pkv.pkv_slot_mapping(bt, torch.from_numpy(wl.fill_seq[o:e]).to(dev),
                                   torch.from_numpy(wl.fill_pos[o:e]).to(dev), wl.block_size)
         pkv.pkv_kv_cache_write(sl, bits(wl.k_src[o:e]), bits(wl.v_src[o:e]), desc, k_pool, v_pool,
-                               ks, vs, src_dtype="bf16")
-    q = bits(wl.q)
+                               ks, vs, src_dtype=wl.src_dtype)
+    q = bits(wl.q, wl.q_dtype)
     rows = wl.decode_new_token_rows()
     k_new, v_new = bits(wl.k_src[rows]), bits(wl.v_src[rows])
     seq_idx = torch.arange(wl.num_seqs, dtype=torch.int32, device=dev)
@@ -242,11 +252,12 @@ def main():
         if a.window > 0:
             pkv.pkv_paged_attention_decode_window(
                 q, desc, k_pool, v_pool, bt, cl, wl.max_context_len, wl.scale, a.window,
-                partition_size=P, k_scale=ks, v_scale=vs, workspace=ws, out=out, q_dtype="bf16")
+                partition_size=P, k_scale=ks, v_scale=vs, workspace=ws, out=out,
+                q_dtype=wl.q_dtype)
         else:
             pkv.pkv_paged_attention_decode(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len,
                                            wl.scale, partition_size=P, k_scale=ks, v_scale=vs,
-                                           workspace=ws, out=out, q_dtype="bf16")
+                                           workspace=ws, out=out, q_dtype=wl.q_dtype)
 
     def fused():
         pkv.pkv_decode_append(q, desc, k_pool, v_pool, bt, cl, wl.max_context_len, k_new, v_new,
@@ -260,7 +271,7 @@ def main():
         # slot mapping and scatter of the new tokens in one launch (the slots are
         # written out too), then the decode
         pkv.pkv_kv_cache_append(bt, seq_idx, pos_new, k_new, v_new, desc, k_pool, v_pool,
-                                ks, vs, src_dtype="bf16", slot_mapping_out=slots)
+                                ks, vs, src_dtype=wl.src_dtype, slot_mapping_out=slots)
         decode()
 
     def timed(fn, n):
@@ -295,7 +306,7 @@ def main():
         import oracle
         sel = np.array([0, int(np.argmax(wl.context_lens))], np.int32)
         opool = _oracle_pool(oracle, wl, sel)
-        ref = oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
+        ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale,
                                   seqs=sel, window=a.window)
         got = out.float().cpu().numpy().astype(np.float64)[sel]
         err = np.abs(got - ref)
@@ -334,12 +345,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.q_dtype,
         "data": "synthetic",
         "config": {
             "workload": wl_text,
             "num_seqs": wl.num_seqs,
-            "context_lens": "U[32768,131072], seed 3" if a.workload == "long" else "U[128,4096], seed 2",
+            "context_lens": {"long": "U[32768,131072], seed 3", "tiny": "{5, 11}, seed 1"}.get(
+                a.workload, "U[128,4096], seed 2"),
             "sum_context": int(wl.context_lens.sum()), "H_q": wl.num_q_heads,
             "H_kv": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
             "kv_dtype": wl.kv_dtype,
@@ -709,7 +721,7 @@ def cpu_baseline_shared(wl, shared_len, budget_s):
         k += len(sel)
     step_s = t_used * wl.num_seqs / done
     return {"value": round((shared_bytes(wl, shared_len) + write_bytes(wl)) / step_s / 1e9, 3),
-            "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "decode of %d of the 256 sequences (%.1f s), scaled to the whole batch"
                       % (done, t_used),
             "us_per_step": round(step_s * 1e6, 1)}
@@ -733,6 +745,7 @@ def cpu_baseline_copy(pairs_np, block_bytes):
     dt = (time.perf_counter() - t0) / n
     alg = 2 * len(pairs_np) * block_bytes * 2
     return {"value": round(alg / dt / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "the same 2048 pairs on host copies of the touched blocks, %d runs" % n}
 
 
@@ -761,7 +774,7 @@ def cpu_baseline_prefill(wl, budget_s):
         if t_used >= budget_s:
             break
     return {"value": round(flops / t_used / 1e12, 5), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of 8192 query rows (every 37th, %d passes), all heads, %.1f s"
                       % (done, done * 37 // total, t_used)}
 
@@ -780,29 +793,57 @@ def _oracle_pool(oracle, wl, seqs=None):
     return opool
 
 
-def cpu_baseline(wl, budget_s, window=0):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline's record."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s, window=0, single_thread_steps=1):
     """The oracle as it stands, on the same workload, on this host's cores: whole steps
-    (the write of the new tokens plus decode attention of every sequence)."""
+    (the write of the new tokens plus decode attention of every sequence); then
+    `single_thread_steps` more whole steps on one thread."""
     import oracle
     opool = _oracle_pool(oracle, wl)
     rows = wl.decode_new_token_rows()
     order = np.arange(wl.num_seqs, dtype=np.int32)
+
+    def one_step():
+        s_new = oracle.slot_mapping(wl.block_table, order, wl.context_lens - 1, wl.block_size)
+        oracle.kv_cache_write(opool, s_new, wl.k_src[rows], wl.v_src[rows], wl.src_dtype)
+        oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale,
+                            window=window)
+
+    cores = oracle.num_threads()
     steps, t_used = 0, 0.0
     while t_used < budget_s and steps < 1000:  # whole steps, at least one
         t0 = time.perf_counter()
-        s_new = oracle.slot_mapping(wl.block_table, order, wl.context_lens - 1, wl.block_size)
-        oracle.kv_cache_write(opool, s_new, wl.k_src[rows], wl.v_src[rows], "bf16")
-        oracle.paged_decode(wl.q, "bf16", opool, wl.block_table, wl.context_lens, wl.scale,
-                            window=window)
+        one_step()
         t_used += time.perf_counter() - t0
         steps += 1
     step_s = t_used / steps
     step_bytes = decode_bytes(wl, window) + write_bytes(wl)
-    return {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d whole steps of the same workload (write of the %d new tokens + decode "
-                      "of all %d sequences), %.1f s" % (steps, wl.num_seqs, wl.num_seqs, t_used),
-            "us_per_step": round(step_s * 1e6, 1)}
+    res = {"value": round(step_bytes / step_s / 1e9, 3), "unit": "GB/s",
+           "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": "%d whole steps of the same workload (write of the %d new tokens + decode "
+                     "of all %d sequences), %.1f s" % (steps, wl.num_seqs, wl.num_seqs, t_used),
+           "us_per_step": round(step_s * 1e6, 1)}
+    if single_thread_steps > 0:
+        oracle.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            for _ in range(single_thread_steps):
+                one_step()
+            res["single_thread_us_per_step"] = round(
+                (time.perf_counter() - t0) / single_thread_steps * 1e6, 1)
+        finally:
+            oracle.set_num_threads(cores)
+    return res
 
 
 if __name__ == "__main__":

@@ -85,6 +85,7 @@ def _load():
                 "orc_split_reduce": (None, [P, P, P, P, I64, I64, I64, I64, I64, P]),
                 "orc_paged_prefill": (I32, [P, I32, P, I64, I64, P, P, I64, P, D, I32, P, I64, P]),
                 "orc_num_threads": (I32, []),
+                "orc_set_num_threads": (None, [I32]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(lib, name)
@@ -104,6 +105,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on (timing only)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------------------

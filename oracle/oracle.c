@@ -24,6 +24,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* threads the OpenMP loops use from now on (n >= 1); a timing knob only */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---- [P2 "Page-table addressing"] ------------------------------------------
  * The page's reference: reject a non-positive block size or a negative position
  * (ValueError); split the position into (logical block, offset); a logical

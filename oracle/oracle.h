@@ -179,6 +179,7 @@ int orc_paged_prefill(const void* q, int q_dtype, const int32_t* cu_seqlens_q, i
 
 /* number of OpenMP threads the oracle uses (for reporting) */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
