@@ -168,6 +168,7 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
                                             uint8_t* vbuf, int base, int end,
                                             const PieceMap<KVT, D>& pm) {
   using C = PCfg<KVT, D>;
+  const bool tail = uniform(base + 64 > end ? 1 : 0) != 0;
 #pragma unroll
   for (int i = 0; i < C::KP; ++i) {
     const int c = pm.k_c[i], tok = pm.k_tok;
@@ -189,11 +190,13 @@ __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t*
     const int lim = end - (base + t0);  // tokens of the piece below end
     uint8_t* row = vbuf + d * C::VROW;
     u32x4 w = r.v[i];
-    if (lim < C::TP) {  // the chunk's last piece: zero what lies past the context
+    if (tail) {
+      if (lim < C::TP) {  // the context's last piece: zero what lies past it
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok_e = e / C::EB;
-        if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+        for (int e = 0; e < 16; ++e) {
+          const int tok_e = e / C::EB;
+          if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+        }
       }
     }
     // 16-bit values of the piece's tokens t0 + i; a row keeps, per 16-byte unit
