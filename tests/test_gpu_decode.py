@@ -261,6 +261,40 @@ def test_llama3_8b_full_peaked(factor):
     print(_compare(case, wl, opool, [0, -1, 512], seqs, factor))
 
 
+@pytest.mark.parametrize("kv,mode", [("fp8", "block"), ("int8", "block"), ("fp8", "tensor"),
+                                     ("int8", "token")])
+def test_llama3_8b_full_quantised(kv, mode):
+    """The full Llama-3-8B-shaped batch over 8-bit pools, in the unsplit launch (whose
+    block- and tensor-scale pools read 128-token super-chunks) and the balanced one:
+    the write path bit for bit against the oracle's, sampled sequences within the
+    tolerance (the longest and the shortest among them)."""
+    wl = W.llama3_8b_decode(kv_dtype=kv, scale_mode=mode)
+    seqs = np.array([int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens)), 5],
+                    np.int32)
+    case = GpuCase(wl)
+    # the oracle's fp8 encoder searches every code: fill its pool with the sampled
+    # sequences' tokens only, and compare the pools on those sequences' blocks
+    keep = np.isin(wl.fill_seq, seqs)
+    opool = oracle.Pool(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv_dtype,
+                        scale_mode=wl.scale_mode)
+    opool.k.view(np.uint8)[...] = 0xFF
+    opool.v.view(np.uint8)[...] = 0xFF
+    opool.k_scale, opool.v_scale = wl.k_scale, wl.v_scale
+    slots = oracle.slot_mapping(wl.block_table, wl.fill_seq[keep], wl.fill_pos[keep],
+                                wl.block_size)
+    oracle.kv_cache_write(opool, slots, wl.k_src[keep], wl.v_src[keep], wl.src_dtype)
+    blocks = np.unique(np.concatenate([wl.block_table[s, :-(-int(wl.context_lens[s]) //
+                                                             wl.block_size)] for s in seqs]))
+    gk, gv = case.logical_pools()
+    assert np.array_equal(gk[blocks].view(np.uint8), opool.k[blocks].view(np.uint8))
+    assert np.array_equal(gv[blocks].view(np.uint8), opool.v[blocks].view(np.uint8))
+    ref = oracle.paged_decode(wl.q, wl.q_dtype, opool, wl.block_table, wl.context_lens, wl.scale,
+                              seqs=seqs)
+    for P in (0, -1, 192):
+        out = to_f64(case.decode(partition_size=P), wl.q_dtype)[seqs]
+        print(assert_close(out, ref, "%s P=%d" % (wl.name, P)))
+
+
 @pytest.mark.parametrize("which", ["llama3 small", "long small", "llama3 full", "edges B4",
                                    "edges B64"])
 def test_planted_keys(which):
