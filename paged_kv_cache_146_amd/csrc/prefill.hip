@@ -19,9 +19,10 @@
 //   O^T = V^T . P^T 16x16x32 MFMA in the V staging type, P from the lane's own
 //                   scores (tile T row n is key 16 T + n, so S^T leaves lane
 //                   (n, g) the keys 16 T + 4 g + r, the k-slots P.V needs).
-// fp8 pools: K's page scale multiplies the scores, V's is folded into P, and
-// P.V runs in f16 (P keeps 11 significant bits).  bf16 pools: P.V in bf16 with
-// P split into hi + lo bf16 terms.
+// fp8 pools: K's page scale multiplies the scores; V's multiplies V as it is
+// widened to f16 in LDS; P.V runs in f16 (P keeps 11 significant bits) and the
+// softmax sum adds the same f16 values of P.  bf16 pools: P.V in bf16 with P split
+// into hi + lo bf16 terms.
 //
 // LDS rows are XOR-swizzled in 16-byte units (K rows by token mod 16, V rows by
 // dim / 2 mod 8) so that the lanes of one LDS cycle hit distinct banks, for the
@@ -161,68 +162,104 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
   }
 }
 
-// Widen the thread's pieces to 16 bits and write them into the LDS buffers;
-// V tokens at or past `end` become zero (their slots may hold anything).
+// Widen K piece i of the thread to 16 bits and write it into a K buffer.
+template <int KVT, int D>
+__device__ __forceinline__ void stage_k_piece(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
+                                              const PieceMap<KVT, D>& pm, int i) {
+  using C = PCfg<KVT, D>;
+  const int c = pm.k_c[i], tok = pm.k_tok;
+  uint8_t* row = kbuf + tok * C::KROW;
+  if constexpr (KVT == DT_FP8) {
+    const u32x4 w = r.k[i];
+    const u32x4 lo = fp8x8<DT_BF16>(w[0], w[1]), hi = fp8x8<DT_BF16>(w[2], w[3]);
+    const int u0 = 2 * c, u1 = 2 * c + 1;
+    *reinterpret_cast<u32x4*>(row + ((u0 ^ (tok & (C::KUNITS - 1))) << 4)) = lo;
+    *reinterpret_cast<u32x4*>(row + ((u1 ^ (tok & (C::KUNITS - 1))) << 4)) = hi;
+  } else {
+    *reinterpret_cast<u32x4*>(row + ((c ^ (tok & (C::KUNITS - 1))) << 4)) = r.k[i];
+  }
+}
+
+// Widen the thread's K pieces to 16 bits and write them into a K buffer.
+template <int KVT, int D>
+__device__ __forceinline__ void stage_k(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
+                                        const PieceMap<KVT, D>& pm) {
+#pragma unroll
+  for (int i = 0; i < PCfg<KVT, D>::KP; ++i) stage_k_piece<KVT, D>(r, kbuf, pm, i);
+}
+
+// Widen V piece i of the thread to 16 bits and write it into a V buffer.  MASK: the
+// tokens at or past `end` (chunk at `base`) become zero, as their slots may hold
+// anything; only the chunk that reaches `end` needs it.
+template <int KVT, int D, bool MASK>
+__device__ __forceinline__ void stage_v_piece(const Raw<PCfg<KVT, D>>& r, uint8_t* vbuf, int base,
+                                              int end, const PieceMap<KVT, D>& pm, int i,
+                                              float vsc) {
+  using C = PCfg<KVT, D>;
+  const int p = pm.v_p[i], d = pm.v_d[i];
+  const int t0 = p * C::TP;
+  uint8_t* row = vbuf + d * C::VROW;
+  u32x4 w = r.v[i];
+  if constexpr (MASK) {
+    const int lim = end - (base + t0);  // tokens of the piece below end
+    if (lim < C::TP) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok_e = e / C::EB;
+        if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
+      }
+    }
+  }
+  // 16-bit values of the piece's tokens t0 + i; a row keeps, per 16-byte unit
+  // u = 4 s2 + g, the keys 32 s2 + 4 g + (0..3) and 32 s2 + 16 + 4 g + (0..3)
+  // (the k-slots of one P.V operand), so key t sits at unit 4 (t / 32) + (t / 4) % 4,
+  // half (t / 16) % 2
+  uint32_t h16[C::TP / 2];
+  if constexpr (KVT == DT_FP8) {
+    // f16(code) times the page's V scale (rounded to f16), one packed multiply per pair
+    const u32x4 lo = fp8x8<DT_F16>(w[0], w[1]), hi = fp8x8<DT_F16>(w[2], w[3]);
+    const f16x2 sc = {(_Float16)vsc, (_Float16)vsc};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      h16[k] = __builtin_bit_cast(uint32_t, as_f16x2(lo[k]) * sc);
+      h16[4 + k] = __builtin_bit_cast(uint32_t, as_f16x2(hi[k]) * sc);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h16[k] = w[k];
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < C::TP / 4; ++q4) {  // runs of four keys
+    const int t = t0 + 4 * q4;
+    const int u = 4 * (t >> 5) + ((t >> 2) & 3);
+    *reinterpret_cast<u32x2*>(row + ((u ^ ((d >> 1) & 7)) << 4) + 8 * ((t >> 4) & 1)) =
+        u32x2{h16[2 * q4], h16[2 * q4 + 1]};
+  }
+}
+
+// Widen the thread's V pieces to 16 bits and write them into a V buffer (MASK as above);
+// fp8: piece i is scaled by vsc[i], the V scale of its page.
+template <int KVT, int D, bool MASK>
+__device__ __forceinline__ void stage_v(const Raw<PCfg<KVT, D>>& r, uint8_t* vbuf, int base,
+                                        int end, const PieceMap<KVT, D>& pm,
+                                        const float (&vsc)[PCfg<KVT, D>::VP]) {
+#pragma unroll
+  for (int i = 0; i < PCfg<KVT, D>::VP; ++i)
+    stage_v_piece<KVT, D, MASK>(r, vbuf, base, end, pm, i, vsc[i]);
+}
+
+// Both halves; V tokens at or past `end` become zero.  Only the chunk that reaches
+// `end` has such tokens: the check sits behind a wave-uniform branch.
 template <int KVT, int D>
 __device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
                                             uint8_t* vbuf, int base, int end,
-                                            const PieceMap<KVT, D>& pm) {
-  using C = PCfg<KVT, D>;
-  const bool tail = uniform(base + 64 > end ? 1 : 0) != 0;
-#pragma unroll
-  for (int i = 0; i < C::KP; ++i) {
-    const int c = pm.k_c[i], tok = pm.k_tok;
-    uint8_t* row = kbuf + tok * C::KROW;
-    if constexpr (KVT == DT_FP8) {
-      const u32x4 w = r.k[i];
-      const u32x4 lo = fp8x8<DT_BF16>(w[0], w[1]), hi = fp8x8<DT_BF16>(w[2], w[3]);
-      const int u0 = 2 * c, u1 = 2 * c + 1;
-      *reinterpret_cast<u32x4*>(row + ((u0 ^ (tok & (C::KUNITS - 1))) << 4)) = lo;
-      *reinterpret_cast<u32x4*>(row + ((u1 ^ (tok & (C::KUNITS - 1))) << 4)) = hi;
-    } else {
-      *reinterpret_cast<u32x4*>(row + ((c ^ (tok & (C::KUNITS - 1))) << 4)) = r.k[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < C::VP; ++i) {
-    const int p = pm.v_p[i], d = pm.v_d[i];
-    const int t0 = p * C::TP;
-    const int lim = end - (base + t0);  // tokens of the piece below end
-    uint8_t* row = vbuf + d * C::VROW;
-    u32x4 w = r.v[i];
-    if (tail) {
-      if (lim < C::TP) {  // the context's last piece: zero what lies past it
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tok_e = e / C::EB;
-          if (tok_e >= lim) w[e >> 2] &= ~(0xffu << (8 * (e & 3)));
-        }
-      }
-    }
-    // 16-bit values of the piece's tokens t0 + i; a row keeps, per 16-byte unit
-    // u = 4 s2 + g, the keys 32 s2 + 4 g + (0..3) and 32 s2 + 16 + 4 g + (0..3)
-    // (the k-slots of one P.V operand), so key t sits at unit 4 (t / 32) + (t / 4) % 4,
-    // half (t / 16) % 2
-    uint32_t h16[C::TP / 2];
-    if constexpr (KVT == DT_FP8) {
-      const u32x4 lo = fp8x8<DT_F16>(w[0], w[1]), hi = fp8x8<DT_F16>(w[2], w[3]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        h16[k] = lo[k];
-        h16[4 + k] = hi[k];
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) h16[k] = w[k];
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < C::TP / 4; ++q4) {  // runs of four keys
-      const int t = t0 + 4 * q4;
-      const int u = 4 * (t >> 5) + ((t >> 2) & 3);
-      *reinterpret_cast<u32x2*>(row + ((u ^ ((d >> 1) & 7)) << 4) + 8 * ((t >> 4) & 1)) =
-          u32x2{h16[2 * q4], h16[2 * q4 + 1]};
-    }
-  }
+                                            const PieceMap<KVT, D>& pm,
+                                            const float (&vsc)[PCfg<KVT, D>::VP]) {
+  stage_k<KVT, D>(r, kbuf, pm);
+  if (uniform(base + 64 > end ? 1 : 0) != 0)
+    stage_v<KVT, D, true>(r, vbuf, base, end, pm, vsc);
+  else
+    stage_v<KVT, D, false>(r, vbuf, base, end, pm, vsc);
 }
 
 // Headroom of the lazily moved softmax reference, in log2 units: p <= 2^kLazyMax.
@@ -231,6 +268,12 @@ constexpr float kLazyMax = 4.0f;
 
 // LDS operand reads in flight ahead of the MFMA that uses them
 constexpr int kPrefetch = 4;
+
+// maximum of four floats (NaN-propagating: v_maximum3, no operand quieting)
+__device__ __forceinline__ float fmax4(float a, float b, float c, float d) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                       __builtin_elementwise_maximum(c, d));
+}
 
 // per-row online-softmax state of one row tile: lane (n, g) holds column n
 template <int D>
@@ -367,6 +410,20 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     fill_window(0);
     __syncthreads();
     const PieceMap<KVT, D> pm(wave, lane, ps.blog2);
+    // V scales of the thread's pieces of the chunk at `base` from window wk (fp8; a
+    // piece's 16 tokens sit in one tile, the same for the whole wavefront)
+    auto piece_scales = [&](int base, int wk, float (&vsc)[C::VP]) {
+      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+#pragma unroll
+      for (int i = 0; i < C::VP; ++i) {
+        if constexpr (kFp8) {
+          const int t = min(base + uniform(pm.v_p[i]) * C::TP, kend - 1);
+          vsc[i] = w_vs[(t >> ps.blog2) - blk0];
+        } else {
+          vsc[i] = 1.0f;
+        }
+      }
+    };
     Raw<C> ra, rb;
     {
       int pg[4];
@@ -377,7 +434,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, wave, pm, ps);
       }
     }
-    chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, 0, kend, pm);
+    {
+      float vsc[C::VP];
+      piece_scales(0, 0, vsc);
+      chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, 0, kend, pm, vsc);
+    }
     __syncthreads();
 
     // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
@@ -390,7 +451,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         win_pages(j + 2, wk, pg);
         chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg, base + 128, kend, kvh, wave, pm, ps);
       }
-      float zs[4], vs[4];
+      float zs[4];  // per tile: softmax scale x K's page scale, log2 units
       {
         const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
 #pragma unroll
@@ -398,10 +459,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           if constexpr (kFp8) {
             const int i = (min(base + 16 * T, kend - 1) >> ps.blog2) - blk0;
             zs[T] = w_ks[i];
-            vs[T] = w_vs[i];
           } else {
             zs[T] = ps.scale_log2;
-            vs[T] = 1.0f;
           }
         }
       }
@@ -456,11 +515,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[rt][T][r] = 16 * T + r < lim ? S[rt][T][r] : -INFINITY;
         }
-        float cm = -INFINITY;
+        float tm[4];
 #pragma unroll
         for (int T = 0; T < 4; ++T)
-          cm = fmaxf(cm, fmaxf(fmaxf(S[rt][T][0], S[rt][T][1]), fmaxf(S[rt][T][2], S[rt][T][3])) * zs[T]);
-        cm = max_groups(cm);
+          tm[T] = fmax4(S[rt][T][0], S[rt][T][1], S[rt][T][2], S[rt][T][3]) * zs[T];
+        float cm = max_groups(fmax4(tm[0], tm[1], tm[2], tm[3]));
         // The reference max moves only when a chunk's max passes it by more than
         // kLazyMax, so the accumulators are rescaled rarely (the softmax does not
         // depend on the reference); p then stays below 2^kLazyMax.
@@ -474,41 +533,45 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
         }
         const float mref = st[rt].m == -INFINITY ? 0.0f : st[rt].m;  // rows that have seen no key yet
-        float p[16], psum = 0.0f;
+        float p[16];
 #pragma unroll
         for (int T = 0; T < 4; ++T)
 #pragma unroll
           for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) psum += p[i];
-        st[rt].l += psum;
+        float psum = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           uint32_t wh[4], wl[4];
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) {
             const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
-            float a = p[i0], b = p[i0 + 1];
-            if constexpr (kFp8) {
-              a *= vs[i0 >> 2];
-              b *= vs[i0 >> 2];
-            }
+            const float a = p[i0], b = p[i0 + 1];
             wh[wd] = pack2<C::PT>(a, b);
             if constexpr (C::SPLIT) {
               const f32x2 h = unpack2<C::PT>(wh[wd]);
               wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
+              psum += a + b;
             } else {
+              // fp8 pools: V carries its page scale, P is f16(p); the row sum adds the
+              // same rounded values (exact f16 products, fp32 sum)
               wl[wd] = 0u;
+              psum = __builtin_amdgcn_fdot2(as_f16x2(wh[wd]), f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                            psum, false);
             }
           }
           phi[rt][s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
           plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
         }
+        st[rt].l += psum;
       }
       // ---- stage chunk j+1 into the other buffer (free since the last barrier)
       // while the matrix cores run O^T += V^T . P^T: the conversions and LDS writes
       // fill the issue slots between the MFMAs
-      if (j + 1 < nch) chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm);
+      if (j + 1 < nch) {
+        float vsc[C::VP];
+        piece_scales(base + 64, wk, vsc);
+        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
+      }
       __builtin_amdgcn_s_setprio(2);
       {
         // V operands (i = 2 dt + s2), read kPrefetch ahead as the K operands above
@@ -541,7 +604,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       }
       __builtin_amdgcn_s_setprio(0);
       } else if (j + 1 < nch) {  // no key of this chunk for the wave: only the staging
-        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm);
+        float vsc[C::VP];
+        piece_scales(base + 64, wk, vsc);
+        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
       }
       issue_point();
       // ---- advance the page window
