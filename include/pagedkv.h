@@ -350,7 +350,11 @@ int pkv_paged_attention_decode_window(const void* q, int32_t q_dtype, int32_t nu
  * per sequence:
  *   1. the prefix tokens [0, shared_len): one pass per (kv head, slice of the
  *      prefix) over row 0's blocks, the queries of 16/G sequences x G heads in
- *      the 16 columns of each matrix-core tile;
+ *      the 16 columns of each matrix-core tile.  For the type pairs, block
+ *      sizes and groups that pkv_paged_prefill takes, the pass is that
+ *      kernel's: each K/V chunk is staged once in LDS for 128/G sequences, and
+ *      a sequence's rows see the prefix keys below min(ctx_s, shared_len);
+ *      prefix slots past every sequence's context are never read;
  *   2. every sequence's own tokens [shared_len, ctx_s): the balanced decode,
  *      started shared_len / block_size entries into each table row;
  *   3. the log-sum-exp merge of the prefix slices and the tail (as
@@ -430,16 +434,17 @@ int pkv_split_kv_reduce(const float* part_out, const float* part_max, const floa
  *   q: device [total_q][num_q_heads][head_dim] of q_dtype; out likewise.
  *   cu_seqlens_q: device int32 [num_seqs + 1], non-decreasing, last = total_q.
  *   max_q_len: host-known upper bound on n_s (sizes the grid).
- *   Supported: q bf16 with a bf16 pool or an fp8 pool in PKV_SCALE_BLOCK mode
- *   (other pools: PKV_EUNSUPPORTED); head_dim 64 or 128; block_size
- *   16..64 (a 16-token tile must lie in one block); group size G = H_q/H_kv
- *   in {1, 2, 4, 8, 16}.  fp8 keys widen exactly to bf16 for QK^T and K's
- *   scale multiplies the scores; fp8 values widen exactly to f16 and V's scale
- *   multiplies the probabilities, which enter P.V as f16 (the probabilities are
- *   taken against a reference that trails the running max by less than a
- *   factor 16, so v_scale must stay below 4096 for f16 to hold them; the
- *   E4M3 values it scales then reach 1.8e6).  With a bf16 pool the
- *   probabilities enter P.V as a hi + lo pair of bf16 values.
+ *   Supported: q bf16 with a bf16 pool or an fp8 pool in PKV_SCALE_BLOCK mode,
+ *   q f16 with an f16 pool (other pairs: PKV_EUNSUPPORTED); out has q's
+ *   dtype; head_dim 64 or 128; block_size 16..64 (a 16-token tile must lie
+ *   in one block); group size G = H_q/H_kv in {1, 2, 4, 8, 16}.  fp8 keys
+ *   widen exactly to bf16 for QK^T and K's scale multiplies the scores; fp8
+ *   values widen exactly to f16 and are multiplied in f16 by V's scale
+ *   (rounded to f16), so the scaled values must lie in f16's range.  The
+ *   probabilities (taken against a reference that trails the running max by
+ *   less than a factor 16) enter P.V as f16 for fp8 and f16 pools, and their
+ *   sum adds those same f16 values; with a bf16 pool they enter as a hi + lo
+ *   pair of bf16 values.
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EHIP. */
 int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
                       int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,

@@ -314,6 +314,17 @@ size_t balanced_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_
          2 * (size_t)PKV_MAX_WORKERS * group * ((size_t)head_dim + 2) * sizeof(float);
 }
 
+// Type pairs of the matrix-core prefill kernel: bf16 q over bf16 or fp8 (one scale
+// per block and kv head) pools, f16 q over f16 pools.
+bool prefill_types_ok(int q_dtype, const pkv_pool_desc* pool) {
+  switch (pool->kv_dtype) {
+    case PKV_BF16: return q_dtype == PKV_BF16;
+    case PKV_F16: return q_dtype == PKV_F16;
+    case PKV_FP8_E4M3: return q_dtype == PKV_BF16 && pool->scale_mode == PKV_SCALE_BLOCK;
+    default: return false;
+  }
+}
+
 // How a shared-prefix decode cuts the prefix: slices of whole 64-token chunks,
 // enough of them that (kv heads x column tiles x slices) reaches about 2048
 // wavefronts; the partial slots are the slices plus one for the tails.
@@ -692,17 +703,57 @@ int pkv_paged_attention_decode_shared(const void* q, int32_t q_dtype, int32_t nu
   p.scale = scale;
   p.max_parts = sp.max_parts;
 
-  // 1. the prefix, read once per kv head: partial slots 0 .. n_slices-1
-  pkv::DecodeLaunch pre = p;
-  pre.prefix = 1;
-  pre.ctx_cap = (int)cap;
-  pre.shared_len = shared_len;
-  pre.n_slices = sp.n_slices;
-  pre.slice_chunks = sp.slice_chunks;
-  pre.part_out = part_out;
-  pre.part_max = part_max;
-  pre.part_sum = part_sum;
-  rc = pkv::launch_decode(pre, as_stream(stream));
+  // 1. the prefix, read once per kv head: partial slots 0 .. n_slices-1.  On the
+  // matrix-core prefill kernel (its K/V chunks staged once in LDS for 128/G
+  // sequences) where it takes the types and shapes, else on the decode tiles.
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (prefill_types_ok(q_dtype, pool) && pool->block_size >= 16 && 16 % group == 0) {
+    pkv::PrefillLaunch pl;
+    pl.q = q;
+    pl.q_dtype = q_dtype;
+    pl.cu_seqlens_q = nullptr;
+    pl.num_seqs = num_seqs;
+    pl.total_q = num_seqs;
+    pl.max_q_len = 1;
+    pl.num_q_heads = num_q_heads;
+    pl.k_pool = k_pool;
+    pl.v_pool = v_pool;
+    pl.k_scale = k_scale;
+    pl.v_scale = v_scale;
+    pl.num_blocks = pool->num_blocks;
+    pl.block_size = pool->block_size;
+    pl.num_kv_heads = pool->num_kv_heads;
+    pl.head_dim = pool->head_dim;
+    pl.kv_dtype = pool->kv_dtype;
+    pl.bstride = block_units(pool);
+    pl.block_table = block_table;
+    pl.max_blocks_per_seq = max_blocks_per_seq;
+    pl.context_lens = context_lens;
+    pl.ctx_cap = (int)cap;
+    pl.scale = scale;
+    pl.causal = 0;
+    pl.out = nullptr;
+    pl.prefix = 1;
+    pl.shared_len = shared_len;
+    pl.n_slices = sp.n_slices;
+    pl.slice_chunks = sp.slice_chunks;
+    pl.max_parts = sp.max_parts;
+    pl.part_out = part_out;
+    pl.part_max = part_max;
+    pl.part_sum = part_sum;
+    rc = pkv::launch_prefill(pl, as_stream(stream));
+  } else {
+    pkv::DecodeLaunch pre = p;
+    pre.prefix = 1;
+    pre.ctx_cap = (int)cap;
+    pre.shared_len = shared_len;
+    pre.n_slices = sp.n_slices;
+    pre.slice_chunks = sp.slice_chunks;
+    pre.part_out = part_out;
+    pre.part_max = part_max;
+    pre.part_sum = part_sum;
+    rc = pkv::launch_decode(pre, as_stream(stream));
+  }
   if (rc != 0) return rc;
 
   // 2. the private tails, balanced: partial slot n_slices
@@ -779,10 +830,7 @@ int pkv_paged_prefill(const void* q, int32_t q_dtype, const int32_t* cu_seqlens_
       max_blocks_per_seq < 1 || max_context_len < 0)
     return PKV_EINVAL;
   if (num_q_heads % pool->num_kv_heads != 0) return PKV_EINVAL;
-  if (q_dtype != PKV_BF16) return PKV_EUNSUPPORTED;
-  if (pool->kv_dtype != PKV_BF16 &&
-      !(pool->kv_dtype == PKV_FP8_E4M3 && pool->scale_mode == PKV_SCALE_BLOCK))
-    return PKV_EUNSUPPORTED;
+  if (!prefill_types_ok(q_dtype, pool)) return PKV_EUNSUPPORTED;
   if (pool->head_dim != 128 && pool->head_dim != 64) return PKV_EUNSUPPORTED;
   if (pool->block_size < 16) return PKV_EUNSUPPORTED;  // a 16-token tile sits in one block
   {

@@ -122,6 +122,15 @@ struct PrefillLaunch {
   float scale;
   int causal;
   void* out;
+  // prefix mode (a shared-prefix decode's prefix on the matrix cores): the rows are
+  // the num_seqs sequences, the keys the first shared_len tokens of table row 0 in
+  // n_slices slices of slice_chunks 64-token chunks; slice i's state goes to partial
+  // slot i of max_parts
+  int prefix = 0;
+  int shared_len = 0, n_slices = 0, slice_chunks = 0, max_parts = 0;
+  float* part_out = nullptr;
+  float* part_max = nullptr;
+  float* part_sum = nullptr;
 };
 int launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 

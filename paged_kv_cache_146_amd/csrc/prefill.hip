@@ -42,9 +42,15 @@ struct PrefillScalars {
   int S, Hq, Hkv, G;
   int blog2, num_blocks, ctx_cap;
   int causal;
-  int nqb;         // query blocks per sequence (grid)
+  int nqb;         // query blocks per pair (grid)
+  int pairs;       // (sequence, kv head) pairs; prefix mode: (kv head, slice) pairs
   float scale_log2;
   long long bstride;  // 16-byte units from one block to the next in each pool
+  // prefix mode: slices of the shared prefix and the partial states they leave
+  int shared_len, n_slices, slice_chunks, max_parts;
+  float* part_out;
+  float* part_max;
+  float* part_sum;
 };
 
 // Workgroups are dealt to the XCDs round robin by id (id mod 8), and each XCD has
@@ -69,10 +75,11 @@ struct PCfg {
   static constexpr int VROW = 64 * 2;               // staged V row (one dim, 64 tokens)
   static constexpr int KBUF = 64 * KROW;
   static constexpr int VBUF = D * VROW;
-  static constexpr int PT = KVT == DT_FP8 ? DT_F16 : DT_BF16;  // type of the P.V product
-  static constexpr bool SPLIT = (PT == DT_BF16);               // P as hi + lo
+  static constexpr int QT = KVT == DT_F16 ? DT_F16 : DT_BF16;  // q, staged K and the output
+  static constexpr int PT = KVT == DT_BF16 ? DT_BF16 : DT_F16;  // type of the P.V product
+  static constexpr bool SPLIT = (PT == DT_BF16);                // P as hi + lo
   // two resident workgroups per CU where the registers allow it (LDS holds two)
-  static constexpr int WPE = (KVT == DT_BF16 && D == 128) ? 1 : 2;
+  static constexpr int WPE = (KVT != DT_FP8 && D == 128) ? 1 : 2;
   static constexpr int KP = 64 * NC / kPfThreads;   // K pool pieces per thread per chunk
   static constexpr int VP = D * (64 / TP) / kPfThreads;  // V pool pieces per thread
   static_assert(KP >= 1 && VP >= 1, "chunk too small for the workgroup");
@@ -282,7 +289,26 @@ struct RowState {
   float m, l;
 };
 
-template <int KVT, int D>
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return uniform(x);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return uniform(x);
+}
+
+// PREFIX: the shared prefix of a decode batch instead of a prefill chunk.  The rows
+// are then (sequence, query head) pairs of one kv head (16/G sequences per row tile,
+// every sequence's one query token), the keys one slice of the prefix that every
+// sequence reads from the same blocks (table row 0); row (s, h) sees the prefix keys
+// below min(ctx_s, shared_len), without a causal bound.  The slice's state of each
+// row (normalised output, reference max in natural-log units, sum) goes to partial
+// slot `slice`, which a log-sum-exp merge combines with the other slices and the
+// sequence's private tail.
+template <int KVT, int D, bool PREFIX = false>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     PCfg<KVT, D>::WPE, PCfg<KVT, D>::WPE))) void paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
                      const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -304,38 +330,53 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
 
   const int xcd = blockIdx.x % kXcds, xslot = blockIdx.x / kXcds;
   const int pair = (xslot / ps.nqb) * kXcds + xcd, qb = xslot % ps.nqb;
-  if (pair >= ps.S * ps.Hkv) return;  // the grid is rounded up to whole XCD rows
-  const int s = pair / ps.Hkv, kvh = pair - s * ps.Hkv;
+  if (pair >= ps.pairs) return;  // the grid is rounded up to whole XCD rows
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-  const int G = ps.G, tpr = 16 / G;           // tokens per row tile
-  const int tpw = NR * tpr, tpg = 4 * tpw;    // tokens per wave / per workgroup
-
-  const int q0 = cu_seqlens_q[s];
-  const int nq = cu_seqlens_q[s + 1] - q0;
+  const int G = ps.G, tpr = 16 / G;           // tokens (prefix: sequences) per row tile
+  const int tpw = NR * tpr, tpg = 4 * tpw;    // per wave / per workgroup
   const int tok0 = qb * tpg;
-  if (tok0 >= nq) return;
-  int ctx = context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > ps.ctx_cap ? ps.ctx_cap : ctx);
-  const int pos0 = ctx - nq;  // absolute position of query token 0
-  const int tok_end = min(nq, tok0 + tpg);
-  // keys the workgroup needs: [0, kend)
-  const int kend = ps.causal ? max(0, min(ctx, pos0 + tok_end)) : ctx;
+
+  // the workgroup's rows and keys [kbeg, kend); row t of the pair is token q0 + t
+  // of the query array
+  int s, kvh, slice = 0, q0, nq, ctx = 0, pos0 = 0, kbeg = 0, kend;
+  if constexpr (PREFIX) {
+    kvh = pair / ps.n_slices;
+    slice = pair - kvh * ps.n_slices;
+    s = 0;  // the shared blocks: table row 0
+    q0 = 0;
+    nq = ps.S;
+    if (tok0 >= nq) return;
+    kbeg = slice * ps.slice_chunks * 64;
+    kend = min(kbeg + ps.slice_chunks * 64, ps.shared_len);
+  } else {
+    s = pair / ps.Hkv;
+    kvh = pair - s * ps.Hkv;
+    q0 = cu_seqlens_q[s];
+    nq = cu_seqlens_q[s + 1] - q0;
+    if (tok0 >= nq) return;
+    ctx = context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > ps.ctx_cap ? ps.ctx_cap : ctx);
+    pos0 = ctx - nq;  // absolute position of query token 0
+    const int tok_end = min(nq, tok0 + tpg);
+    kend = ps.causal ? max(0, min(ctx, pos0 + tok_end)) : ctx;
+  }
 
   // ---- this lane's rows: token and head of column n in each row tile
   const int hq = kvh * G + n % G;
   int rtok[NR];  // query token (chunk-relative) of column n, or -1 when past the chunk
   int rlim[NR];  // keys [0, rlim) visible to that row
-  int tile_lim[NR];  // keys [0, tile_lim) visible to any row of the tile (wave-uniform)
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
     const int t = tok0 + wave * tpw + rt * tpr + n / G;
     rtok[rt] = t < nq ? t : -1;
-    rlim[rt] = rtok[rt] < 0 ? 0 : (ps.causal ? max(0, min(ctx, pos0 + t + 1)) : ctx);
-    const int tlast = min(nq, tok0 + wave * tpw + (rt + 1) * tpr) - 1;
-    tile_lim[rt] = uniform(tlast < tok0 + wave * tpw + rt * tpr
-                               ? 0
-                               : (ps.causal ? max(0, min(ctx, pos0 + tlast + 1)) : ctx));
+    if constexpr (PREFIX) {
+      int c = rtok[rt] < 0 ? 0 : context_lens[rtok[rt] < 0 ? 0 : t];  // never past S
+      c = c < 0 ? 0 : (c > ps.ctx_cap ? ps.ctx_cap : c);
+      rlim[rt] = min(c, ps.shared_len);
+    } else {
+      rlim[rt] = rtok[rt] < 0 ? 0 : (ps.causal ? max(0, min(ctx, pos0 + t + 1)) : ctx);
+    }
   }
 
   // ---- q operands (B of S^T), one per row tile and k-step; dead rows are zero
@@ -360,16 +401,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     st[rt].l = 0.0f;
   }
 
-  // keys [0, wave_min_lim) are visible to every live row of the wave; [0, wave_max_lim)
-  // to at least one (wave-uniform)
-  int wave_min_lim = kend, wave_max_lim = 0;
-#pragma unroll
-  for (int rt = 0; rt < NR; ++rt) wave_max_lim = max(wave_max_lim, tile_lim[rt]);
-  {
-    const int t_first = tok0 + wave * tpw;
-    wave_min_lim = t_first >= nq ? 0
-                                 : uniform(ps.causal ? max(0, min(ctx, pos0 + t_first + 1)) : ctx);
-    if (tok0 + wave * tpw + tpw > nq) wave_min_lim = 0;  // the wave holds rows past the chunk
+  // keys [0, wave_min_lim) are visible to every row of the wave (a dead row counts as
+  // seeing none); [0, wave_max_lim) to at least one (wave-uniform)
+  const int wave_min_lim = wave_min_i(min(rlim[0], rlim[NR - 1]));
+  const int wave_max_lim = wave_max_i(max(rlim[0], rlim[NR - 1]));
+  static_assert(NR == 2, "the wave bounds above take the two row tiles");
+  if constexpr (PREFIX) {
+    // keys past every row's bound are never read: they need not have been written
+    // (a prefix token lies in the context of some sequence that sees it)
+    __shared__ int wg_lim[4];
+    if (lane == 0) wg_lim[wave] = wave_max_lim;
+    __syncthreads();
+    kend = min(kend, max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3])));
   }
   // this lane's LDS offsets (swizzled 16-byte units), the same for every chunk
   int k_off[4], k_unit[C::NKS], v_off, v_unit[2];
@@ -381,12 +424,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
   // rows d = 16 dt + n share (d >> 1) & 7 = (n >> 1) & 7 for every dt
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) v_unit[s2] = ((4 * s2 + g) ^ ((n >> 1) & 7)) << 4;
-  const int nch = (kend + 63) >> 6;
+  const int nch = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;  // chunk j: keys kbeg + 64 j ..
   if (nch > 0) {
     const int32_t* trow = block_table + (size_t)s * ps.W;
-    // window k holds the blocks of chunks [32 k, 32 k + 34) (two chunks of lookahead)
+    // window k holds the blocks of chunks [32 k, 32 k + 34) (two chunks of lookahead);
+    // kbeg is a multiple of 64, so of the block size
     auto fill_window = [&](int wk) {
-      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+      const int blk0 = (kbeg + wk * kWinChunks * 64) >> ps.blog2;
       const int last = (kend - 1) >> ps.blog2;
       for (int t = threadIdx.x; t < kWinBlocks; t += kPfThreads) {
         const int e = clamp_block(trow[min(blk0 + t, last)], ps.num_blocks);
@@ -400,10 +444,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     };
     // block ids of chunk c's four tiles from window wk (which must cover c)
     auto win_pages = [&](int c, int wk, int (&pg)[4]) {
-      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+      const int blk0 = (kbeg + wk * kWinChunks * 64) >> ps.blog2;
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
-        const int t = min(64 * c + 16 * T, kend - 1);
+        const int t = min(kbeg + 64 * c + 16 * T, kend - 1);
         pg[T] = uniform(w_blk[(t >> ps.blog2) - blk0]);
       }
     };
@@ -413,7 +457,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     // V scales of the thread's pieces of the chunk at `base` from window wk (fp8; a
     // piece's 16 tokens sit in one tile, the same for the whole wavefront)
     auto piece_scales = [&](int base, int wk, float (&vsc)[C::VP]) {
-      const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+      const int blk0 = (kbeg + wk * kWinChunks * 64) >> ps.blog2;
 #pragma unroll
       for (int i = 0; i < C::VP; ++i) {
         if constexpr (kFp8) {
@@ -428,23 +472,23 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     {
       int pg[4];
       win_pages(0, 0, pg);
-      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, 0, kend, kvh, wave, pm, ps);
+      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, kbeg, kend, kvh, wave, pm, ps);
       if (nch > 1) {
         win_pages(1, 0, pg);
-        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, 64, kend, kvh, wave, pm, ps);
+        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, kbeg + 64, kend, kvh, wave, pm, ps);
       }
     }
     {
       float vsc[C::VP];
-      piece_scales(0, 0, vsc);
-      chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, 0, kend, pm, vsc);
+      piece_scales(kbeg, 0, vsc);
+      chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, kbeg, kend, pm, vsc);
     }
     __syncthreads();
 
     // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
     // are staged after chunk j is computed
     auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1, uint8_t* cur_buf, uint8_t* nxt_buf) {
-      const int base = 64 * j;
+      const int base = kbeg + 64 * j;
       const int wk = j / kWinChunks;
       if (j + 2 < nch) {
         int pg[4];
@@ -453,7 +497,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       }
       float zs[4];  // per tile: softmax scale x K's page scale, log2 units
       {
-        const int blk0 = (wk * kWinChunks * 64) >> ps.blog2;
+        const int blk0 = (kbeg + wk * kWinChunks * 64) >> ps.blog2;
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
           if constexpr (kFp8) {
@@ -490,7 +534,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
           const int T = i / C::NKS, ks = i % C::NKS;
 #pragma unroll
           for (int rt = 0; rt < NR; ++rt)
-            S[rt][T] = mma16<DT_BF16>(kop[i % (kPrefetch + 1)], qop[rt][ks], ks == 0 ? zero : S[rt][T]);
+            S[rt][T] = mma16<C::QT>(kop[i % (kPrefetch + 1)], qop[rt][ks], ks == 0 ? zero : S[rt][T]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 1);
 #pragma unroll
@@ -525,8 +569,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         // depend on the reference); p then stays below 2^kLazyMax.
         const bool moves = cm > st[rt].m + kLazyMax;
         if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+          // 0 for a row's first keys; 1 for a row that does not move (which may not have
+          // seen a key yet: m = -inf, where m - m would be NaN)
           const float mn = moves ? cm : st[rt].m;
-          const float alpha = __builtin_amdgcn_exp2f(st[rt].m - mn);  // 0 for a row's first keys
+          const float alpha = moves ? __builtin_amdgcn_exp2f(st[rt].m - mn) : 1.0f;
           st[rt].m = mn;
           st[rt].l *= alpha;
 #pragma unroll
@@ -623,15 +669,28 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // ---- normalise and store the live rows
+  // ---- normalise and store the live rows (prefix: the slice's partial state; a row
+  // that saw no key leaves an empty state, weight 0)
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
     const float lw = sum_groups(st[rt].l);
     if (rtok[rt] < 0) continue;
     const float inv = lw > 0.0f ? 1.0f / lw : 0.0f;
-    const size_t orow = ((size_t)(q0 + rtok[rt]) * ps.Hq + hq) * D + 4 * g;
+    if constexpr (PREFIX) {
+      const size_t pi = ((size_t)rtok[rt] * ps.Hq + hq) * ps.max_parts + slice;
+      float* o = ps.part_out + pi * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) store4(out, DT_BF16, orow + 16 * dt, st[rt].acc[dt] * inv);
+      for (int dt = 0; dt < C::NDT; ++dt)
+        *reinterpret_cast<f32x4*>(o + 16 * dt) = st[rt].acc[dt] * inv;
+      if (g == 0) {
+        ps.part_max[pi] = lw > 0.0f ? st[rt].m * kLn2 : -INFINITY;
+        ps.part_sum[pi] = lw;
+      }
+    } else {
+      const size_t orow = ((size_t)(q0 + rtok[rt]) * ps.Hq + hq) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) store4(out, C::QT, orow + 16 * dt, st[rt].acc[dt] * inv);
+    }
   }
 }
 
@@ -643,21 +702,29 @@ int log2_exact(int x) {
   return (1 << l) == x ? l : -1;
 }
 
-template <int KVT, int D>
+template <int KVT, int D, bool PREFIX>
 int launch_pf(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) {
   const int tpg = 4 * PCfg<KVT, D>::NR * (16 / ps.G);
   PrefillScalars q = ps;
-  q.nqb = (p.max_q_len + tpg - 1) / tpg;
-  const long long pairs = (long long)p.num_seqs * p.num_kv_heads;
+  const long long rows = PREFIX ? p.num_seqs : p.max_q_len;  // per pair
+  q.nqb = (int)((rows + tpg - 1) / tpg);
+  const long long pairs = PREFIX ? (long long)p.num_kv_heads * p.n_slices
+                                 : (long long)p.num_seqs * p.num_kv_heads;
   const long long per_xcd = (pairs + kXcds - 1) / kXcds;
   const long long blocks = per_xcd * kXcds * q.nqb;
   if (blocks > 0x7fffffffLL) return -3;
+  q.pairs = (int)pairs;
   dim3 grid((unsigned)blocks);
-  hipLaunchKernelGGL((paged_prefill_kernel<KVT, D>), grid, dim3(kPfThreads), 0, st,
+  hipLaunchKernelGGL((paged_prefill_kernel<KVT, D, PREFIX>), grid, dim3(kPfThreads), 0, st,
                      (const uint8_t*)p.q, p.cu_seqlens_q, (const uint8_t*)p.k_pool,
                      (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
                      p.context_lens, (uint8_t*)p.out, q);
   return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <int KVT, int D>
+int pick_mode(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) {
+  return p.prefix ? launch_pf<KVT, D, true>(p, ps, st) : launch_pf<KVT, D, false>(p, ps, st);
 }
 
 }  // namespace
@@ -675,16 +742,32 @@ int launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   ps.causal = p.causal;
   ps.scale_log2 = p.scale * kLog2e;
   ps.bstride = p.bstride;
+  ps.shared_len = p.shared_len;
+  ps.n_slices = p.n_slices;
+  ps.slice_chunks = p.slice_chunks;
+  ps.max_parts = p.max_parts;
+  ps.part_out = p.part_out;
+  ps.part_max = p.part_max;
+  ps.part_sum = p.part_sum;
   if (ps.blog2 < 4 || p.block_size > 64) return -3;  // a 16-token tile must sit in one block
   if (ps.G < 1 || ps.G > 16 || (16 % ps.G) != 0) return -3;
-  if (p.q_dtype != DT_BF16) return -3;
-  if (p.max_q_len <= 0) return 0;
+  // q (and the output) in bf16 over bf16 and fp8 pools, in f16 over f16 pools
+  if (p.q_dtype != (p.kv_dtype == DT_F16 ? DT_F16 : DT_BF16)) return -3;
+  if (p.prefix) {
+    if (p.n_slices < 1 || p.slice_chunks < 1 || p.max_parts < p.n_slices) return -3;
+    if (p.num_seqs <= 0 || p.shared_len <= 0) return 0;
+  } else if (p.max_q_len <= 0) {
+    return 0;
+  }
   if (p.kv_dtype == DT_FP8) {
-    if (p.head_dim == 128) return launch_pf<DT_FP8, 128>(p, ps, st);
-    if (p.head_dim == 64) return launch_pf<DT_FP8, 64>(p, ps, st);
+    if (p.head_dim == 128) return pick_mode<DT_FP8, 128>(p, ps, st);
+    if (p.head_dim == 64) return pick_mode<DT_FP8, 64>(p, ps, st);
   } else if (p.kv_dtype == DT_BF16) {
-    if (p.head_dim == 128) return launch_pf<DT_BF16, 128>(p, ps, st);
-    if (p.head_dim == 64) return launch_pf<DT_BF16, 64>(p, ps, st);
+    if (p.head_dim == 128) return pick_mode<DT_BF16, 128>(p, ps, st);
+    if (p.head_dim == 64) return pick_mode<DT_BF16, 64>(p, ps, st);
+  } else if (p.kv_dtype == DT_F16) {
+    if (p.head_dim == 128) return pick_mode<DT_F16, 128>(p, ps, st);
+    if (p.head_dim == 64) return pick_mode<DT_F16, 64>(p, ps, st);
   }
   return -3;
 }

@@ -43,27 +43,34 @@ def test_bf16_prefill_small():
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("kv", ["fp8", "bf16", "f16"])
 def test_prefill_group_sizes(G, kv):
-    # chunk lengths that end mid-tile and mid-workgroup, a chunk with no cache
+    # chunk lengths that end mid-tile and mid-workgroup, a chunk with no cache; f16 pools
+    # take f16 queries
     Hkv = 2
     wl = W.make_prefill("prefill G=%d %s" % (G, kv), 30 + G, 3, [77, 0, 130], [45, 19, 3], G * Hkv,
-                        Hkv, 128, 16, kv_dtype=kv)
+                        Hkv, 128, 16, kv_dtype=kv, q_dtype="f16" if kv == "f16" else "bf16")
     print(_run(wl, causal=True))
 
 
 @pytest.mark.parametrize("B", [16, 32, 64])
 @pytest.mark.parametrize("D", [64, 128])
-def test_prefill_block_and_head_dim(B, D):
-    wl = W.make_prefill("prefill B=%d D=%d" % (B, D), 40 + B + D, 2, [93, 200], [61, 128], 8, 2, D, B)
+@pytest.mark.parametrize("kv", ["fp8", "f16"])
+def test_prefill_block_and_head_dim(B, D, kv):
+    wl = W.make_prefill("prefill B=%d D=%d %s" % (B, D, kv), 40 + B + D, 2, [93, 200], [61, 128],
+                        8, 2, D, B, kv_dtype=kv, q_dtype="f16" if kv == "f16" else "bf16")
     print(_run(wl, causal=True))
 
 
-def test_prefill_rows_past_the_context_are_zero():
-    # context_lens shorter than the chunk: rows at negative positions see no key
-    wl = W.make_prefill("prefill short ctx", 50, 2, [0, 40], [24, 10], 8, 2, 128, 16)
+@pytest.mark.parametrize("short", [4, 2, 1, 3])
+@pytest.mark.parametrize("G", [4, 2])
+def test_prefill_rows_past_the_context_are_zero(short, G):
+    # context_lens shorter than the chunk: rows at negative positions see no key.  A row
+    # tile holds 16/G tokens; a shortfall that is not a multiple of it puts rows that see
+    # nothing and rows that do in one tile (the first keys must not rescale the others)
+    wl = W.make_prefill("prefill short ctx", 50, 2, [0, 40], [24, 10], 2 * G, 2, 128, 16)
     wl.context_lens = wl.context_lens.copy()
-    wl.context_lens[0] = 20  # chunk of 24 rows, 20 visible positions: rows 0..3 see nothing
+    wl.context_lens[0] = 24 - short  # chunk of 24 rows: rows 0 .. short-1 see nothing
     print(_run(wl, causal=True))
 
 

@@ -1,6 +1,8 @@
 """GPU parity of the shared-prefix decode (pkv_paged_attention_decode_shared) against
 the oracle's paged decode: the same function, computed with the shared blocks read
-once per kv head.
+once per kv head.  The prefix runs on the matrix-core prefill kernel for bf16, f16
+and fp8-block pools with G dividing 16 and blocks of 16 tokens or more, on the decode
+tiles otherwise; the grid below covers both.
 
 "03 | PagedAttention and the KV-cache memory system" §5 (requests that hit the same
 prefix pages point their tables at the same physical blocks); "PagedAttention 的原理是
@@ -57,6 +59,9 @@ def test_shared_prefix_config_small():
     ("int8", 8, 8, 64, 64, 448, 20, "block"),     # MHA, int8, B 64
     ("bf16", 8, 2, 64, 4, 96, 5, "block"),        # B 4: tokens look up their own blocks
     ("f32", 4, 2, 64, 8, 40, 3, "block"),         # f32 pool, prefix of 40 tokens
+    ("fp8", 16, 2, 128, 16, 512, 9, "block"),     # G 8, fp8 block scales
+    ("f16", 8, 4, 64, 64, 640, 13, "block"),      # G 2, B 64, D 64
+    ("f16", 4, 4, 128, 32, 384, 150, "block"),    # MHA, 150 sequences: two ragged row blocks
 ])
 def test_shared_prefix_grid(kv, Hq, Hkv, D, B, prefix, S, mode):
     q_dtype = "bf16" if kv in ("fp8", "int8") else kv
@@ -76,6 +81,22 @@ def test_contexts_shorter_than_the_prefix():
     wl.context_lens[[0, 3, 5, 7, 8]] = [1, 100, 0, 256, 255]
     case = GpuCase(wl)
     print(_check(wl, [256, 128], case=case))
+
+
+def test_prefix_slots_past_every_context_unwritten():
+    """Every context ends inside the shared prefix (the longest at 200 of 256 tokens), and
+    only the prefix tokens below 200 were ever written: the slots from 200 on hold NaN
+    bytes, which no sequence may read."""
+    wl = W.make_decode("unwritten prefix tail", 97, num_seqs=40, Hq=16, Hkv=4, D=128, B=16,
+                       kv_dtype="bf16", shared_prefix=256, tail_range=(0, 30))
+    rng = np.random.default_rng(3)
+    ctx = rng.integers(1, 201, size=wl.num_seqs).astype(np.int32)
+    ctx[5] = 200
+    keep = wl.fill_pos < 200  # the prefix is stored under sequence 0; every tail dropped
+    wl.context_lens = ctx
+    wl.fill_seq, wl.fill_pos = wl.fill_seq[keep], wl.fill_pos[keep]
+    wl.k_src, wl.v_src = wl.k_src[keep], wl.v_src[keep]
+    print(_check(wl, [256, 128]))
 
 
 def test_contexts_inside_an_unaligned_prefix_tile():
