@@ -79,7 +79,11 @@ struct PCfg {
   static constexpr int PT = KVT == DT_BF16 ? DT_BF16 : DT_F16;  // type of the P.V product
   static constexpr bool SPLIT = (PT == DT_BF16);                // P as hi + lo
   // two resident workgroups per CU where the registers allow it (LDS holds two)
-  static constexpr int WPE = (KVT != DT_FP8 && D == 128) ? 1 : 2;
+  static constexpr int WPE = (KVT == DT_BF16 && D == 128) ? 1 : 2;
+  // chunks of pool bytes held in registers: two (loads issued two chunks ahead) where
+  // they are small; one (a chunk ahead) for 16-bit pools of 128 dims, whose 32
+  // registers per chunk would not leave two workgroups per CU
+  static constexpr int NRAW = (EB == 2 && D == 128) ? 1 : 2;
   static constexpr int KP = 64 * NC / kPfThreads;   // K pool pieces per thread per chunk
   static constexpr int VP = D * (64 / TP) / kPfThreads;  // V pool pieces per thread
   static_assert(KP >= 1 && VP >= 1, "chunk too small for the workgroup");
@@ -468,12 +472,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         }
       }
     };
+    constexpr bool kOneRaw = (C::NRAW == 1);
     Raw<C> ra, rb;
     {
       int pg[4];
       win_pages(0, 0, pg);
       chunk_load<KVT, D>(ra, k_pool, v_pool, pg, kbeg, kend, kvh, wave, pm, ps);
-      if (nch > 1) {
+      if (!kOneRaw && nch > 1) {
         win_pages(1, 0, pg);
         chunk_load<KVT, D>(rb, k_pool, v_pool, pg, kbeg + 64, kend, kvh, wave, pm, ps);
       }
@@ -485,15 +490,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    // one chunk: loads of chunk j+2 go to `nxt2`, chunk j+1's pieces (in `nxt1`)
-    // are staged after chunk j is computed
+    // one chunk: loads of chunk j+2 go to `nxt2` (one raw buffer: chunk j+1's to
+    // `nxt1`), chunk j+1's pieces (in `nxt1`) are staged after chunk j is computed
     auto step = [&](int j, Raw<C>& nxt2, Raw<C>& nxt1, uint8_t* cur_buf, uint8_t* nxt_buf) {
       const int base = kbeg + 64 * j;
       const int wk = j / kWinChunks;
-      if (j + 2 < nch) {
+      const int ahead = kOneRaw ? 1 : 2;
+      if (j + ahead < nch) {
         int pg[4];
-        win_pages(j + 2, wk, pg);
-        chunk_load<KVT, D>(nxt2, k_pool, v_pool, pg, base + 128, kend, kvh, wave, pm, ps);
+        win_pages(j + ahead, wk, pg);
+        chunk_load<KVT, D>(kOneRaw ? nxt1 : nxt2, k_pool, v_pool, pg, base + 64 * ahead, kend,
+                           kvh, wave, pm, ps);
       }
       float zs[4];  // per tile: softmax scale x K's page scale, log2 units
       {
@@ -662,10 +669,16 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       }
       __syncthreads();
     };
-    // chunk j's raw pieces live in ra (j even) / rb (j odd) until staged
+    // chunk j's raw pieces live in ra (j even) / rb (j odd) until staged (one raw
+    // buffer: in ra)
     for (int j = 0; j < nch; j += 2) {
-      step(j, ra, rb, lds0, lds1);
-      if (j + 1 < nch) step(j + 1, rb, ra, lds1, lds0);
+      if constexpr (kOneRaw) {
+        step(j, ra, ra, lds0, lds1);
+        if (j + 1 < nch) step(j + 1, ra, ra, lds1, lds0);
+      } else {
+        step(j, ra, rb, lds0, lds1);
+        if (j + 1 < nch) step(j + 1, rb, ra, lds1, lds0);
+      }
     }
   }
 
