@@ -10,6 +10,7 @@
 #include <atomic>
 
 #include "internal.hpp"
+#include "prefill.hpp"
 #include "slot.hpp"
 
 namespace {

@@ -31,6 +31,7 @@
 // scalar load is outstanding when the loop waits on LDS (both share a counter).
 #include "device.hpp"
 #include "internal.hpp"
+#include "prefill.hpp"
 #include "tile.hpp"
 
 #include <math.h>
