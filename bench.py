@@ -693,8 +693,8 @@ def shared_main(a):
         "decode_us": round(dec_us, 2),
         "per_sequence_balanced_decode_us": round(plain_us, 2),
         "roofline": {"bound": "hbm",
-                     "kernel": "shared_prefix_kernel + paged_decode_balanced_kernel (tails) + "
-                               "merge_slots_kernel, one call",
+                     "kernel": "paged_prefill_kernel (prefix mode) + paged_decode_balanced_kernel "
+                               "(tails) + merge_slots_kernel, one call",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(dec_us, 2)},
