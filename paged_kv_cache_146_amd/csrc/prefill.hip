@@ -64,6 +64,7 @@ constexpr int kPfThreads = 256;
 
 template <int KVT, int D>
 struct PCfg {
+  static constexpr int Dim = D;
   static constexpr int EB = Elem<KVT>::bytes;       // pool bytes per element
   static constexpr int X = 16 / EB;                 // K dims per pool piece
   static constexpr int NC = D / X;                  // K pieces per token
@@ -293,6 +294,144 @@ struct RowState {
   f32x4 acc[D / 16];
   float m, l;
 };
+
+// S^T = K . Q^T of every row tile for the chunk staged at kbuf.  K operands
+// (i = T * NKS + ks) are read kPrefetch ahead of their MFMAs, so the LDS latency hides
+// behind the products of the operands before them.
+template <class C>
+__device__ __forceinline__ void chunk_scores(f32x4 (&S)[C::NR][4], const uint8_t* kbuf,
+                                             const int (&k_off)[4], const int (&k_unit)[C::NKS],
+                                             const u32x4 (&qop)[C::NR][C::NKS]) {
+  constexpr int NR = C::NR, NI = 4 * C::NKS;
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto rd = [&](int i) {
+    return *reinterpret_cast<const u32x4*>(kbuf + k_off[i / C::NKS] + k_unit[i % C::NKS]);
+  };
+  u32x4 kop[kPrefetch + 1];
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) kop[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + kPrefetch < NI) kop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
+    const int T = i / C::NKS, ks = i % C::NKS;
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt)
+      S[rt][T] = mma16<C::QT>(kop[i % (kPrefetch + 1)], qop[rt][ks], ks == 0 ? zero : S[rt][T]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 1);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, NR, 1);
+  }
+}
+
+// Online softmax of one chunk (keys base ..) for every row tile: the P operands, the
+// reference and the sum updated, the accumulators rescaled when a reference moves.
+// Keys at or past a row's bound (rlim) exist only where need_mask says so.
+template <class C>
+__device__ __forceinline__ void chunk_softmax(f32x4 (&S)[C::NR][4], RowState<C::Dim> (&st)[C::NR],
+                                              const float (&zs)[4], const int (&rlim)[C::NR],
+                                              int base, int g, bool need_mask,
+                                              u32x4 (&phi)[C::NR][2], u32x4 (&plo)[C::NR][2]) {
+  constexpr int NR = C::NR;
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    // scores in log2 units are S zs (zs > 0: the softmax scale times K's page
+    // scale); masked keys become -inf in place, which the same path turns into 0
+    if (need_mask) {
+      const int lim = rlim[rt] - base - 4 * g;  // keys 16 T + r below lim are visible
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[rt][T][r] = 16 * T + r < lim ? S[rt][T][r] : -INFINITY;
+    }
+    float tm[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      tm[T] = fmax4(S[rt][T][0], S[rt][T][1], S[rt][T][2], S[rt][T][3]) * zs[T];
+    float cm = max_groups(fmax4(tm[0], tm[1], tm[2], tm[3]));
+    // The reference max moves only when a chunk's max passes it by more than
+    // kLazyMax, so the accumulators are rescaled rarely (the softmax does not
+    // depend on the reference); p then stays below 2^kLazyMax.
+    const bool moves = cm > st[rt].m + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(moves) != 0) {
+      // 0 for a row's first keys; 1 for a row that does not move (which may not have
+      // seen a key yet: m = -inf, where m - m would be NaN)
+      const float mn = moves ? cm : st[rt].m;
+      const float alpha = moves ? __builtin_amdgcn_exp2f(st[rt].m - mn) : 1.0f;
+      st[rt].m = mn;
+      st[rt].l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
+    }
+    const float mref = st[rt].m == -INFINITY ? 0.0f : st[rt].m;  // rows that have seen no key yet
+    float p[16];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
+    float psum = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
+        const float a = p[i0], b = p[i0 + 1];
+        wh[wd] = pack2<C::PT>(a, b);
+        if constexpr (C::SPLIT) {
+          const f32x2 h = unpack2<C::PT>(wh[wd]);
+          wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
+          psum += a + b;
+        } else {
+          // fp8 and f16 pools: P is f16(p) (fp8: V carries its page scale); the row sum
+          // adds the same rounded values (exact f16 products, fp32 sum)
+          wl[wd] = 0u;
+          psum = __builtin_amdgcn_fdot2(as_f16x2(wh[wd]), f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                        psum, false);
+        }
+      }
+      phi[rt][s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+      plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+    }
+    st[rt].l += psum;
+  }
+}
+
+// O^T += V^T . P^T of every row tile for the chunk staged at vbuf.  V operands
+// (i = 2 dt + s2) are read kPrefetch ahead as the K operands above.
+template <class C>
+__device__ __forceinline__ void chunk_pv(RowState<C::Dim> (&st)[C::NR], const uint8_t* vbuf,
+                                         int v_off, const int (&v_unit)[2],
+                                         const u32x4 (&phi)[C::NR][2],
+                                         const u32x4 (&plo)[C::NR][2]) {
+  constexpr int NR = C::NR, NI = 2 * C::NDT;
+  constexpr int MPI = NR * (C::SPLIT ? 2 : 1);  // MFMAs per operand
+  auto rd = [&](int i) {
+    return *reinterpret_cast<const u32x4*>(vbuf + v_off + (i / 2) * 16 * C::VROW + v_unit[i % 2]);
+  };
+  u32x4 vop[kPrefetch + 1];
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) vop[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + kPrefetch < NI) vop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
+    const int dt = i / 2, s2 = i % 2;
+    const u32x4 a = vop[i % (kPrefetch + 1)];
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+      st[rt].acc[dt] = mma16<C::PT>(a, phi[rt][s2], st[rt].acc[dt]);
+      if constexpr (C::SPLIT) st[rt].acc[dt] = mma16<C::PT>(a, plo[rt][s2], st[rt].acc[dt]);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 2);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, MPI, 2);
+  }
+}
 
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
@@ -525,99 +664,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       // the one with MFMAs ready issues first while the other works on its softmax.
       __builtin_amdgcn_s_setprio(2);
       f32x4 S[NR][4];
-      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      // K operands (i = T * NKS + ks) are read kPrefetch ahead of their MFMAs, so the
-      // LDS latency hides behind the products of the operands before them
-      {
-        constexpr int NI = 4 * C::NKS;
-        auto rd = [&](int i) {
-          return *reinterpret_cast<const u32x4*>(kbuf + k_off[i / C::NKS] + k_unit[i % C::NKS]);
-        };
-        u32x4 kop[kPrefetch + 1];
-#pragma unroll
-        for (int i = 0; i < kPrefetch; ++i) kop[i] = rd(i);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + kPrefetch < NI) kop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
-          const int T = i / C::NKS, ks = i % C::NKS;
-#pragma unroll
-          for (int rt = 0; rt < NR; ++rt)
-            S[rt][T] = mma16<C::QT>(kop[i % (kPrefetch + 1)], qop[rt][ks], ks == 0 ? zero : S[rt][T]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 1);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x008, NR, 1);
-        }
-      }
+      chunk_scores<C>(S, kbuf, k_off, k_unit, qop);
       __builtin_amdgcn_s_setprio(0);
-      // ---- online softmax per row tile; P operands.  Keys at or past a row's bound
-      // exist only in chunks that reach the wave's smallest bound.
-      const bool need_mask = base + 64 > wave_min_lim;
+      // ---- online softmax per row tile; P operands
       u32x4 phi[NR][2], plo[NR][2];
-#pragma unroll
-      for (int rt = 0; rt < NR; ++rt) {
-        // scores in log2 units are S zs (zs > 0: the softmax scale times K's page
-        // scale); masked keys become -inf in place, which the same path turns into 0
-        if (need_mask) {
-          const int lim = rlim[rt] - base - 4 * g;  // keys 16 T + r below lim are visible
-#pragma unroll
-          for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[rt][T][r] = 16 * T + r < lim ? S[rt][T][r] : -INFINITY;
-        }
-        float tm[4];
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-          tm[T] = fmax4(S[rt][T][0], S[rt][T][1], S[rt][T][2], S[rt][T][3]) * zs[T];
-        float cm = max_groups(fmax4(tm[0], tm[1], tm[2], tm[3]));
-        // The reference max moves only when a chunk's max passes it by more than
-        // kLazyMax, so the accumulators are rescaled rarely (the softmax does not
-        // depend on the reference); p then stays below 2^kLazyMax.
-        const bool moves = cm > st[rt].m + kLazyMax;
-        if (__builtin_amdgcn_ballot_w64(moves) != 0) {
-          // 0 for a row's first keys; 1 for a row that does not move (which may not have
-          // seen a key yet: m = -inf, where m - m would be NaN)
-          const float mn = moves ? cm : st[rt].m;
-          const float alpha = moves ? __builtin_amdgcn_exp2f(st[rt].m - mn) : 1.0f;
-          st[rt].m = mn;
-          st[rt].l *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
-        }
-        const float mref = st[rt].m == -INFINITY ? 0.0f : st[rt].m;  // rows that have seen no key yet
-        float p[16];
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
-        float psum = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          uint32_t wh[4], wl[4];
-#pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
-            const float a = p[i0], b = p[i0 + 1];
-            wh[wd] = pack2<C::PT>(a, b);
-            if constexpr (C::SPLIT) {
-              const f32x2 h = unpack2<C::PT>(wh[wd]);
-              wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
-              psum += a + b;
-            } else {
-              // fp8 pools: V carries its page scale, P is f16(p); the row sum adds the
-              // same rounded values (exact f16 products, fp32 sum)
-              wl[wd] = 0u;
-              psum = __builtin_amdgcn_fdot2(as_f16x2(wh[wd]), f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                            psum, false);
-            }
-          }
-          phi[rt][s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
-          plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
-        }
-        st[rt].l += psum;
-      }
+      chunk_softmax<C>(S, st, zs, rlim, base, g, base + 64 > wave_min_lim, phi, plo);
       // ---- stage chunk j+1 into the other buffer (free since the last barrier)
       // while the matrix cores run O^T += V^T . P^T: the conversions and LDS writes
       // fill the issue slots between the MFMAs
@@ -627,35 +678,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
         chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
       }
       __builtin_amdgcn_s_setprio(2);
-      {
-        // V operands (i = 2 dt + s2), read kPrefetch ahead as the K operands above
-        constexpr int NI = 2 * C::NDT;
-        constexpr int MPI = NR * (C::SPLIT ? 2 : 1);  // MFMAs per operand
-        auto rd = [&](int i) {
-          return *reinterpret_cast<const u32x4*>(vbuf + v_off + (i / 2) * 16 * C::VROW +
-                                                 v_unit[i % 2]);
-        };
-        u32x4 vop[kPrefetch + 1];
-#pragma unroll
-        for (int i = 0; i < kPrefetch; ++i) vop[i] = rd(i);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + kPrefetch < NI) vop[(i + kPrefetch) % (kPrefetch + 1)] = rd(i + kPrefetch);
-          const int dt = i / 2, s2 = i % 2;
-          const u32x4 a = vop[i % (kPrefetch + 1)];
-#pragma unroll
-          for (int rt = 0; rt < NR; ++rt) {
-            st[rt].acc[dt] = mma16<C::PT>(a, phi[rt][s2], st[rt].acc[dt]);
-            if constexpr (C::SPLIT) st[rt].acc[dt] = mma16<C::PT>(a, plo[rt][s2], st[rt].acc[dt]);
-          }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 2);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          if (i + kPrefetch < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
-          __builtin_amdgcn_sched_group_barrier(0x008, MPI, 2);
-        }
-      }
+      chunk_pv<C>(st, vbuf, v_off, v_unit, phi, plo);
       __builtin_amdgcn_s_setprio(0);
       } else if (j + 1 < nch) {  // no key of this chunk for the wave: only the staging
         float vsc[C::VP];
