@@ -5,10 +5,12 @@
 // query row i of an n-token chunk sits at position a = ctx - n + i and sees the
 // keys 0..a (the whole cache, causal inside the chunk).
 //
-// Work cut: one workgroup (4 waves) per (query block, kv head, sequence).  A
-// "row" is a (query token, query head) pair; a 16-row tile holds 16/G tokens x
-// the G heads of the kv head, so every K/V tile is reused by all G heads.  Each
-// wave owns two row tiles, the workgroup 128/G tokens.  The query blocks of one
+// Work cut: one workgroup (4 waves; 8 for fp8 pools of 128 dims) per (query block,
+// kv head, sequence).  A "row" is a (query token, query head) pair; a 16-row tile
+// holds 16/G tokens x the G heads of the kv head, so every K/V tile is reused by all
+// G heads.  Each wave owns two row tiles, the workgroup 128/G tokens (256/G with 8
+// waves, which share each staged chunk: half the staging per wave and half the
+// pool reads per query, at the same two waves per SIMD).  The query blocks of one
 // (sequence, kv head) pair run on one XCD, so their shared K/V hits in its L2.
 //
 // Per 64-key chunk the workgroup stages K and V once into LDS, widened to 16
@@ -62,9 +64,11 @@ constexpr int kXcds = 8;
 
 constexpr int kPfThreads = 256;
 
-template <int KVT, int D>
+template <int KVT, int D, int NT_ = kPfThreads>
 struct PCfg {
+  static constexpr int KV = KVT;                    // pool element type
   static constexpr int Dim = D;
+  static constexpr int NT = NT_;                    // threads per workgroup
   static constexpr int EB = Elem<KVT>::bytes;       // pool bytes per element
   static constexpr int X = 16 / EB;                 // K dims per pool piece
   static constexpr int NC = D / X;                  // K pieces per token
@@ -86,8 +90,8 @@ struct PCfg {
   // they are small; one (a chunk ahead) for 16-bit pools of 128 dims, whose 32
   // registers per chunk would not leave two workgroups per CU
   static constexpr int NRAW = (EB == 2 && D == 128) ? 1 : 2;
-  static constexpr int KP = 64 * NC / kPfThreads;   // K pool pieces per thread per chunk
-  static constexpr int VP = D * (64 / TP) / kPfThreads;  // V pool pieces per thread
+  static constexpr int KP = 64 * NC / NT;           // K pool pieces per thread per chunk
+  static constexpr int VP = D * (64 / TP) / NT;     // V pool pieces per thread
   static_assert(KP >= 1 && VP >= 1, "chunk too small for the workgroup");
 };
 
@@ -106,15 +110,14 @@ __device__ __forceinline__ int pick4(const int (&v)[4], int i) {
 // tile per piece index, so the page is wave-uniform: its base address is scalar
 // and each lane adds an offset that is the same for every chunk (recomputed only
 // in a chunk that runs past the context, whose tokens are clamped).
-//   K piece i of thread (w, l): token 16 w + l % 16, dims [c X, c X + X) with
-//     c = l / 16 + 4 i (tile w).
-//   V piece i: vp = 256 i + 64 w + l covers tokens [TP p, TP p + TP) of dim
+//   K piece i of thread (w, l): token 16 (w % 4) + l % 16, dims [c X, c X + X) with
+//     c = l / 16 + 4 (w / 4) + 4 (NT / 256) i (tile w % 4; NT threads per workgroup).
+//   V piece i: vp = NT i + 64 w + l covers tokens [TP p, TP p + TP) of dim
 //     vp % D, p = vp / D (tile TP p / 16, the same for the whole wavefront as
 //     64 divides D).  A V page is [B/TP][D][TP] (block_size >= 16 >= TP), so the
 //     piece of tokens [t, t + TP) of dim d is the 16 bytes at (t/TP * D + d) * 16.
-template <int KVT, int D>
+template <class C>
 struct PieceMap {
-  using C = PCfg<KVT, D>;
   int k_tok;               // chunk-relative token of this lane's K pieces
   int k_c[C::KP];          // K piece index c
   int v_p[C::VP], v_d[C::VP];
@@ -123,33 +126,35 @@ struct PieceMap {
 
   __device__ __forceinline__ PieceMap(int wave, int lane, int blog2) {
     const int B = 1 << blog2;
-    k_tok = 16 * wave + (lane & 15);
+    const int tile = C::NT == 256 ? wave : (wave & 3), half = C::NT == 256 ? 0 : (wave >> 2);
+    k_tok = 16 * tile + (lane & 15);
 #pragma unroll
     for (int i = 0; i < C::KP; ++i) {
-      k_c[i] = (lane >> 4) + 4 * i;
+      k_c[i] = (lane >> 4) + 4 * half + 4 * (C::NT / 256) * i;
       k_off[i] = (uint32_t)((k_c[i] * B + (k_tok & (B - 1))) * 16);
     }
 #pragma unroll
     for (int i = 0; i < C::VP; ++i) {
-      const int vp = kPfThreads * i + 64 * wave + lane;
-      v_p[i] = vp / D;
-      v_d[i] = vp % D;
-      v_off[i] = (uint32_t)(((((v_p[i] * C::TP) & (B - 1)) / C::TP) * D + v_d[i]) * 16);
+      const int vp = C::NT * i + 64 * wave + lane;
+      v_p[i] = vp / C::Dim;
+      v_d[i] = vp % C::Dim;
+      v_off[i] = (uint32_t)(((((v_p[i] * C::TP) & (B - 1)) / C::TP) * C::Dim + v_d[i]) * 16);
     }
   }
 };
 
 // Issue the pool loads of the chunk at `base` (tokens clamped below `end`).
-template <int KVT, int D>
-__device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* __restrict__ k_pool,
+template <class C>
+__device__ __forceinline__ void chunk_load(Raw<C>& r, const uint8_t* __restrict__ k_pool,
                                            const uint8_t* __restrict__ v_pool, const int (&pg)[4],
                                            int base, int end, int kvh, int wave,
-                                           const PieceMap<KVT, D>& pm, const PrefillScalars& ps) {
-  using C = PCfg<KVT, D>;
+                                           const PieceMap<C>& pm, const PrefillScalars& ps) {
+  constexpr int D = C::Dim;
   const int B = 1 << ps.blog2;
   const bool full = base + 64 <= end;  // uniform
   {
-    const uint8_t* pb = k_pool + ((size_t)pick4(pg, wave) * (size_t)ps.bstride +
+    const uint8_t* pb = k_pool + ((size_t)pick4(pg, C::NT == 256 ? wave : (wave & 3)) *
+                                      (size_t)ps.bstride +
                                   (size_t)kvh * C::NC * B) * 16;
 #pragma unroll
     for (int i = 0; i < C::KP; ++i) {
@@ -176,10 +181,10 @@ __device__ __forceinline__ void chunk_load(Raw<PCfg<KVT, D>>& r, const uint8_t* 
 }
 
 // Widen K piece i of the thread to 16 bits and write it into a K buffer.
-template <int KVT, int D>
-__device__ __forceinline__ void stage_k_piece(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
-                                              const PieceMap<KVT, D>& pm, int i) {
-  using C = PCfg<KVT, D>;
+template <class C>
+__device__ __forceinline__ void stage_k_piece(const Raw<C>& r, uint8_t* kbuf,
+                                              const PieceMap<C>& pm, int i) {
+  constexpr int KVT = C::KV;
   const int c = pm.k_c[i], tok = pm.k_tok;
   uint8_t* row = kbuf + tok * C::KROW;
   if constexpr (KVT == DT_FP8) {
@@ -194,21 +199,19 @@ __device__ __forceinline__ void stage_k_piece(const Raw<PCfg<KVT, D>>& r, uint8_
 }
 
 // Widen the thread's K pieces to 16 bits and write them into a K buffer.
-template <int KVT, int D>
-__device__ __forceinline__ void stage_k(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
-                                        const PieceMap<KVT, D>& pm) {
+template <class C>
+__device__ __forceinline__ void stage_k(const Raw<C>& r, uint8_t* kbuf, const PieceMap<C>& pm) {
 #pragma unroll
-  for (int i = 0; i < PCfg<KVT, D>::KP; ++i) stage_k_piece<KVT, D>(r, kbuf, pm, i);
+  for (int i = 0; i < C::KP; ++i) stage_k_piece<C>(r, kbuf, pm, i);
 }
 
 // Widen V piece i of the thread to 16 bits and write it into a V buffer.  MASK: the
 // tokens at or past `end` (chunk at `base`) become zero, as their slots may hold
 // anything; only the chunk that reaches `end` needs it.
-template <int KVT, int D, bool MASK>
-__device__ __forceinline__ void stage_v_piece(const Raw<PCfg<KVT, D>>& r, uint8_t* vbuf, int base,
-                                              int end, const PieceMap<KVT, D>& pm, int i,
-                                              float vsc) {
-  using C = PCfg<KVT, D>;
+template <class C, bool MASK>
+__device__ __forceinline__ void stage_v_piece(const Raw<C>& r, uint8_t* vbuf, int base, int end,
+                                              const PieceMap<C>& pm, int i, float vsc) {
+  constexpr int KVT = C::KV;
   const int p = pm.v_p[i], d = pm.v_d[i];
   const int t0 = p * C::TP;
   uint8_t* row = vbuf + d * C::VROW;
@@ -252,27 +255,24 @@ __device__ __forceinline__ void stage_v_piece(const Raw<PCfg<KVT, D>>& r, uint8_
 
 // Widen the thread's V pieces to 16 bits and write them into a V buffer (MASK as above);
 // fp8: piece i is scaled by vsc[i], the V scale of its page.
-template <int KVT, int D, bool MASK>
-__device__ __forceinline__ void stage_v(const Raw<PCfg<KVT, D>>& r, uint8_t* vbuf, int base,
-                                        int end, const PieceMap<KVT, D>& pm,
-                                        const float (&vsc)[PCfg<KVT, D>::VP]) {
+template <class C, bool MASK>
+__device__ __forceinline__ void stage_v(const Raw<C>& r, uint8_t* vbuf, int base, int end,
+                                        const PieceMap<C>& pm, const float (&vsc)[C::VP]) {
 #pragma unroll
-  for (int i = 0; i < PCfg<KVT, D>::VP; ++i)
-    stage_v_piece<KVT, D, MASK>(r, vbuf, base, end, pm, i, vsc[i]);
+  for (int i = 0; i < C::VP; ++i) stage_v_piece<C, MASK>(r, vbuf, base, end, pm, i, vsc[i]);
 }
 
 // Both halves; V tokens at or past `end` become zero.  Only the chunk that reaches
 // `end` has such tokens: the check sits behind a wave-uniform branch.
-template <int KVT, int D>
-__device__ __forceinline__ void chunk_stage(const Raw<PCfg<KVT, D>>& r, uint8_t* kbuf,
-                                            uint8_t* vbuf, int base, int end,
-                                            const PieceMap<KVT, D>& pm,
-                                            const float (&vsc)[PCfg<KVT, D>::VP]) {
-  stage_k<KVT, D>(r, kbuf, pm);
+template <class C>
+__device__ __forceinline__ void chunk_stage(const Raw<C>& r, uint8_t* kbuf, uint8_t* vbuf,
+                                            int base, int end, const PieceMap<C>& pm,
+                                            const float (&vsc)[C::VP]) {
+  stage_k<C>(r, kbuf, pm);
   if (uniform(base + 64 > end ? 1 : 0) != 0)
-    stage_v<KVT, D, true>(r, vbuf, base, end, pm, vsc);
+    stage_v<C, true>(r, vbuf, base, end, pm, vsc);
   else
-    stage_v<KVT, D, false>(r, vbuf, base, end, pm, vsc);
+    stage_v<C, false>(r, vbuf, base, end, pm, vsc);
 }
 
 // Headroom of the lazily moved softmax reference, in log2 units: p <= 2^kLazyMax.
@@ -452,15 +452,15 @@ __device__ __forceinline__ int wave_max_i(int x) {
 // row (normalised output, reference max in natural-log units, sum) goes to partial
 // slot `slice`, which a log-sum-exp merge combines with the other slices and the
 // sequence's private tail.
-template <int KVT, int D, bool PREFIX = false>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
+template <int KVT, int D, bool PREFIX = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     PCfg<KVT, D>::WPE, PCfg<KVT, D>::WPE))) void paged_prefill_kernel(const uint8_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
                      const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                      const float* __restrict__ k_scale, const float* __restrict__ v_scale,
                      const int32_t* __restrict__ block_table,
                      const int32_t* __restrict__ context_lens, uint8_t* __restrict__ out,
                      const PrefillScalars ps) {
-  using C = PCfg<KVT, D>;
+  using C = PCfg<KVT, D, 64 * NW>;
   constexpr bool kFp8 = (KVT == DT_FP8);
   constexpr int NR = C::NR;
   // two chunk buffers as separate arrays, so that the staging writes into one are
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
   const int G = ps.G, tpr = 16 / G;           // tokens (prefix: sequences) per row tile
-  const int tpw = NR * tpr, tpg = 4 * tpw;    // per wave / per workgroup
+  const int tpw = NR * tpr, tpg = NW * tpw;   // per wave / per workgroup
   const int tok0 = qb * tpg;
 
   // the workgroup's rows and keys [kbeg, kend); row t of the pair is token q0 + t
@@ -553,10 +553,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
   if constexpr (PREFIX) {
     // keys past every row's bound are never read: they need not have been written
     // (a prefix token lies in the context of some sequence that sees it)
-    __shared__ int wg_lim[4];
+    __shared__ int wg_lim[NW];
     if (lane == 0) wg_lim[wave] = wave_max_lim;
     __syncthreads();
-    kend = min(kend, max(max(wg_lim[0], wg_lim[1]), max(wg_lim[2], wg_lim[3])));
+    int wl = wg_lim[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) wl = max(wl, wg_lim[w]);
+    kend = min(kend, wl);
   }
   // this lane's LDS offsets (swizzled 16-byte units), the same for every chunk
   int k_off[4], k_unit[C::NKS], v_off, v_unit[2];
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     auto fill_window = [&](int wk) {
       const int blk0 = (kbeg + wk * kWinChunks * 64) >> ps.blog2;
       const int last = (kend - 1) >> ps.blog2;
-      for (int t = threadIdx.x; t < kWinBlocks; t += kPfThreads) {
+      for (int t = threadIdx.x; t < kWinBlocks; t += 64 * NW) {
         const int e = clamp_block(trow[min(blk0 + t, last)], ps.num_blocks);
         w_blk[t] = e;
         if constexpr (kFp8) {
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     };
     fill_window(0);
     __syncthreads();
-    const PieceMap<KVT, D> pm(wave, lane, ps.blog2);
+    const PieceMap<C> pm(wave, lane, ps.blog2);
     // V scales of the thread's pieces of the chunk at `base` from window wk (fp8; a
     // piece's 16 tokens sit in one tile, the same for the whole wavefront)
     auto piece_scales = [&](int base, int wk, float (&vsc)[C::VP]) {
@@ -617,16 +620,16 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
     {
       int pg[4];
       win_pages(0, 0, pg);
-      chunk_load<KVT, D>(ra, k_pool, v_pool, pg, kbeg, kend, kvh, wave, pm, ps);
+      chunk_load<C>(ra, k_pool, v_pool, pg, kbeg, kend, kvh, wave, pm, ps);
       if (!kOneRaw && nch > 1) {
         win_pages(1, 0, pg);
-        chunk_load<KVT, D>(rb, k_pool, v_pool, pg, kbeg + 64, kend, kvh, wave, pm, ps);
+        chunk_load<C>(rb, k_pool, v_pool, pg, kbeg + 64, kend, kvh, wave, pm, ps);
       }
     }
     {
       float vsc[C::VP];
       piece_scales(kbeg, 0, vsc);
-      chunk_stage<KVT, D>(ra, lds0, lds0 + C::KBUF, kbeg, kend, pm, vsc);
+      chunk_stage<C>(ra, lds0, lds0 + C::KBUF, kbeg, kend, pm, vsc);
     }
     __syncthreads();
 
@@ -639,7 +642,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       if (j + ahead < nch) {
         int pg[4];
         win_pages(j + ahead, wk, pg);
-        chunk_load<KVT, D>(kOneRaw ? nxt1 : nxt2, k_pool, v_pool, pg, base + 64 * ahead, kend,
+        chunk_load<C>(kOneRaw ? nxt1 : nxt2, k_pool, v_pool, pg, base + 64 * ahead, kend,
                            kvh, wave, pm, ps);
       }
       float zs[4];  // per tile: softmax scale x K's page scale, log2 units
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       if (j + 1 < nch) {
         float vsc[C::VP];
         piece_scales(base + 64, wk, vsc);
-        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
+        chunk_stage<C>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
       }
       __builtin_amdgcn_s_setprio(2);
       chunk_pv<C>(st, vbuf, v_off, v_unit, phi, plo);
@@ -683,7 +686,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(
       } else if (j + 1 < nch) {  // no key of this chunk for the wave: only the staging
         float vsc[C::VP];
         piece_scales(base + 64, wk, vsc);
-        chunk_stage<KVT, D>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
+        chunk_stage<C>(nxt1, nxt_buf, nxt_buf + C::KBUF, base + 64, kend, pm, vsc);
       }
       issue_point();
       // ---- advance the page window
@@ -741,7 +744,10 @@ int log2_exact(int x) {
 
 template <int KVT, int D, bool PREFIX>
 int launch_pf(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) {
-  const int tpg = 4 * PCfg<KVT, D>::NR * (16 / ps.G);
+  // fp8 pools of 128 dims: one 8-wave workgroup per CU staging each chunk for 256/G
+  // tokens (two waves per SIMD, as two 4-wave workgroups would be)
+  constexpr int NW = (!PREFIX && KVT == DT_FP8 && D == 128) ? 8 : 4;
+  const int tpg = NW * PCfg<KVT, D>::NR * (16 / ps.G);
   PrefillScalars q = ps;
   const long long rows = PREFIX ? p.num_seqs : p.max_q_len;  // per pair
   q.nqb = (int)((rows + tpg - 1) / tpg);
@@ -752,7 +758,7 @@ int launch_pf(const PrefillLaunch& p, const PrefillScalars& ps, hipStream_t st) 
   if (blocks > 0x7fffffffLL) return -3;
   q.pairs = (int)pairs;
   dim3 grid((unsigned)blocks);
-  hipLaunchKernelGGL((paged_prefill_kernel<KVT, D, PREFIX>), grid, dim3(kPfThreads), 0, st,
+  hipLaunchKernelGGL((paged_prefill_kernel<KVT, D, PREFIX, NW>), grid, dim3(64 * NW), 0, st,
                      (const uint8_t*)p.q, p.cu_seqlens_q, (const uint8_t*)p.k_pool,
                      (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
                      p.context_lens, (uint8_t*)p.out, q);
