@@ -261,7 +261,9 @@ int pkv_decode_partition_size(const int32_t* context_lens, int32_t num_seqs,
  * must already have been written (context_lens counts it).
  *   q: device [num_seqs][num_q_heads][head_dim] of q_dtype;
  *      (pool f32, q f32), (f16, f16), (bf16, bf16), (fp8 or int8, bf16|f16)
- *      supported, each scale mode for the quantised pools.
+ *      supported, each scale mode for the quantised pools.  Quantised pools:
+ *      the softmax weights (at most 1) times V's scale enter the P.V product
+ *      as f16 values, so v_scale must stay below 65504.
  *   k_pool, v_pool: device, layout above; k_scale, v_scale: quantised pools
  *      only, else NULL.  Scales of slots past a sequence's context are never
  *      used (in token mode they may hold anything, NaN included).

@@ -31,10 +31,14 @@
 // the lane.  With block_size >= 16 the 16 tokens of a tile share one block, so
 // the table entries of a chunk are wave-uniform (scalar loads).
 //
-// fp8 (OCP E4M3) and int8 pages are widened exactly to the query's 16-bit type
-// before the product; K's scale (per page, per pool or per token) multiplies the
-// scores and V's is folded into P.  P enters the second product as a hi + lo pair of the 16-bit type.  f32
-// pools use the 16x16x4 f32 product with one k-slot per lane.
+// fp8 (OCP E4M3) and int8 pages are widened exactly to the query's 16-bit type for
+// S^T and to f16 for P.V; K's scale (per page, per pool or per token) multiplies the
+// scores and V's is folded into P, which enters P.V as one f16 term (p <= 1 against
+// the running max).  With a 16-bit pool P enters as a hi + lo pair of that type.
+// The 8-bit V pages are loaded by rows: lane group g takes the whole 16-token row of
+// tile g for its dims (one 16-byte load per dim tile), and a 4 x 4 transpose across
+// the lane groups (permlane swaps) hands each lane its four tokens of every tile.
+// f32 pools use the 16x16x4 f32 product with one k-slot per lane.
 //
 // Three ways to cut the work:
 //   unsplit / fixed partitions — one workgroup (4 waves) per (kv head,
@@ -267,6 +271,23 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
                                         int kvh, const DecodeScalars& sc, int n, int g) {
   using VP = typename C::VPiece;
   const int B = 1 << sc.blog2;
+  if constexpr (C::EB == 1) {
+    // 8-bit pools: lane group g loads tile g's whole 16-token row of each dim (one
+    // 16-byte load per dim tile instead of four 4-byte ones); v_rows_to_tiles then
+    // hands each lane its four tokens of every tile
+    const int bg = g == 0 ? pg.b[0] : (g == 1 ? pg.b[1] : (g == 2 ? pg.b[2] : pg.b[3]));
+    const int t = (pg.off + 16 * g) & (B - 1);  // the group's tile: 16 tokens, one row
+    const uint8_t* vp = v_pool + block_k16(sc, bg) * 16 +
+                        ((size_t)kvh * C::Dim * B + ((size_t)(t / 16) * C::Dim + n) * 16);
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const u32x4* a = reinterpret_cast<const u32x4*>(vp + (size_t)16 * dt * 16);
+      const u32x4 w = STREAM ? __builtin_nontemporal_load(a) : *a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vr[dt * 4 + r] = w[r];
+    }
+    return;
+  }
   // V page [B/E][D][E] (block_size >= 16 >= E): token t of dim d at (t/E * D + d) E + t%E
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
@@ -281,6 +302,34 @@ __device__ __forceinline__ void issue_v(typename C::VPiece (&vr)[C::NV],
         vr[dt * 4 + T] = __builtin_nontemporal_load(a);
       else
         vr[dt * 4 + T] = *a;
+    }
+  }
+}
+
+// 8-bit pools loaded by rows (issue_v): lane group g holds, for each dim tile, the
+// four 4-token words of tile g; a 4 x 4 transpose across the lane groups (two
+// permlane32 and two permlane16 swaps per dim tile) leaves word T = tokens
+// 16 T + 4 g + (0..3), the layout the P.V products take
+template <class C>
+__device__ __forceinline__ void v_rows_to_tiles(typename C::VPiece (&vr)[C::NV]) {
+  if constexpr (C::EB == 1) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      uint32_t* w = &vr[dt * 4];
+      // across lane-group halves (g and g ^ 2): words 0/2 and 1/3
+      auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+      w[0] = a[0];
+      w[2] = a[1];
+      auto b = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+      w[1] = b[0];
+      w[3] = b[1];
+      // within each half (g and g ^ 1): words 0/1 and 2/3
+      auto c = __builtin_amdgcn_permlane16_swap(w[0], w[1], false, false);
+      w[0] = c[0];
+      w[1] = c[1];
+      auto d = __builtin_amdgcn_permlane16_swap(w[2], w[3], false, false);
+      w[2] = d[0];
+      w[3] = d[1];
     }
   }
 }
@@ -525,6 +574,28 @@ __device__ __forceinline__ void chunk_softmax_pv(State<C>& st, const f32x4 (&S)[
 #pragma unroll
         for (int r = 0; r < 4; ++r) st.acc[dt] = mma_f32(as_f32(piece[r]), p[4 * T + r], st.acc[dt]);
       }  // the f32 pool: VPiece is u32x4
+  } else if constexpr (kFp8) {
+    // 8-bit pools: the codes widen exactly to f16, and P (times V's scale, p <= 1)
+    // enters P.V as one f16 term: 11 significant bits, one product per operand
+    u32x4 pv[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int i0 = 8 * s2 + 2 * wd;
+        w[wd] = pack2<DT_F16>(p[i0] * vs[i0], p[i0 + 1] * vs[i0 + 1]);
+      }
+      pv[s2] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        // slots 0-3: tokens 32 s2 + 4 g + (0..3) (tile 2 s2); 4-7: tile 2 s2 + 1
+        const u32x4 a = widen8<KVT, DT_F16>(vr[dt * 4 + 2 * s2], vr[dt * 4 + 2 * s2 + 1]);
+        st.acc[dt] = mma16<DT_F16>(a, pv[s2], st.acc[dt]);
+      }
   } else {
     // P = hi + lo, both in CT: the pair carries about twice CT's significand, so
     // the weights reach the product essentially unrounded (a single 16-bit P
@@ -841,6 +912,7 @@ paged_decode_kernel(
       issue_point();
       if constexpr (FUSE)
         if (patch_now) patch_v<C>(R.v, new_lds, r_new, n, g);
+      v_rows_to_tiles<C>(R.v);
       chunk_softmax_pv<C, KVT, CT>(st, S, R.v, sc.scale_log2, ks0, vs0, min(64, t_end - b0),
                                    g, 64, lo - b0);
       issue_point();
@@ -1378,6 +1450,7 @@ paged_decode_balanced_kernel(
       const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
       if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
       issue_point();
+      v_rows_to_tiles<C>(cur.v);
       chunk_softmax_pv<C, KVT, CT>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
                                    min(64, p0.ctx - base0), g, 64, p0.lo - base0);
       issue_point();
@@ -1624,6 +1697,7 @@ __global__ __launch_bounds__(kThreads) void shared_prefix_kernel(
         p2 = pages_of(trow, base_of(i + 2), t_end, sc);
       }
       issue_point();
+      v_rows_to_tiles<C>(R.v);
       chunk_softmax_pv<C, KVT, CT, true>(st, S, R.v, sc.scale_log2, ks0, vs0,
                                          min(64, t_end - b0), g, lim - b0);
       issue_point();

@@ -84,7 +84,8 @@ __device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
 
 // eight int8 codes (two words) -> eight CT values; exact, as every int8 value is
 // an integer of at most 8 bits.  f16: each byte, sign bit flipped (u = x + 128),
-// becomes the f16 1024 + u by its bits, and a packed subtraction of 1152 leaves x.
+// becomes the f16 1024 + u by its bits (one byte permute places two of them under
+// the exponent byte 0x64), and a packed subtraction of 1152 leaves x.
 // bf16: each byte sign-extended and converted to f32 (one instruction per code:
 // the conversion reads the byte in place), then a conversion that is exact.
 template <int CT>
@@ -97,8 +98,11 @@ __device__ __forceinline__ u32x4 i8x8(uint32_t w0, uint32_t w1) {
     for (int hp = 0; hp < 2; ++hp) {  // bytes 2 hp, 2 hp + 1
       if constexpr (CT == DT_F16) {
         const uint32_t x = w[i] ^ 0x80808080u;
-        const uint32_t u0 = (x >> (16 * hp)) & 0xffu, u1 = (x >> (16 * hp + 8)) & 0xffu;
-        const f16x2 h = __builtin_bit_cast(f16x2, 0x64006400u | u0 | (u1 << 16));
+        // bytes [u(2 hp), 0x64, u(2 hp + 1), 0x64]: selector values 0-3 take x's
+        // bytes, 4 takes a byte of the 0x64 word
+        const uint32_t bits =
+            __builtin_amdgcn_perm(0x64646464u, x, hp == 0 ? 0x04010400u : 0x04030402u);
+        const f16x2 h = __builtin_bit_cast(f16x2, bits);
         r[2 * i + hp] = __builtin_bit_cast(uint32_t, h - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
       } else {
         static_assert(CT == DT_BF16, "int8 widens to f16 or bf16");
