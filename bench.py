@@ -4,7 +4,8 @@ Workload: 64 sequences, context lengths U[128, 4096] (seed 2), H_q 32, H_kv 8,
 D 128, bf16 KV, block size 16, pool = needed blocks + 20% spare with shuffled
 block tables.  A step is the whole hot path for one new token per sequence:
 slot mapping -> store of the new K/V -> paged decode attention, by default in one
-launch (pkv_decode_append, balanced split-KV); `--separate` runs the append and
+launch (pkv_decode_append, in the mode pkv_decode_partition_size picks from the
+context lengths: unsplit for this batch); `--separate` runs the append and
 the decode as two launches, `--partition P` fixed partitions + the log-sum-exp
 reduce (two launches as well).  Inputs are resident in HBM;
 the L2 and Infinity Cache are flushed before every step (outside the timed
@@ -74,8 +75,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--partition", type=int, default=None,
                     help="split-KV partition size (0 = unsplit, -1 = balanced; default: "
-                         "pkv_decode_partition_size over a 16-bit pool, balanced over "
-                         "an 8-bit one)")
+                         "pkv_decode_partition_size from the context lengths)")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -119,13 +119,9 @@ def calibrate():
 
 
 def default_partition(pkv, wl):
-    """The decode mode: over a 16-bit pool, the library's choice from the host's
-    context lengths (unsplit for the Llama-3-8B-shaped batch, whose 512 pairs fill the
-    CUs; one round of fixed partitions for the 8 long contexts); balanced split-KV
-    over an fp8 / int8 pool, where each key costs more ALU work to widen and the even
-    split of the work over all CUs wins."""
-    if wl.kv_dtype in ("fp8", "int8"):
-        return -1
+    """The decode mode: the library's choice from the host's context lengths, for
+    every pool type (unsplit for the Llama-3-8B-shaped batch, whose 512 pairs fill the
+    CUs; one round of fixed partitions for the 8 long contexts)."""
     return pkv.pkv_decode_partition_size(wl.context_lens, wl.num_kv_heads, wl.max_context_len)
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}  # pool bytes per element
 

@@ -59,14 +59,16 @@
 // Both main kernels also take a sliding window (a sequence's chunk grid starts
 // at its window's first 16-token tile), and both can store each sequence's
 // newest token themselves before decoding it (the fused decode step).
-// The workgroup kernel's chunk loop is software-pipelined on one buffer: the
-// next chunk's K pieces are requested as soon as the current scores are done
-// and its V pieces as soon as the current P.V is done, the table entries one
-// chunk further ahead.  The balanced kernel's runs on two buffers (the next
-// chunk in flight while the current one is computed).  Both are compiled for
-// one wavefront per SIMD, whose registers hold the buffers: buffers beyond the
-// 256 architectural registers would live in AGPRs, and their copies cost more
-// than the deeper pipeline gains.
+// The workgroup kernel's chunk loop is software-pipelined on one buffer for 16-
+// and 32-bit pools: the next chunk's K pieces are requested as soon as the
+// current scores are done and its V pieces as soon as the current P.V is done,
+// the table entries one chunk further ahead.  Over 8-bit pools, whose chunks are
+// half the bytes, it runs two buffers deep (chunk i+1 in flight while chunk i is
+// computed, chunk i+2 requested into chunk i's buffer in the same two halves), so
+// that a wavefront keeps as many bytes in flight as over a 16-bit pool.  The
+// balanced kernel's loop runs on two buffers (the next chunk in flight while the
+// current one is computed).  Both are compiled for one wavefront per SIMD, whose
+// registers hold the buffers.
 #include "device.hpp"
 #include "internal.hpp"
 #include "tile.hpp"
@@ -145,8 +147,10 @@ struct Cfg {
   static constexpr int NK = 4 * NPL;          // K pieces per lane per chunk: [T][q]
   static constexpr int NV = NDT * 4;          // V pieces per lane per chunk: [dt][T]
   static constexpr int QEB = F32 ? 4 : 2;     // bytes per q element
-  // chunk buffers in the balanced kernel's software pipeline (a third does not
-  // fit the 256 architectural registers: the compiler parks buffers in AGPRs)
+  // chunk buffers in the balanced kernel's software pipeline (for 16-bit pools the
+  // second lives in AGPRs, which measured faster than one buffer whose next chunk is
+  // requested in two halves as in the workgroup kernel; a third costs more in copies
+  // than it gains)
   static constexpr int NBUF = 2;
   using QOp = std::conditional_t<F32, float, u32x4>;
   // a V piece: four consecutive tokens of one dim
@@ -367,6 +371,53 @@ __device__ __forceinline__ void chunk_scales(float (&ks)[16], float (&vs)[16],
         ks[4 * T + r] = a;
         vs[4 * T + r] = b;
       }
+    }
+  }
+}
+
+// The same scales with the mode fixed at compile time: per token (TOK) the lane's 16
+// keys, else one per tile (page or pool scale), so a software pipeline that holds the
+// scales of two chunks keeps 8 registers per chunk instead of 32 outside token mode
+template <bool TOK>
+struct ChunkScales {
+  float k[TOK ? 16 : 4], v[TOK ? 16 : 4];
+};
+
+template <bool TOK>
+__device__ __forceinline__ void load_scales(ChunkScales<TOK>& cs, const float* __restrict__ k_scale,
+                                            const float* __restrict__ v_scale, const Pages& pg,
+                                            int kvh, const DecodeScalars& sc, int g) {
+  const int B = 1 << sc.blog2;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const size_t page = (size_t)pg.b[T] * sc.Hkv + kvh;
+    if constexpr (TOK) {
+      const size_t i0 = page * B + ((pg.off + 16 * T) & (B - 1)) + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cs.k[4 * T + r] = k_scale[i0 + r];
+        cs.v[4 * T + r] = v_scale[i0 + r];
+      }
+    } else {
+      const size_t i = sc.scale_mode == SCALE_TENSOR ? 0 : page;
+      cs.k[T] = k_scale[i];
+      cs.v[T] = v_scale[i];
+    }
+  }
+}
+
+// the 16 per-key scales (key 16 T + 4 g + r at slot 4 T + r) the softmax takes
+template <bool TOK>
+__device__ __forceinline__ void expand_scales(const ChunkScales<TOK>& cs, float (&ks)[16],
+                                              float (&vs)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (TOK) {
+      ks[i] = cs.k[i];
+      vs[i] = cs.v[i];
+    } else {
+      ks[i] = cs.k[i >> 2];
+      vs[i] = cs.v[i >> 2];
     }
   }
 }
@@ -757,6 +808,63 @@ __device__ int seq_by_rank(const int32_t* __restrict__ context_lens, int S, int 
   return uniform(pick);
 }
 
+// A wave's chunks of one (sequence, kv head) over an 8-bit pool (block_size >= 16):
+// chunks c, c + 4, ... for c = wave, each base(i) = t_begin + 64 (wave + 4 i).  An
+// 8-bit chunk is half the bytes of a 16-bit one, so the pipeline runs two chunks
+// deep on two buffers: while chunk i is computed, chunk i+1 is in flight in the
+// other buffer, and chunk i+2's K pieces are requested into the current buffer as
+// soon as chunk i's scores are done, its V pieces as soon as chunk i's P.V is done.
+// A chunk's scales are requested one stage ahead of their use.
+template <class C, int KVT, int CT, bool TOK>
+__device__ __forceinline__ void wave_chunks_8bit(
+    State<C>& st, const typename C::QOp (&qop)[C::NQ], const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, const int32_t* __restrict__ trow, int t_begin, int t_end,
+    int lo, int wave, int cnt, int kvh, const DecodeScalars& sc, int n, int g) {
+  static_assert(C::EB == 1, "two-deep pipeline for 8-bit pools");
+  auto base_of = [&](int i) { return t_begin + 64 * (wave + kWaves * min(i, cnt - 1)); };
+  Chunk<C> RA, RB;
+  ChunkScales<TOK> sa, sb;
+  Pages pg1 = pages_of(trow, base_of(0), t_end, sc);
+  issue_k<C>(RA.k, k_pool, pg1, kvh, sc, n, g);
+  load_scales<TOK>(sa, k_scale, v_scale, pg1, kvh, sc, g);
+  issue_v<C>(RA.v, v_pool, pg1, kvh, sc, n, g);
+  pg1 = pages_of(trow, base_of(1), t_end, sc);
+  if (cnt > 1) {
+    issue_k<C>(RB.k, k_pool, pg1, kvh, sc, n, g);
+    issue_v<C>(RB.v, v_pool, pg1, kvh, sc, n, g);
+  }
+  Pages pg2 = pages_of(trow, base_of(2), t_end, sc);
+  // chunk i sits in R with its scales in cur; chunk i+1 (pages pg1) is in flight in
+  // the other buffer and its scales go to nxt; chunk i+2 (pages pg2) goes to R
+  auto stage = [&](Chunk<C>& R, ChunkScales<TOK>& cur, ChunkScales<TOK>& nxt, int i)
+      __attribute__((always_inline)) {
+    const int b0 = base_of(i);
+    f32x4 S[4];
+    chunk_qk<C, KVT, CT>(S, R.k, qop);
+    issue_point();
+    if (i + 1 < cnt) load_scales<TOK>(nxt, k_scale, v_scale, pg1, kvh, sc, g);
+    if (i + 2 < cnt) issue_k<C>(R.k, k_pool, pg2, kvh, sc, n, g);
+    const Pages pg3 = pages_of(trow, base_of(i + 3), t_end, sc);
+    issue_point();
+    float ks[16], vs[16];
+    expand_scales<TOK>(cur, ks, vs);
+    v_rows_to_tiles<C>(R.v);
+    chunk_softmax_pv<C, KVT, CT>(st, S, R.v, sc.scale_log2, ks, vs, min(64, t_end - b0), g, 64,
+                                 lo - b0);
+    issue_point();
+    if (i + 2 < cnt) issue_v<C>(R.v, v_pool, pg2, kvh, sc, n, g);
+    issue_point();
+    pg1 = pg2;
+    pg2 = pg3;
+  };
+  for (int i = 0; i < cnt; i += 2) {
+    stage(RA, sa, sb, i);
+    if (i + 1 >= cnt) break;
+    stage(RB, sb, sa, i + 1);
+  }
+}
+
 // =================================================================================
 // Kernel A: one workgroup per (partition, kv head, sequence)
 // =================================================================================
@@ -872,6 +980,15 @@ paged_decode_kernel(
       chunk_qk<C, KVT, CT>(S, ch.k, qop);
       chunk_softmax_pv<C, KVT, CT>(st, S, ch.v, sc.scale_log2, ks, vs, min(64, t_end - base), g,
                                    64, lo - base);
+    }
+  } else if (C::EB == 1 && cnt > 0) {
+    if constexpr (C::EB == 1) {
+      if (sc.scale_mode == SCALE_TOKEN)
+        wave_chunks_8bit<C, KVT, CT, true>(st, qop, k_pool, v_pool, k_scale, v_scale, trow,
+                                           t_begin, t_end, lo, wave, cnt, kvh, sc, n, g);
+      else
+        wave_chunks_8bit<C, KVT, CT, false>(st, qop, k_pool, v_pool, k_scale, v_scale, trow,
+                                            t_begin, t_end, lo, wave, cnt, kvh, sc, n, g);
     }
   } else if (cnt > 0) {
     // Single-buffered pipeline: chunk i+1's K pieces are requested as soon as

@@ -82,6 +82,27 @@ __device__ __forceinline__ u32x4 fp8x8(uint32_t w0, uint32_t w1) {
   }
 }
 
+// byte B of a word, sign-extended, as f32: one conversion that selects the byte in
+// its operand (written out so that the compiler cannot split it into a shift, kept
+// alive, and a conversion of byte 0)
+template <int B>
+__device__ __forceinline__ float sbyte_f32(uint32_t w) {
+  float f;
+  if constexpr (B == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+        : "=v"(f) : "v"(w));
+  else if constexpr (B == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+        : "=v"(f) : "v"(w));
+  else if constexpr (B == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+        : "=v"(f) : "v"(w));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+        : "=v"(f) : "v"(w));
+  return f;
+}
+
 // eight int8 codes (two words) -> eight CT values; exact, as every int8 value is
 // an integer of at most 8 bits.  f16: each byte, sign bit flipped (u = x + 128),
 // becomes the f16 1024 + u by its bits (one byte permute places two of them under
@@ -106,9 +127,8 @@ __device__ __forceinline__ u32x4 i8x8(uint32_t w0, uint32_t w1) {
         r[2 * i + hp] = __builtin_bit_cast(uint32_t, h - f16x2{(_Float16)1152.0f, (_Float16)1152.0f});
       } else {
         static_assert(CT == DT_BF16, "int8 widens to f16 or bf16");
-        const float a = (float)(signed char)(w[i] >> (16 * hp));
-        const float b = (float)(signed char)(w[i] >> (16 * hp + 8));
-        r[2 * i + hp] = pack2<DT_BF16>(a, b);
+        r[2 * i + hp] = hp == 0 ? pack2<DT_BF16>(sbyte_f32<0>(w[i]), sbyte_f32<1>(w[i]))
+                                : pack2<DT_BF16>(sbyte_f32<2>(w[i]), sbyte_f32<3>(w[i]));
       }
     }
   }

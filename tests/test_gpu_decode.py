@@ -262,10 +262,11 @@ def test_llama3_8b_full_peaked(factor):
 
 
 @pytest.mark.parametrize("kv,mode", [("fp8", "block"), ("int8", "block"), ("fp8", "tensor"),
-                                     ("int8", "token")])
+                                     ("int8", "token"), ("fp8", "token")])
 def test_llama3_8b_full_quantised(kv, mode):
-    """The full Llama-3-8B-shaped batch over 8-bit pools, in the unsplit launch (whose
-    block- and tensor-scale pools read 128-token super-chunks) and the balanced one:
+    """The full Llama-3-8B-shaped batch over 8-bit pools, in the unsplit launch (two
+    chunks deep per wavefront, up to 16 chunks each), the balanced one and 192-token
+    partitions:
     the write path bit for bit against the oracle's, sampled sequences within the
     tolerance (the longest and the shortest among them)."""
     wl = W.llama3_8b_decode(kv_dtype=kv, scale_mode=mode)
