@@ -872,7 +872,7 @@ __device__ __forceinline__ void wave_chunks_8bit(
 // partition reaches the end of the clamped context) also appends the newest token
 // (position ctx - 1, from sc.k_new / sc.v_new): it stores the row into its slot at
 // the start and patches it into its registers at that chunk.
-template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false>
+template <int KVT, int CT, int D, bool SMALLB, bool FUSE = false, bool TOKSC = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 paged_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k_pool,
@@ -982,14 +982,9 @@ paged_decode_kernel(
                                    64, lo - base);
     }
   } else if (C::EB == 1 && cnt > 0) {
-    if constexpr (C::EB == 1) {
-      if (sc.scale_mode == SCALE_TOKEN)
-        wave_chunks_8bit<C, KVT, CT, true>(st, qop, k_pool, v_pool, k_scale, v_scale, trow,
-                                           t_begin, t_end, lo, wave, cnt, kvh, sc, n, g);
-      else
-        wave_chunks_8bit<C, KVT, CT, false>(st, qop, k_pool, v_pool, k_scale, v_scale, trow,
-                                            t_begin, t_end, lo, wave, cnt, kvh, sc, n, g);
-    }
+    if constexpr (C::EB == 1)
+      wave_chunks_8bit<C, KVT, CT, TOKSC>(st, qop, k_pool, v_pool, k_scale, v_scale, trow,
+                                          t_begin, t_end, lo, wave, cnt, kvh, sc, n, g);
   } else if (cnt > 0) {
     // Single-buffered pipeline: chunk i+1's K pieces are requested as soon as
     // chunk i's scores are computed and its V pieces as soon as chunk i's P.V is
@@ -1903,6 +1898,18 @@ int launch_t(const DecodeLaunch& p, const DecodeScalars& sc, hipStream_t st) {
       return hipGetLastError() == hipSuccess ? 0 : -5;
     } else {
       return -3;
+    }
+  }
+  // 8-bit pools with per-token scales: an instantiation of their own, so that the
+  // others keep 8 scale registers per chunk in flight (and two waves per SIMD)
+  if constexpr (Elem<KVT>::bytes == 1 && !SMALLB) {
+    if (sc.scale_mode == SCALE_TOKEN) {
+      hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB, false, true>), grid,
+                         dim3(kThreads), 0, st, (const uint8_t*)p.q, (const uint8_t*)p.k_pool,
+                         (const uint8_t*)p.v_pool, p.k_scale, p.v_scale, p.block_table,
+                         p.context_lens, (uint8_t*)p.out, p.part_out, p.part_max, p.part_sum,
+                         sc);
+      return hipGetLastError() == hipSuccess ? 0 : -5;
     }
   }
   hipLaunchKernelGGL((paged_decode_kernel<KVT, CT, D, SMALLB>), grid, dim3(kThreads), 0, st,
