@@ -1504,8 +1504,8 @@ paged_decode_balanced_kernel(
     // the loads of the next NBUF-2 chunks are in flight; the stage requests
     // chunk +NBUF-1 into the buffer freed by the previous stage, then computes
     // the current one.  The table entries run one chunk ahead of the requests.
-    // The next pair's q is loaded into qop right after the current pair's last
-    // scores have consumed it.
+    // The next pair's q is requested a whole stage before its first chunk is
+    // computed.
     constexpr int NB = C::NBUF;
     Chunk<C> R[NB];
     Pos pp[NB];          // pp[k]: position of the chunk k stages ahead of pc
@@ -1534,14 +1534,16 @@ paged_decode_balanced_kernel(
     }
     pp[NB - 1] = advance(pp[NB - 2]);
     Pages en = pages_at(pp[NB - 1]);
-    bool q_raw = false;  // qop holds a fresh load whose dead columns are not yet zeroed
     bool done = false;
+    // The q of the pair that starts at pp[1] is requested a whole stage before its
+    // first chunk is computed (into qn, moved to qop when the pair starts)
+    typename C::QOp qn[C::NQ];
+    auto switch_next = [&]() {
+      return pp[0].k + 1 < n_units && (pp[1].s != pp[0].s || pp[1].kvh != pp[0].kvh);
+    };
+    if (switch_next()) load_q<C>(qn, q, pp[1].s, pp[1].kvh, sc, n, g);
     // stage: chunk pp[0] sits in R[c]; chunk pp[NB-1] goes to R[f]
     auto stage = [&](Chunk<C>& cur, Chunk<C>& fill, int c, int f) {
-      if (q_raw) {
-        q_live<C>(qop, qop, n < sc.G);
-        q_raw = false;
-      }
       const Pos& p0 = pp[0];
       const bool last = p0.k + 1 >= n_units;
       const bool fetch = pp[NB - 1].k != pp[NB - 2].k;  // a chunk that is not a repeat
@@ -1560,7 +1562,6 @@ paged_decode_balanced_kernel(
       chunk_qk<C, KVT, CT>(S, cur.k, qop);
       issue_point();
       const bool new_pair = !last && (pp[1].s != p0.s || pp[1].kvh != p0.kvh);
-      if (new_pair) load_q<C>(qop, q, pp[1].s, pp[1].kvh, sc, n, g);
       issue_point();
       v_rows_to_tiles<C>(cur.v);
       chunk_softmax_pv<C, KVT, CT>(st, S, cur.v, sc.scale_log2, ksr[c], vsr[c],
@@ -1570,13 +1571,14 @@ paged_decode_balanced_kernel(
         finish_piece(p0);
         piece_j0 = pp[1].j;
         piece_u0 = pp[1].u;
-        q_raw = new_pair;
+        if (new_pair) q_live<C>(qop, qn, n < sc.G);
       }
       done = last;
 #pragma unroll
       for (int k = 0; k + 1 < NB; ++k) pp[k] = pp[k + 1];
       pp[NB - 1] = pnext;
       en = en2;
+      if (!done && switch_next()) load_q<C>(qn, q, pp[1].s, pp[1].kvh, sc, n, g);
     };
     while (true) {
       if constexpr (NB == 3) {
