@@ -891,9 +891,29 @@ paged_decode_kernel(
 
   // grid (kv head, sequence, partition): launch order runs over the kv heads first,
   // so with H_kv a multiple of 8 every XCD (workgroups go to the 8 XCDs round-robin)
-  // takes the same kv head of every (sequence, partition), the same work
-  const int part = blockIdx.z, kvh = blockIdx.x;
-  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, blockIdx.y) : blockIdx.y;
+  // takes the same kv head of every (sequence, partition), the same work.  8-bit
+  // pools instead keep the kv heads of a sequence on one XCD, so that they share, in
+  // its L2, the lines that hold their blocks' scales ([block][kv head] floats): the
+  // launch runs in groups of 8 sequences x H_kv heads, the i-th workgroup of a group
+  // takes sequence i mod 8 (reversed in every other group, which evens out the XCDs'
+  // shares of the longest-first order) and kv head i / 8.
+  const int part = blockIdx.z;
+  int kvh = blockIdx.x, srank = blockIdx.y;
+  if constexpr (C::EB == 1) {
+    const int L = blockIdx.x + sc.Hkv * blockIdx.y;  // launch order in the partition
+    const int full = (sc.S / 8) * 8 * sc.Hkv;        // workgroups in whole groups
+    if (L < full) {
+      const int grp = L / (8 * sc.Hkv), r = L - grp * 8 * sc.Hkv, x = r & 7;
+      kvh = r >> 3;
+      srank = 8 * grp + ((grp & 1) ? 7 - x : x);
+    } else {
+      kvh = (L - full) % sc.Hkv;
+      srank = (sc.S / 8) * 8 + (L - full) / sc.Hkv;
+    }
+    kvh = uniform(kvh);
+    srank = uniform(srank);
+  }
+  const int s = sc.lpt ? seq_by_rank(context_lens, sc.S, srank) : srank;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
 
