@@ -21,6 +21,8 @@
 //   O^T = V^T . P^T 16x16x32 MFMA in the V staging type, P from the lane's own
 //                   scores (tile T row n is key 16 T + n, so S^T leaves lane
 //                   (n, g) the keys 16 T + 4 g + r, the k-slots P.V needs).
+// The softmax first takes a chunk's p against each row's current reference and
+// computes the chunk's maxima only where that would leave the P operand's range.
 // fp8 pools: K's page scale multiplies the scores; V's multiplies V as it is
 // widened to f16 in LDS; P.V runs in f16 (P keeps 11 significant bits) and the
 // softmax sum adds the same f16 values of P.  bf16 pools: P.V in bf16 with P split
@@ -326,34 +328,109 @@ __device__ __forceinline__ void chunk_scores(f32x4 (&S)[C::NR][4], const uint8_t
   }
 }
 
+// S^T = K . q^T of one row tile (the rare second pass of a chunk's softmax)
+template <class C>
+__device__ __forceinline__ void tile_scores(f32x4 (&S)[4], const uint8_t* kbuf,
+                                            const int (&k_off)[4], const int (&k_unit)[C::NKS],
+                                            const u32x4 (&q)[C::NKS]) {
+  const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+      S[T] = mma16<C::QT>(*reinterpret_cast<const u32x4*>(kbuf + k_off[T] + k_unit[ks]), q[ks],
+                          ks == 0 ? zero : S[T]);
+}
+
+// scores of keys at or past a row's bound become -inf (the softmax then gives them 0)
+__device__ __forceinline__ void mask_scores(f32x4 (&S)[4], int rlim, int base, int g) {
+  const int lim = rlim - base - 4 * g;  // keys 16 T + r below lim are visible
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[T][r] = 16 * T + r < lim ? S[T][r] : -INFINITY;
+}
+
+// p = 2^(S zs - mref) of one row tile's 16 keys, packed into the P operands of P.V,
+// and the row sum of the same values (masked keys: S = -inf, p = 0)
+template <class C>
+__device__ __forceinline__ float chunk_p(const f32x4 (&S)[4], const float (&zs)[4], float mref,
+                                         u32x4 (&phi)[2], u32x4 (&plo)[2]) {
+  float p[16];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[T][r], zs[T], -mref));
+  float psum = 0.0f;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
+      const float a = p[i0], b = p[i0 + 1];
+      wh[wd] = pack2<C::PT>(a, b);
+      if constexpr (C::SPLIT) {
+        const f32x2 h = unpack2<C::PT>(wh[wd]);
+        wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
+        psum += a + b;
+      } else {
+        // fp8 and f16 pools: P is f16(p) (fp8: V carries its page scale); the row sum
+        // adds the same rounded values (exact f16 products, fp32 sum)
+        wl[wd] = 0u;
+        psum = __builtin_amdgcn_fdot2(as_f16x2(wh[wd]), f16x2{(_Float16)1.0f, (_Float16)1.0f},
+                                      psum, false);
+      }
+    }
+    phi[s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
+    plo[s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+  }
+  return psum;
+}
+
 // Online softmax of one chunk (keys base ..) for every row tile: the P operands, the
 // reference and the sum updated, the accumulators rescaled when a reference moves.
 // Keys at or past a row's bound (rlim) exist only where need_mask says so.
-template <class C>
+//
+// The softmax does not depend on the reference a row's p are taken against, as long
+// as they stay finite in the P operand's type.  So a chunk first takes p against the
+// row's current reference without computing the chunk's maxima; that is kept when
+// every row of the tile has a reference and its chunk sum is at most 2^15 (each p is
+// then at most 2^15, inside f16 and bf16).  Otherwise (a row's first keys, or scores
+// that passed the reference by about 9 or more in log2 units) the chunk takes the
+// maxima: the reference moves only when a chunk's max passes it by more than
+// kLazyMax, so the accumulators are rescaled rarely, and p is taken again (after a
+// failed first pass from scores computed again, so that the first pass need not keep
+// them).
+template <class C, bool TWO_PASS>
 __device__ __forceinline__ void chunk_softmax(f32x4 (&S)[C::NR][4], RowState<C::Dim> (&st)[C::NR],
                                               const float (&zs)[4], const int (&rlim)[C::NR],
                                               int base, int g, bool need_mask,
-                                              u32x4 (&phi)[C::NR][2], u32x4 (&plo)[C::NR][2]) {
+                                              u32x4 (&phi)[C::NR][2], u32x4 (&plo)[C::NR][2],
+                                              const uint8_t* kbuf, const int (&k_off)[4],
+                                              const int (&k_unit)[C::NKS],
+                                              const u32x4 (&qop)[C::NR][C::NKS]) {
   constexpr int NR = C::NR;
+  constexpr float kFastSum = 32768.0f;
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
     // scores in log2 units are S zs (zs > 0: the softmax scale times K's page
     // scale); masked keys become -inf in place, which the same path turns into 0
-    if (need_mask) {
-      const int lim = rlim[rt] - base - 4 * g;  // keys 16 T + r below lim are visible
-#pragma unroll
-      for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[rt][T][r] = 16 * T + r < lim ? S[rt][T][r] : -INFINITY;
+    if (need_mask) mask_scores(S[rt], rlim[rt], base, g);
+    if (TWO_PASS && __builtin_amdgcn_ballot_w64(st[rt].m == -INFINITY) == 0) {
+      const float psum = chunk_p<C>(S[rt], zs, st[rt].m, phi[rt], plo[rt]);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= kFastSum)) == 0) {
+        st[rt].l += psum;
+        continue;
+      }
+      tile_scores<C>(S[rt], kbuf, k_off, k_unit, qop[rt]);
+      if (need_mask) mask_scores(S[rt], rlim[rt], base, g);
     }
     float tm[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T)
       tm[T] = fmax4(S[rt][T][0], S[rt][T][1], S[rt][T][2], S[rt][T][3]) * zs[T];
     float cm = max_groups(fmax4(tm[0], tm[1], tm[2], tm[3]));
-    // The reference max moves only when a chunk's max passes it by more than
-    // kLazyMax, so the accumulators are rescaled rarely (the softmax does not
-    // depend on the reference); p then stays below 2^kLazyMax.
     const bool moves = cm > st[rt].m + kLazyMax;
     if (__builtin_amdgcn_ballot_w64(moves) != 0) {
       // 0 for a row's first keys; 1 for a row that does not move (which may not have
@@ -366,36 +443,7 @@ __device__ __forceinline__ void chunk_softmax(f32x4 (&S)[C::NR][4], RowState<C::
       for (int dt = 0; dt < C::NDT; ++dt) st[rt].acc[dt] *= alpha;
     }
     const float mref = st[rt].m == -INFINITY ? 0.0f : st[rt].m;  // rows that have seen no key yet
-    float p[16];
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[4 * T + r] = __builtin_amdgcn_exp2f(fmaf(S[rt][T][r], zs[T], -mref));
-    float psum = 0.0f;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      uint32_t wh[4], wl[4];
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const int i0 = 8 * s2 + 2 * wd;  // keys 32 s2 + 16 (wd / 2) + 4 g + 2 (wd % 2) + {0, 1}
-        const float a = p[i0], b = p[i0 + 1];
-        wh[wd] = pack2<C::PT>(a, b);
-        if constexpr (C::SPLIT) {
-          const f32x2 h = unpack2<C::PT>(wh[wd]);
-          wl[wd] = pack2<C::PT>(a - h[0], b - h[1]);
-          psum += a + b;
-        } else {
-          // fp8 and f16 pools: P is f16(p) (fp8: V carries its page scale); the row sum
-          // adds the same rounded values (exact f16 products, fp32 sum)
-          wl[wd] = 0u;
-          psum = __builtin_amdgcn_fdot2(as_f16x2(wh[wd]), f16x2{(_Float16)1.0f, (_Float16)1.0f},
-                                        psum, false);
-        }
-      }
-      phi[rt][s2] = u32x4{wh[0], wh[1], wh[2], wh[3]};
-      plo[rt][s2] = u32x4{wl[0], wl[1], wl[2], wl[3]};
-    }
-    st[rt].l += psum;
+    st[rt].l += chunk_p<C>(S[rt], zs, mref, phi[rt], plo[rt]);
   }
 }
 
@@ -671,7 +719,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
       __builtin_amdgcn_s_setprio(0);
       // ---- online softmax per row tile; P operands
       u32x4 phi[NR][2], plo[NR][2];
-      chunk_softmax<C>(S, st, zs, rlim, base, g, base + 64 > wave_min_lim, phi, plo);
+      // the first pass without the chunk's maxima where the registers allow it (not in
+      // prefix mode, nor over f16 pools of 128 dims: there it would not leave two
+      // workgroups per CU)
+      constexpr bool kTwoPass = !PREFIX && !(KVT == DT_F16 && D == 128);
+      chunk_softmax<C, kTwoPass>(S, st, zs, rlim, base, g, base + 64 > wave_min_lim, phi, plo,
+                                 kbuf, k_off, k_unit, qop);
       // ---- stage chunk j+1 into the other buffer (free since the last barrier)
       // while the matrix cores run O^T += V^T . P^T: the conversions and LDS writes
       // fill the issue slots between the MFMAs
