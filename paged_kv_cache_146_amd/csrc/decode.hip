@@ -67,8 +67,10 @@
 // computed, chunk i+2 requested into chunk i's buffer in the same two halves), so
 // that a wavefront keeps as many bytes in flight as over a 16-bit pool.  The
 // balanced kernel's loop runs on two buffers (the next chunk in flight while the
-// current one is computed).  Both are compiled for one wavefront per SIMD, whose
-// registers hold the buffers.
+// current one is computed).  Both are compiled with the whole register file open
+// to a wavefront, whose registers hold the buffers; where an instantiation needs at
+// most 256 of them (the workgroup kernel over 16-bit pools, and over 8-bit pools
+// with page or pool scales), the hardware keeps two wavefronts per SIMD.
 #include "device.hpp"
 #include "internal.hpp"
 #include "tile.hpp"
