@@ -90,3 +90,15 @@ def test_fp8_prefill_full_sampled(factor):
         rows += [a, a + 1, b - 1, b - 2] + list(rng.integers(a, b, 4))
     rows = np.array(sorted(set(rows)), np.int64)
     print(_run(wl, causal=True, rows=rows))
+
+
+@pytest.mark.parametrize("kv,D", [("fp8", 128), ("bf16", 128), ("f16", 64), ("fp8", 64)])
+def test_prefill_sharp_softmax(kv, D):
+    # q x 32 (exact): scores spread over ~45 log2 units, so later chunks often pass a
+    # row's reference by far more than the first softmax pass allows (a chunk sum above
+    # 2^15), and the tile takes its scores again and the maxima path; several chunks
+    # per sequence, rows that start inside a tile
+    wl = W.make_prefill("prefill sharp %s D=%d" % (kv, D), 60 + D, 3, [300, 90, 0],
+                        [77, 130, 64], 8, 2, D, 16, kv_dtype=kv,
+                        q_dtype="f16" if kv == "f16" else "bf16")
+    print(_run(peaked(wl, 32), causal=True))
